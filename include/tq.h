@@ -1,0 +1,166 @@
+/*
+ * libtq: rotation + Lloyd-Max weight quantization and its fused quantized linear layers,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method (turboquant-mlx, "How it works"):
+ *   - "Quantizing a weight, with no data": every weight row w (length K, the input
+ *     dimension) is rotated, w' = R w with R = H_K diag(s) / sqrt(K) (random +-1 signs s,
+ *     then a Hadamard matrix); the rotated row is cut into groups of 16/32/64/128 along K,
+ *     each group is divided by its root-mean-square, every value snaps to the nearest
+ *     centroid of a fixed Lloyd-Max codebook for N(0,1) (2, 3 or 4 bits), and the indices
+ *     are bit-packed into 32-bit words with per-group scales stored alongside.
+ *   - "The ternary tier (1.58 bits)": a 3-level codebook {-c, 0, +c}; twenty base-3
+ *     digits per 32-bit word. The codebook size tells which packing is used.
+ *   - "Running a quantized layer": R is orthonormal, so the layer rotates its input,
+ *     x' = R x, and multiplies by the packed weights, decoding them inline:
+ *         y_i = sum_g scale_{i,g} sum_{j in g} c[idx_ij] x'_j .
+ *     Mixture-of-Experts layers use gather_qmv (one token, shared input),
+ *     multi_gather_qmv (a different input per expert) and gather_qmm (a large batch
+ *     sorted by expert).
+ *   - "Quantizing a weight, with no data", last paragraph: all experts of a layer share
+ *     the rotation signs and the codebook.
+ *
+ * Conventions shared by every entry point
+ *   Memory    Pointers marked "device" are HIP device pointers; "host" are host pointers.
+ *             The caller owns all memory, including workspaces. The library never
+ *             allocates and keeps no pointer after a call returns.
+ *   Streams   `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *             Calls only enqueue work on it and never synchronize; routing ids and offsets
+ *             stay on the device.
+ *   Errors    Arguments are checked on the host before anything is launched. A failed
+ *             check returns a negative tq_status and sets a thread-local message readable
+ *             with tq_last_error(). A launch failure returns TQ_ERR_HIP. Nothing aborts
+ *             and nothing throws across this interface. TQ_OK is 0.
+ *   Shapes    K = m * 2^k with m in {1, 12, 20, 28}, K a multiple of 32 in [64, 8192];
+ *             group in {16, 32, 64, 128} dividing K; n_levels in {3, 4, 8, 16};
+ *             E in [1, 8192]. Other shapes return TQ_ERR_UNSUPPORTED.
+ *   Layout    codes  uint32 [E][N][words_per_row], rows packed independently;
+ *                    words_per_row = ceil(K * b / 32) for b = log2(n_levels) bits, element
+ *                    j of a row in bits [b*j, b*j + b) of the row's little-endian
+ *                    bitstream (bit p is bit p%32 of word p/32), unused bits zero;
+ *                    n_levels = 3: words_per_row = ceil(K / 20), word w holds elements
+ *                    20w..20w+19 as sum_k t_k 3^k (element 20w+k is digit k), padding
+ *                    digits 0. Index 0 is the most negative centroid.
+ *             scales fp16 bit patterns [E][N][K / group]: the group RMS rounded to
+ *                    nearest even, saturating at 65504.
+ *             signs  uint32 [ceil(K / 32)]: bit i (bit i%32 of word i/32) set means
+ *                    s_i = -1. Produced by tq_signs from the seed.
+ *   Signs     s_i = -1 iff the top bit of SplitMix64 output i of the generator seeded with
+ *             `seed` is set: output i = mix64(seed + (i + 1) * 0x9E3779B97F4A7C15) with the
+ *             SplitMix64 finalizer (Steele, Lea, Flood 2014). The pages only say the
+ *             rotation comes from a seed; this generator is this library's choice.
+ *   Hadamard  H_K = H_m (x) H_{2^k}: natural-order Sylvester H_{2^k}; H_12 and H_20 from
+ *             Paley's first construction (q = 11, 19), H_28 from Paley's second (q = 13),
+ *             with Jacobsthal matrix Q[a][b] = chi(a - b).
+ *   Dtypes    Activations and outputs are fp32, bf16 or fp16 (tq_dtype). Accumulation is
+ *             fp32. Weights for tq_encode are fp32, bf16 or fp16.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_ERR_ARG = -1,          /* null pointer, bad size, bad dtype */
+  TQ_ERR_UNSUPPORTED = -2,  /* K, group or n_levels outside the supported set */
+  TQ_ERR_ALIGN = -3,        /* a pointer is not aligned as documented */
+  TQ_ERR_WORKSPACE = -4,    /* workspace missing or smaller than tq_workspace_bytes */
+  TQ_ERR_HIP = -5           /* the HIP runtime reported an error */
+} tq_status;
+
+/* flags for the qmv family */
+enum { TQ_X_ROTATED = 1 }; /* x is already R x: skip the input rotation */
+
+/* operation ids for tq_workspace_bytes */
+enum { TQ_OP_QMV = 1, TQ_OP_GATHER_QMV = 2, TQ_OP_MULTI_GATHER_QMV = 3, TQ_OP_GATHER_QMM = 4 };
+
+/* A packed quantized weight: E experts of N x K (E = 1 for a dense layer). Read only
+ * during the call. */
+typedef struct {
+  const uint32_t *codes;  /* device, [E][N][words_per_row], 16-byte aligned */
+  const uint16_t *scales; /* device, [E][N][K / group], fp16 bits, 2-byte aligned */
+  const uint32_t *signs;  /* device, [ceil(K / 32)] rotation sign bits (tq_signs) */
+  int32_t n_levels;       /* 3 -> trit packed; 4 / 8 / 16 -> 2 / 3 / 4-bit bitstream */
+  int32_t group;          /* 16, 32, 64 or 128 */
+  int64_t K, N, E;        /* input dim, output dim, number of experts */
+  uint64_t seed;          /* the seed the signs came from (recorded, not read by kernels) */
+} tq_qweight;
+
+/* Number of uint32 words per packed row, or 0 for an unsupported (K, n_levels). */
+int64_t tq_words_per_row(int64_t K, int32_t n_levels);
+
+/* Centroids (ascending, n_levels floats) and, if `thresholds` is not NULL, the n_levels-1
+ * decision thresholds (midpoints of neighbouring centroids), both binary32, host memory.
+ * The codebook is the Lloyd-Max quantizer of N(0,1) ("Quantizing a weight, with no data",
+ * third bullet; "The ternary tier"), computed by Lloyd iteration in double precision when
+ * the library loads and rounded once. Returns TQ_OK or TQ_ERR_UNSUPPORTED. */
+int tq_codebook(int32_t n_levels, float *centroids, float *thresholds);
+
+/* Rotation sign bits for (seed, K) into device memory `bits` (ceil(K/32) words). */
+int tq_signs(uint64_t seed, int64_t K, uint32_t *bits, void *stream);
+
+/* Encode `rows` weight rows of length K (device, row-major, dtype w_dtype) into codes
+ * (device, [rows][words_per_row]) and scales (device, [rows][K/group]). For an expert
+ * stack pass rows = E * N. Steps ("Quantizing a weight, with no data"): v = R w; per
+ * group r = sqrt(mean v^2), scale = fp16(r); u = v / r (u = 0 when r = 0);
+ * idx = #{k : u > t_k} with u and t_k in binary32; pack. Rotation and RMS are computed in
+ * double precision. Deterministic and independent of how rows are split across calls. */
+int tq_encode(const void *W, tq_dtype w_dtype, int64_t rows, int64_t K, int32_t n_levels,
+              int32_t group, uint64_t seed, uint32_t *codes, uint16_t *scales, void *stream);
+
+/* out[r] = R x[r] for `rows` rows of length K (device, row-major). Computed in fp32.
+ * ("Running a quantized layer": the input is rotated with the weights' rotation.) */
+int tq_fwht(const void *x, tq_dtype x_dtype, int64_t rows, int64_t K, uint64_t seed,
+            void *out, tq_dtype out_dtype, void *stream);
+
+/* Bytes of workspace an operation needs (0 if none). `count` is n (ids) for
+ * gather_qmv, P (pairs) for multi_gather_qmv, M (rows) for gather_qmm; T is the number
+ * of input rows of gather_qmm. Returns SIZE_MAX for invalid arguments. Workspaces are
+ * 16-byte aligned (multi_gather_qmv) or 256-byte aligned (gather_qmm). */
+size_t tq_workspace_bytes(int32_t op, const tq_qweight *w, int64_t count, int64_t T);
+
+/* Dense layer (E must be 1): y[N] = W R x, x device [K]. Workspace: none. */
+int tq_qmv(const tq_qweight *w, const void *x, tq_dtype x_dtype, void *y, tq_dtype y_dtype,
+           uint32_t flags, void *ws, size_t ws_bytes, void *stream);
+
+/* One token through n routed experts sharing one input ("Running a quantized layer",
+ * kernel table, first row): y[k][N] = W_{ids[k]} R x for k < n. ids device int32 [n].
+ * An id outside [0, E) yields a row of NaN (no out-of-range access). */
+int tq_gather_qmv(const tq_qweight *w, const int32_t *ids, int32_t n, const void *x,
+                  tq_dtype x_dtype, void *y, tq_dtype y_dtype, uint32_t flags, void *ws,
+                  size_t ws_bytes, void *stream);
+
+/* P (input, expert) pairs, each with its own input ("Running a quantized layer", kernel
+ * table, second row): y[p] = W_{ids[p]} R x[p]. x device [P][K], y device [P][N]. Pairs
+ * are bucketed by expert on the device so that each W_e is streamed once; y keeps the
+ * caller's pair order. Ids outside [0, E) yield NaN rows. Workspace: tq_workspace_bytes. */
+int tq_multi_gather_qmv(const tq_qweight *w, const int32_t *ids, int64_t P, const void *x,
+                        tq_dtype x_dtype, void *y, tq_dtype y_dtype, uint32_t flags, void *ws,
+                        size_t ws_bytes, void *stream);
+
+/* Batched gather-GEMM over rows sorted by expert ("Running a quantized layer", kernel
+ * table, third row): for offsets[e] <= m < offsets[e+1], y[m] = W_e R x[row_token[m]].
+ * x device [T][K]; row_token device int32 [M]; expert_offsets device int32 [E+1],
+ * non-decreasing, offsets[0] = 0, offsets[E] = M; y device [M][N] in sorted-row order.
+ * Rows are multiplied with bf16 MFMA (weights decoded to bf16, inputs rotated to bf16),
+ * accumulated in fp32. Workspace: tq_workspace_bytes. */
+int tq_gather_qmm(const tq_qweight *w, const void *x, tq_dtype x_dtype, int64_t T,
+                  const int32_t *row_token, const int32_t *expert_offsets, int64_t M, void *y,
+                  tq_dtype y_dtype, uint32_t flags, void *ws, size_t ws_bytes, void *stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *tq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

@@ -1,0 +1,246 @@
+"""Python binding of libtq (include/tq.h): argument marshalling only.
+
+Every step of encode and of the qmv family runs in the HIP kernels of libtq.so; this module
+only turns torch tensors into pointers, dtypes and the caller's current HIP stream, and
+allocates outputs and workspaces with torch. If libtq.so is missing, every call raises.
+
+The method: turboquant-mlx "How it works" -- "Quantizing a weight, with no data" (rotate,
+group RMS, snap to a Lloyd-Max codebook, pack), "The ternary tier (1.58 bits)" and
+"Running a quantized layer" (rotate the input, multiply by inline-decoded codes; the MoE
+kernels gather_qmv, multi_gather_qmv and gather_qmm).
+"""
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+__all__ = [
+    "TqError", "QWeight", "lib", "codebook", "words_per_row", "signs", "encode", "fwht",
+    "qmv", "gather_qmv", "multi_gather_qmv", "gather_qmm", "workspace_bytes",
+    "F32", "BF16", "F16", "X_ROTATED",
+]
+
+F32, BF16, F16 = 0, 1, 2
+X_ROTATED = 1
+OP_QMV, OP_GATHER_QMV, OP_MULTI_GATHER_QMV, OP_GATHER_QMM = 1, 2, 3, 4
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
+
+_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+
+
+class TqError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"libtq status {status}: {message}")
+        self.status = status
+
+
+class _QWeight(ctypes.Structure):
+    _fields_ = [
+        ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("signs", ctypes.c_void_p),
+        ("n_levels", ctypes.c_int32), ("group", ctypes.c_int32),
+        ("K", ctypes.c_int64), ("N", ctypes.c_int64), ("E", ctypes.c_int64),
+        ("seed", ctypes.c_uint64),
+    ]
+
+
+_lib = None
+
+# (name, restype, argtypes) for every function declared in include/tq.h
+_P, _I32, _I64, _U32, _U64, _SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                   ctypes.c_uint32, ctypes.c_uint64, ctypes.c_size_t)
+_QW = ctypes.POINTER(_QWeight)
+SIGNATURES = [
+    ("tq_words_per_row", _I64, [_I64, _I32]),
+    ("tq_codebook", ctypes.c_int, [_I32, _P, _P]),
+    ("tq_signs", ctypes.c_int, [_U64, _I64, _P, _P]),
+    ("tq_encode", ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I32, _I32, _U64, _P, _P, _P]),
+    ("tq_fwht", ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _U64, _P, ctypes.c_int, _P]),
+    ("tq_workspace_bytes", _SZ, [_I32, _QW, _I64, _I64]),
+    ("tq_qmv", ctypes.c_int, [_QW, _P, ctypes.c_int, _P, ctypes.c_int, _U32, _P, _SZ, _P]),
+    ("tq_gather_qmv", ctypes.c_int,
+     [_QW, _P, _I32, _P, ctypes.c_int, _P, ctypes.c_int, _U32, _P, _SZ, _P]),
+    ("tq_multi_gather_qmv", ctypes.c_int,
+     [_QW, _P, _I64, _P, ctypes.c_int, _P, ctypes.c_int, _U32, _P, _SZ, _P]),
+    ("tq_gather_qmm", ctypes.c_int,
+     [_QW, _P, ctypes.c_int, _I64, _P, _P, _I64, _P, ctypes.c_int, _U32, _P, _SZ, _P]),
+    ("tq_last_error", ctypes.c_char_p, []),
+]
+
+
+def lib():
+    """The loaded libtq.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m rotation_lloyd_max_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, res, args in SIGNATURES:
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        raise TqError(status, lib().tq_last_error().decode())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _dt(t):
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+def words_per_row(K, levels):
+    return int(lib().tq_words_per_row(K, levels))
+
+
+def codebook(levels):
+    """(centroids, thresholds) as float32 numpy arrays, from the library."""
+    c = np.zeros(16, dtype=np.float32)
+    t = np.zeros(15, dtype=np.float32)
+    _check(lib().tq_codebook(levels, c.ctypes.data, t.ctypes.data))
+    return c[:levels].copy(), t[:levels - 1].copy()
+
+
+def signs(seed, K, device="cuda"):
+    """Rotation sign bits for (seed, K) as an int32 tensor of ceil(K/32) words."""
+    out = torch.empty((K + 31) // 32, dtype=torch.int32, device=device)
+    _check(lib().tq_signs(seed, K, _ptr(out), _stream()))
+    return out
+
+
+@dataclass
+class QWeight:
+    """Packed weight of E experts of N x K: codes int32 [E, N, wpr] (uint32 bit patterns),
+    scales float16 [E, N, K/group], signs int32 [ceil(K/32)]."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    signs: torch.Tensor
+    levels: int
+    group: int
+    K: int
+    N: int
+    E: int
+    seed: int
+
+    def desc(self):
+        return _QWeight(self.codes.data_ptr(), self.scales.data_ptr(), self.signs.data_ptr(),
+                        self.levels, self.group, self.K, self.N, self.E, self.seed)
+
+    def expert(self, e):
+        """View of expert e as a dense (E = 1) weight."""
+        return QWeight(self.codes[e:e + 1], self.scales[e:e + 1], self.signs, self.levels,
+                       self.group, self.K, self.N, 1, self.seed)
+
+
+def encode(W, levels, group, seed, out=None):
+    """Quantize W ([N, K] or [E, N, K], float32/bfloat16/float16 on the GPU)."""
+    if W.dim() == 2:
+        W = W.unsqueeze(0)
+    W = W.contiguous()
+    E, N, K = W.shape
+    wpr = words_per_row(K, levels)
+    if out is None:
+        codes = torch.empty((E, N, wpr), dtype=torch.int32, device=W.device)
+        scales = torch.empty((E, N, K // group), dtype=torch.float16, device=W.device)
+        sg = signs(seed, K, W.device)
+    else:
+        codes, scales, sg = out.codes, out.scales, out.signs
+    _check(lib().tq_encode(_ptr(W), _dt(W), E * N, K, levels, group, seed, _ptr(codes),
+                           _ptr(scales), _stream()))
+    return QWeight(codes, scales, sg, levels, group, K, N, E, seed)
+
+
+def fwht(x, seed, out_dtype=torch.float32):
+    """R x for each row of x ([rows, K])."""
+    x = x.contiguous()
+    K = x.shape[-1]
+    rows = x.numel() // K
+    out = torch.empty(x.shape, dtype=out_dtype, device=x.device)
+    _check(lib().tq_fwht(_ptr(x), _dt(x), rows, K, seed, _ptr(out), _dt(out), _stream()))
+    return out
+
+
+def workspace_bytes(op, qw, count=0, T=0):
+    d = qw.desc()
+    n = lib().tq_workspace_bytes(op, ctypes.byref(d), count, T)
+    if n == ctypes.c_size_t(-1).value:
+        raise TqError(-1, lib().tq_last_error().decode())
+    return int(n)
+
+
+def _workspace(nbytes, device):
+    if nbytes == 0:
+        return None
+    # int64 storage keeps torch's (256-byte aligned) allocation; size in 8-byte units
+    return torch.empty((nbytes + 7) // 8, dtype=torch.int64, device=device)
+
+
+def qmv(qw, x, out_dtype=torch.float32, rotated=False, out=None):
+    x = x.contiguous()
+    y = out if out is not None else torch.empty(qw.N, dtype=out_dtype, device=x.device)
+    d = qw.desc()
+    _check(lib().tq_qmv(ctypes.byref(d), _ptr(x), _dt(x), _ptr(y), _dt(y),
+                        X_ROTATED if rotated else 0, None, 0, _stream()))
+    return y
+
+
+def gather_qmv(qw, ids, x, out_dtype=torch.float32, rotated=False, out=None):
+    x = x.contiguous()
+    ids = ids.to(torch.int32).contiguous()
+    n = ids.numel()
+    y = out if out is not None else torch.empty((n, qw.N), dtype=out_dtype, device=x.device)
+    d = qw.desc()
+    _check(lib().tq_gather_qmv(ctypes.byref(d), _ptr(ids), n, _ptr(x), _dt(x), _ptr(y), _dt(y),
+                               X_ROTATED if rotated else 0, None, 0, _stream()))
+    return y
+
+
+def multi_gather_qmv(qw, ids, X, out_dtype=torch.float32, rotated=False, out=None, ws=None):
+    X = X.contiguous()
+    ids = ids.to(torch.int32).contiguous()
+    P = ids.numel()
+    y = out if out is not None else torch.empty((P, qw.N), dtype=out_dtype, device=X.device)
+    nbytes = workspace_bytes(OP_MULTI_GATHER_QMV, qw, P)
+    if ws is None:
+        ws = _workspace(nbytes, X.device)
+    d = qw.desc()
+    _check(lib().tq_multi_gather_qmv(ctypes.byref(d), _ptr(ids), P, _ptr(X), _dt(X), _ptr(y),
+                                     _dt(y), X_ROTATED if rotated else 0, _ptr(ws), nbytes,
+                                     _stream()))
+    return y
+
+
+def gather_qmm(qw, X, row_token, offsets, out_dtype=torch.float32, rotated=False, out=None,
+               ws=None):
+    X = X.contiguous()
+    row_token = row_token.to(torch.int32).contiguous()
+    offsets = offsets.to(torch.int32).contiguous()
+    T = X.shape[0]
+    M = row_token.numel()
+    y = out if out is not None else torch.empty((M, qw.N), dtype=out_dtype, device=X.device)
+    nbytes = workspace_bytes(OP_GATHER_QMM, qw, M, T)
+    if ws is None:
+        ws = _workspace(nbytes, X.device)
+    d = qw.desc()
+    _check(lib().tq_gather_qmm(ctypes.byref(d), _ptr(X), _dt(X), T, _ptr(row_token),
+                               _ptr(offsets), M, _ptr(y), _dt(y),
+                               X_ROTATED if rotated else 0, _ptr(ws), nbytes, _stream()))
+    return y

@@ -1,0 +1,239 @@
+// Device-side building blocks shared by the libtq kernels (gfx950, wave64).
+//
+// * SplitMix64 counter form for the rotation signs.
+// * The m-point Hadamard factors (Paley I for m = 12, 20; Paley II for m = 28) as
+//   compile-time sign tables, and the Sylvester transform as radix-2^r butterfly passes
+//   over a row held in LDS. Together they apply H_K = H_m (x) H_{2^k}, the Hadamard matrix
+//   of the rotation in turboquant-mlx "How it works", "Quantizing a weight, with no data"
+//   (first bullet) and "Running a quantized layer" (the input is rotated the same way).
+// * fp16 / bf16 conversions with explicit rounding.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq {
+
+constexpr int kBlock = 256;  // threads per workgroup for every libtq kernel
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------------------
+// Rotation signs: SplitMix64 output i of the generator seeded with `seed` is
+// mix64(seed + (i + 1) * golden_gamma); s_i = -1 when its top bit is set.
+__host__ __device__ __forceinline__ uint64_t splitmix64_at(uint64_t seed, uint64_t i) {
+  uint64_t z = seed + (i + 1) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// ---------------------------------------------------------------------------------------
+// m-point Hadamard factors, evaluated at compile time.
+//   chi: quadratic character mod prime q; Jacobsthal Q[a][b] = chi(a - b).
+//   Paley I  (q = 3 mod 4): H = I + [[0, 1^T], [-1, Q]]                    order q + 1
+//   Paley II (q = 1 mod 4): H = S (x) [[1,1],[1,-1]] + I (x) [[1,-1],[-1,-1]],
+//                           S = [[0, 1^T], [1, Q]]                          order 2(q + 1)
+constexpr int qchar(int a, int q) {
+  a %= q;
+  if (a < 0) a += q;
+  if (a == 0) return 0;
+  for (int x = 1; x < q; ++x)
+    if ((x * x) % q == a) return 1;
+  return -1;
+}
+
+constexpr int paley1_entry(int q, int r, int c) {
+  int cm = 0;
+  if (r == 0 && c == 0) cm = 0;
+  else if (r == 0) cm = 1;
+  else if (c == 0) cm = -1;
+  else cm = qchar((r - 1) - (c - 1), q);
+  return (r == c ? 1 : 0) + cm;
+}
+
+constexpr int paley2_entry(int q, int r, int c) {
+  const int R = r / 2, C = c / 2, i = r % 2, j = c % 2;
+  int s = 0;
+  if (R == 0 && C == 0) s = 0;
+  else if (R == 0 || C == 0) s = 1;
+  else s = qchar((R - 1) - (C - 1), q);
+  const int a = (i == 1 && j == 1) ? -1 : 1;  // [[1, 1], [1, -1]]
+  const int b = (i == 0 && j == 0) ? 1 : -1;  // [[1, -1], [-1, -1]]
+  return s * a + (R == C ? b : 0);
+}
+
+constexpr int hadamard_entry(int m, int r, int c) {
+  return m == 1 ? 1 : m == 12 ? paley1_entry(11, r, c)
+                    : m == 20 ? paley1_entry(19, r, c)
+                              : paley2_entry(13, r, c);
+}
+
+template <int M>
+struct HadamardFactor {
+  float sgn[M][M];  // H_m[r][c] as +-1.0f
+  constexpr HadamardFactor() : sgn{} {
+    for (int r = 0; r < M; ++r)
+      for (int c = 0; c < M; ++c) sgn[r][c] = hadamard_entry(M, r, c) < 0 ? -1.0f : 1.0f;
+  }
+};
+
+template <int M>
+struct HadamardTable {
+  static constexpr HadamardFactor<M> value{};
+};
+
+// ---------------------------------------------------------------------------------------
+// Sylvester transform (unnormalized) along contiguous runs of length P (a power of two)
+// of buf[0 .. total), in place in LDS, by radix-2^R passes: a pass of stride h combines
+// the 2^R elements base + j*h, doing R butterfly stages in registers. All threads of the
+// block take part; the caller synchronizes before and the function synchronizes after
+// every pass.
+template <typename T, int R>
+__device__ __forceinline__ void sylvester_pass(T* buf, int total, int h) {
+  constexpr int n = 1 << R;
+  const int ngroups = total >> R;
+  for (int g = threadIdx.x; g < ngroups; g += blockDim.x) {
+    const int blk = g / h, off = g - blk * h;
+    T* base = buf + blk * (h << R) + off;
+    T v[n];
+#pragma unroll
+    for (int j = 0; j < n; ++j) v[j] = base[j * h];
+#pragma unroll
+    for (int s = 0; s < R; ++s) {
+#pragma unroll
+      for (int j = 0; j < n; ++j) {
+        if ((j >> s) & 1) continue;
+        const T a = v[j], b = v[j + (1 << s)];
+        v[j] = a + b;
+        v[j + (1 << s)] = a - b;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < n; ++j) base[j * h] = v[j];
+  }
+  __syncthreads();
+}
+
+template <typename T>
+__device__ __forceinline__ void sylvester_lds(T* buf, int total, int P) {
+  int h = 1;
+  while (h < P) {
+    const int left = __builtin_ctz(P / h);
+    if (left >= 4) { sylvester_pass<T, 4>(buf, total, h); h <<= 4; }
+    else if (left == 3) { sylvester_pass<T, 3>(buf, total, h); h <<= 3; }
+    else if (left == 2) { sylvester_pass<T, 2>(buf, total, h); h <<= 2; }
+    else { sylvester_pass<T, 1>(buf, total, h); h <<= 1; }
+  }
+}
+
+// H_m along the strided dimension: row r of `nrows` rows of length M*P, element (a, b) at
+// r*M*P + a*P + b; y[a][b] = sum_a' H_m[a][a'] x[a'][b]. The outputs are produced one at a
+// time from a table of +-1 factors read with uniform (scalar) loads, which keeps register
+// use at about M values per lane; multiplying by +-1 is exact.
+template <typename T, int M>
+__device__ __forceinline__ void hadamard_m_lds(T* buf, int nrows, int P) {
+  const float(*sgn)[M] = HadamardTable<M>::value.sgn;
+  const int cols = nrows * P;
+  for (int col = threadIdx.x; col < cols; col += blockDim.x) {
+    const int r = col / P, b = col - r * P;
+    T* base = buf + r * M * P + b;
+    T x[M];
+#pragma unroll
+    for (int a = 0; a < M; ++a) x[a] = base[a * P];
+#pragma unroll 1
+    for (int a = 0; a < M; ++a) {
+      T acc = 0;
+#pragma unroll
+      for (int c = 0; c < M; ++c) acc += static_cast<T>(sgn[a][c]) * x[c];
+      base[a * P] = acc;
+    }
+  }
+  __syncthreads();
+}
+
+// Full unnormalized H_K = H_m (x) H_P on `nrows` rows of length m*P held in LDS.
+template <typename T>
+__device__ __forceinline__ void hadamard_lds(T* buf, int nrows, int m, int P) {
+  sylvester_lds<T>(buf, nrows * m * P, P);
+  switch (m) {
+    case 12: hadamard_m_lds<T, 12>(buf, nrows, P); break;
+    case 20: hadamard_m_lds<T, 20>(buf, nrows, P); break;
+    case 28: hadamard_m_lds<T, 28>(buf, nrows, P); break;
+    default: break;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Conversions.
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ uint16_t float_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return static_cast<uint16_t>((u >> 16) | ((u & 0xffff) ? 0x40 : 0));
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+__device__ __forceinline__ float half_bits_to_float(uint16_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+__device__ __forceinline__ uint16_t float_to_half_rne(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+
+// fp64 -> fp16 bits, round to nearest even in one step (no double rounding through fp32),
+// saturating at 65504. Input is >= 0 (an RMS) or NaN.
+__device__ __forceinline__ uint16_t double_to_half_rne_sat(double r) {
+  if (!(r < 65520.0)) return (r != r) ? 0x7e00 : 0x7bff;
+  if (r <= 0.0) return 0;
+  const uint64_t bits = static_cast<uint64_t>(__double_as_longlong(r));
+  const int e = static_cast<int>((bits >> 52) & 0x7ff) - 1023;
+  const uint64_t mant = (bits & ((1ull << 52) - 1)) | ((bits >> 52) & 0x7ff ? (1ull << 52) : 0);
+  // drop `shift` low bits of the 53-bit significand: normal results keep 11 bits,
+  // subnormal ones are multiples of 2^-24
+  const int shift = (e >= -14) ? 42 : (28 - e);
+  uint64_t q;
+  if (shift >= 64) {
+    q = 0;
+  } else {
+    q = mant >> shift;
+    const uint64_t rem = mant & ((1ull << shift) - 1);
+    const uint64_t half = 1ull << (shift - 1);
+    if (rem > half || (rem == half && (q & 1))) ++q;
+  }
+  if (e >= -14) return static_cast<uint16_t>(((e + 15) << 10) + static_cast<int>(q) - 1024);
+  return static_cast<uint16_t>(q);
+}
+
+template <int DT>
+__device__ __forceinline__ float load_elem(const void* p, int64_t i) {
+  if constexpr (DT == 0) return static_cast<const float*>(p)[i];
+  else if constexpr (DT == 1) return bf16_bits_to_float(static_cast<const uint16_t*>(p)[i]);
+  else return half_bits_to_float(static_cast<const uint16_t*>(p)[i]);
+}
+
+__device__ __forceinline__ float load_any(const void* p, int dt, int64_t i) {
+  return dt == 0 ? load_elem<0>(p, i) : dt == 1 ? load_elem<1>(p, i) : load_elem<2>(p, i);
+}
+
+__device__ __forceinline__ void store_any(void* p, int dt, int64_t i, float v) {
+  if (dt == 0) static_cast<float*>(p)[i] = v;
+  else if (dt == 1) static_cast<uint16_t*>(p)[i] = float_to_bf16_rne(v);
+  else static_cast<uint16_t*>(p)[i] = float_to_half_rne(v);
+}
+
+// Block-wide max of non-negative floats; `red` is LDS scratch of at least 32 floats.
+__device__ __forceinline__ float block_max(float v, float* red) {
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float m = red[0];
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) m = fmaxf(m, red[w]);
+  __syncthreads();
+  return m;
+}
+
+}  // namespace tq

@@ -1,0 +1,58 @@
+// Declarations shared by the host entry points (tq_api.cpp) and the kernel launchers
+// (*.hip). Nothing here is part of the public interface in include/tq.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq {
+
+// A codebook as the kernels see it: centroids and thresholds in binary32, centroids also
+// as fp16 bit patterns (for the packed-fp16 decode tables). Passed by value.
+struct CodebookArgs {
+  float c[16];
+  float t[15];
+  uint16_t h[16];
+  int levels;
+};
+
+// Lloyd-Max codebook for `levels` in {3, 4, 8, 16}; nullptr otherwise.
+const CodebookArgs* codebook_for(int levels);
+
+// K = m * P with m in {1, 12, 20, 28}, P a power of two.
+bool split_dim(int64_t K, int* m, int* P);
+
+// Everything a qmv-family launch needs about the weight, resolved on the host.
+struct WeightArgs {
+  const uint32_t* codes;
+  const uint16_t* scales;
+  const uint32_t* signs;
+  int levels, group, K, N, E, wpr, m, P;
+};
+
+hipError_t launch_signs(uint64_t seed, int K, uint32_t* bits, hipStream_t s);
+
+// out[r] = R x[r]; `signbits` (device) or, when null, signs computed from `seed`.
+hipError_t launch_fwht(const void* x, int xdt, int64_t rows, int K, int m, int P,
+                       const uint32_t* signbits, uint64_t seed, void* out, int odt,
+                       hipStream_t s);
+
+hipError_t launch_encode(const void* W, int wdt, int64_t rows, int K, int m, int P,
+                         int levels, int group, uint64_t seed, uint32_t* codes,
+                         uint16_t* scales, hipStream_t s);
+
+// qmv (ids == nullptr, n = 1) and gather_qmv.
+hipError_t launch_qmv(const WeightArgs& w, const int32_t* ids, int n, const void* x, int xdt,
+                      bool x_rotated, void* y, int ydt, hipStream_t s);
+
+size_t multi_gather_workspace(const WeightArgs& w, int64_t P);
+hipError_t launch_multi_gather(const WeightArgs& w, const int32_t* ids, int64_t P,
+                               const void* x, int xdt, bool x_rotated, void* y, int ydt,
+                               void* ws, hipStream_t s);
+
+size_t gather_qmm_workspace(const WeightArgs& w, int64_t M, int64_t T);
+hipError_t launch_gather_qmm(const WeightArgs& w, const void* x, int xdt, int64_t T,
+                             const int32_t* row_token, const int32_t* offsets, int64_t M,
+                             bool x_rotated, void* y, int ydt, void* ws, hipStream_t s);
+
+}  // namespace tq

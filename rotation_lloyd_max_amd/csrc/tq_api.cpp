@@ -1,0 +1,349 @@
+// Host side of libtq: the C entry points declared in include/tq.h.
+//
+// Every call validates its arguments before launching anything, reports failures through a
+// negative status and a thread-local message, and never throws or aborts across the C
+// interface. The Lloyd-Max codebooks are computed here once, in double precision, by
+// Lloyd's iteration on the N(0,1) density (turboquant-mlx "How it works", "Quantizing a
+// weight, with no data", third bullet: one fixed codebook per bit width, a mathematical
+// constant; "The ternary tier (1.58 bits)": levels {-c, 0, +c}).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/tq.h"
+#include "internal.hpp"
+
+namespace tq {
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return TQ_OK;
+  return fail(TQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---- Lloyd-Max codebooks ---------------------------------------------------------------
+double normal_pdf(double x) {
+  if (std::isinf(x)) return 0.0;
+  return std::exp(-0.5 * x * x) / std::sqrt(2.0 * M_PI);
+}
+// P(X > x)
+double normal_sf(double x) {
+  if (x == INFINITY) return 0.0;
+  if (x == -INFINITY) return 1.0;
+  return 0.5 * std::erfc(x / std::sqrt(2.0));
+}
+// P(a < X <= b), evaluated on the side of 0 where it does not cancel
+double cell_mass(double a, double b) {
+  if (a >= 0.0) return normal_sf(a) - normal_sf(b);
+  if (b <= 0.0) return normal_sf(-b) - normal_sf(-a);
+  return 1.0 - normal_sf(-a) - normal_sf(b);
+}
+
+void lloyd(int L, double* c, double* t) {
+  for (int k = 0; k < L; ++k) c[k] = -2.0 + 4.0 * (k + 0.5) / L;
+  double nc[16];
+  for (int it = 0; it < 200000; ++it) {
+    for (int k = 0; k + 1 < L; ++k) t[k] = 0.5 * (c[k] + c[k + 1]);
+    for (int k = 0; k < L; ++k) {
+      const double a = k == 0 ? -INFINITY : t[k - 1];
+      const double b = k == L - 1 ? INFINITY : t[k];
+      nc[k] = (normal_pdf(a) - normal_pdf(b)) / cell_mass(a, b);
+    }
+    double delta = 0.0;
+    for (int k = 0; k < L; ++k) {
+      const double v = 0.5 * (nc[k] - nc[L - 1 - k]);  // keep the exact symmetry
+      delta = std::fmax(delta, std::fabs(v - c[k]));
+      c[k] = v;
+    }
+    if (delta < 1e-15) break;
+  }
+  for (int k = 0; k + 1 < L; ++k) t[k] = 0.5 * (c[k] + c[k + 1]);
+}
+
+CodebookArgs g_books[4];
+std::once_flag g_books_once;
+
+void init_books() {
+  const int levels[4] = {3, 4, 8, 16};
+  for (int i = 0; i < 4; ++i) {
+    CodebookArgs& b = g_books[i];
+    std::memset(&b, 0, sizeof b);
+    const int L = levels[i];
+    double c[16], t[15];
+    lloyd(L, c, t);
+    b.levels = L;
+    for (int k = 0; k < L; ++k) {
+      b.c[k] = static_cast<float>(c[k]);
+      const _Float16 h = static_cast<_Float16>(c[k]);
+      std::memcpy(&b.h[k], &h, 2);
+    }
+    for (int k = 0; k + 1 < L; ++k) b.t[k] = static_cast<float>(t[k]);
+  }
+}
+
+int64_t words_per_row(int64_t K, int levels) {
+  switch (levels) {
+    case 3: return (K + 19) / 20;
+    case 4: return (2 * K + 31) / 32;
+    case 8: return (3 * K + 31) / 32;
+    case 16: return (4 * K + 31) / 32;
+    default: return 0;
+  }
+}
+
+bool valid_dtype(int d) { return d == TQ_F32 || d == TQ_BF16 || d == TQ_F16; }
+size_t dtype_size(int d) { return d == TQ_F32 ? 4 : 2; }
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_shape(int64_t K, int levels, int group, int* m, int* P) {
+  if (levels != 3 && levels != 4 && levels != 8 && levels != 16)
+    return fail(TQ_ERR_UNSUPPORTED, "n_levels must be 3, 4, 8 or 16 (got %d)", levels);
+  if (group != 16 && group != 32 && group != 64 && group != 128)
+    return fail(TQ_ERR_UNSUPPORTED, "group must be 16, 32, 64 or 128 (got %d)", group);
+  if (K < 64 || K > 8192 || K % 32 != 0)
+    return fail(TQ_ERR_UNSUPPORTED, "K must be a multiple of 32 in [64, 8192] (got %lld)",
+                static_cast<long long>(K));
+  if (!split_dim(K, m, P))
+    return fail(TQ_ERR_UNSUPPORTED, "K=%lld is not m*2^k with m in {1, 12, 20, 28}",
+                static_cast<long long>(K));
+  if (K % group != 0)
+    return fail(TQ_ERR_UNSUPPORTED, "group %d does not divide K=%lld", group,
+                static_cast<long long>(K));
+  return TQ_OK;
+}
+
+int check_weight(const tq_qweight* w, WeightArgs* out) {
+  if (!w) return fail(TQ_ERR_ARG, "weight descriptor is NULL");
+  int m = 1, P = 1;
+  const int rc = check_shape(w->K, w->n_levels, w->group, &m, &P);
+  if (rc != TQ_OK) return rc;
+  if (w->N < 0 || w->N > (1 << 24)) return fail(TQ_ERR_ARG, "N out of range");
+  if (w->E < 1 || w->E > 8192) return fail(TQ_ERR_ARG, "E must be in [1, 8192]");
+  if (w->N > 0) {
+    if (!w->codes || !w->scales || !w->signs)
+      return fail(TQ_ERR_ARG, "codes, scales and signs must be non-NULL");
+    if (!aligned(w->codes, 16)) return fail(TQ_ERR_ALIGN, "codes must be 16-byte aligned");
+    if (!aligned(w->scales, 2) || !aligned(w->signs, 4))
+      return fail(TQ_ERR_ALIGN, "scales/signs misaligned");
+  }
+  out->codes = w->codes;
+  out->scales = w->scales;
+  out->signs = w->signs;
+  out->levels = w->n_levels;
+  out->group = w->group;
+  out->K = static_cast<int>(w->K);
+  out->N = static_cast<int>(w->N);
+  out->E = static_cast<int>(w->E);
+  out->wpr = static_cast<int>(words_per_row(w->K, w->n_levels));
+  out->m = m;
+  out->P = P;
+  return TQ_OK;
+}
+
+int check_io(const void* x, int xdt, const void* y, int ydt, bool need) {
+  if (!valid_dtype(xdt) || !valid_dtype(ydt)) return fail(TQ_ERR_ARG, "bad dtype");
+  if (!need) return TQ_OK;
+  if (!x || !y) return fail(TQ_ERR_ARG, "x and y must be non-NULL");
+  if (!aligned(x, dtype_size(xdt)) || !aligned(y, dtype_size(ydt)))
+    return fail(TQ_ERR_ALIGN, "x or y misaligned for its dtype");
+  return TQ_OK;
+}
+
+}  // namespace
+
+const CodebookArgs* codebook_for(int levels) {
+  std::call_once(g_books_once, init_books);
+  switch (levels) {
+    case 3: return &g_books[0];
+    case 4: return &g_books[1];
+    case 8: return &g_books[2];
+    case 16: return &g_books[3];
+    default: return nullptr;
+  }
+}
+
+bool split_dim(int64_t K, int* m, int* P) {
+  const int ms[4] = {1, 12, 20, 28};
+  for (int i = 0; i < 4; ++i) {
+    if (K % ms[i] != 0) continue;
+    const int64_t p = K / ms[i];
+    if (p >= 1 && (p & (p - 1)) == 0) {
+      *m = ms[i];
+      *P = static_cast<int>(p);
+      return true;
+    }
+  }
+  return false;
+}
+
+}  // namespace tq
+
+using namespace tq;
+
+extern "C" {
+
+int64_t tq_words_per_row(int64_t K, int32_t n_levels) {
+  if (K <= 0) return 0;
+  return words_per_row(K, n_levels);
+}
+
+int tq_codebook(int32_t n_levels, float* centroids, float* thresholds) {
+  const CodebookArgs* b = codebook_for(n_levels);
+  if (!b) return fail(TQ_ERR_UNSUPPORTED, "n_levels must be 3, 4, 8 or 16 (got %d)", n_levels);
+  if (!centroids) return fail(TQ_ERR_ARG, "centroids is NULL");
+  std::memcpy(centroids, b->c, sizeof(float) * n_levels);
+  if (thresholds) std::memcpy(thresholds, b->t, sizeof(float) * (n_levels - 1));
+  return TQ_OK;
+}
+
+int tq_signs(uint64_t seed, int64_t K, uint32_t* bits, void* stream) {
+  if (K <= 0 || K > (1 << 24)) return fail(TQ_ERR_ARG, "K out of range");
+  if (!bits) return fail(TQ_ERR_ARG, "bits is NULL");
+  if (!aligned(bits, 4)) return fail(TQ_ERR_ALIGN, "bits must be 4-byte aligned");
+  return hip_status(launch_signs(seed, static_cast<int>(K), bits, static_cast<hipStream_t>(stream)),
+                    "tq_signs");
+}
+
+int tq_encode(const void* W, tq_dtype w_dtype, int64_t rows, int64_t K, int32_t n_levels,
+              int32_t group, uint64_t seed, uint32_t* codes, uint16_t* scales, void* stream) {
+  int m = 1, P = 1;
+  const int rc = check_shape(K, n_levels, group, &m, &P);
+  if (rc != TQ_OK) return rc;
+  if (!valid_dtype(w_dtype)) return fail(TQ_ERR_ARG, "bad weight dtype");
+  if (rows < 0) return fail(TQ_ERR_ARG, "rows must be >= 0");
+  if (rows == 0) return TQ_OK;
+  if (!W || !codes || !scales) return fail(TQ_ERR_ARG, "W, codes and scales must be non-NULL");
+  if (!aligned(W, dtype_size(w_dtype)) || !aligned(codes, 4) || !aligned(scales, 2))
+    return fail(TQ_ERR_ALIGN, "W, codes or scales misaligned");
+  return hip_status(launch_encode(W, w_dtype, rows, static_cast<int>(K), m, P, n_levels, group,
+                                  seed, codes, scales, static_cast<hipStream_t>(stream)),
+                    "tq_encode");
+}
+
+int tq_fwht(const void* x, tq_dtype x_dtype, int64_t rows, int64_t K, uint64_t seed, void* out,
+            tq_dtype out_dtype, void* stream) {
+  int m = 1, P = 1;
+  if (K < 64 || K > 8192 || K % 32 != 0 || !split_dim(K, &m, &P))
+    return fail(TQ_ERR_UNSUPPORTED, "K must be m*2^k (m in {1,12,20,28}), a multiple of 32 in [64, 8192]");
+  if (rows < 0) return fail(TQ_ERR_ARG, "rows must be >= 0");
+  const int rc = check_io(x, x_dtype, out, out_dtype, rows > 0);
+  if (rc != TQ_OK) return rc;
+  if (rows == 0) return TQ_OK;
+  return hip_status(launch_fwht(x, x_dtype, rows, static_cast<int>(K), m, P, nullptr, seed, out,
+                                out_dtype, static_cast<hipStream_t>(stream)),
+                    "tq_fwht");
+}
+
+size_t tq_workspace_bytes(int32_t op, const tq_qweight* w, int64_t count, int64_t T) {
+  WeightArgs a{};
+  if (check_weight(w, &a) != TQ_OK || count < 0 || T < 0) return SIZE_MAX;
+  switch (op) {
+    case TQ_OP_QMV:
+    case TQ_OP_GATHER_QMV: return 0;
+    case TQ_OP_MULTI_GATHER_QMV: return multi_gather_workspace(a, count);
+    case TQ_OP_GATHER_QMM: return gather_qmm_workspace(a, count, T);
+    default: fail(TQ_ERR_ARG, "unknown op %d", op); return SIZE_MAX;
+  }
+}
+
+int tq_qmv(const tq_qweight* w, const void* x, tq_dtype x_dtype, void* y, tq_dtype y_dtype,
+           uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  WeightArgs a{};
+  int rc = check_weight(w, &a);
+  if (rc != TQ_OK) return rc;
+  if (a.E != 1) return fail(TQ_ERR_ARG, "tq_qmv needs E = 1 (use tq_gather_qmv for experts)");
+  rc = check_io(x, x_dtype, y, y_dtype, a.N > 0);
+  if (rc != TQ_OK) return rc;
+  return hip_status(launch_qmv(a, nullptr, 1, x, x_dtype, (flags & TQ_X_ROTATED) != 0, y, y_dtype,
+                               static_cast<hipStream_t>(stream)),
+                    "tq_qmv");
+}
+
+int tq_gather_qmv(const tq_qweight* w, const int32_t* ids, int32_t n, const void* x,
+                  tq_dtype x_dtype, void* y, tq_dtype y_dtype, uint32_t flags, void* ws,
+                  size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  WeightArgs a{};
+  int rc = check_weight(w, &a);
+  if (rc != TQ_OK) return rc;
+  if (n < 0) return fail(TQ_ERR_ARG, "n must be >= 0");
+  if (n > 0 && !ids) return fail(TQ_ERR_ARG, "ids is NULL");
+  if (n > 0 && !aligned(ids, 4)) return fail(TQ_ERR_ALIGN, "ids misaligned");
+  rc = check_io(x, x_dtype, y, y_dtype, n > 0 && a.N > 0);
+  if (rc != TQ_OK) return rc;
+  return hip_status(launch_qmv(a, ids, n, x, x_dtype, (flags & TQ_X_ROTATED) != 0, y, y_dtype,
+                               static_cast<hipStream_t>(stream)),
+                    "tq_gather_qmv");
+}
+
+int tq_multi_gather_qmv(const tq_qweight* w, const int32_t* ids, int64_t P, const void* x,
+                        tq_dtype x_dtype, void* y, tq_dtype y_dtype, uint32_t flags, void* ws,
+                        size_t ws_bytes, void* stream) {
+  WeightArgs a{};
+  int rc = check_weight(w, &a);
+  if (rc != TQ_OK) return rc;
+  if (P < 0 || P > (1 << 30)) return fail(TQ_ERR_ARG, "P out of range");
+  if (P > 0 && !ids) return fail(TQ_ERR_ARG, "ids is NULL");
+  if (P > 0 && !aligned(ids, 4)) return fail(TQ_ERR_ALIGN, "ids misaligned");
+  rc = check_io(x, x_dtype, y, y_dtype, P > 0 && a.N > 0);
+  if (rc != TQ_OK) return rc;
+  if (P == 0 || a.N == 0) return TQ_OK;
+  const size_t need = multi_gather_workspace(a, P);
+  if (!ws || ws_bytes < need)
+    return fail(TQ_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  if (!aligned(ws, 16)) return fail(TQ_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return hip_status(launch_multi_gather(a, ids, P, x, x_dtype, (flags & TQ_X_ROTATED) != 0, y,
+                                        y_dtype, ws, static_cast<hipStream_t>(stream)),
+                    "tq_multi_gather_qmv");
+}
+
+int tq_gather_qmm(const tq_qweight* w, const void* x, tq_dtype x_dtype, int64_t T,
+                  const int32_t* row_token, const int32_t* expert_offsets, int64_t M, void* y,
+                  tq_dtype y_dtype, uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  WeightArgs a{};
+  int rc = check_weight(w, &a);
+  if (rc != TQ_OK) return rc;
+  if (T < 0 || M < 0 || M > (1ll << 31) - 1 || T > (1ll << 31) - 1)
+    return fail(TQ_ERR_ARG, "T and M must be in [0, 2^31)");
+  rc = check_io(x, x_dtype, y, y_dtype, M > 0 && a.N > 0);
+  if (rc != TQ_OK) return rc;
+  if (M == 0 || a.N == 0) return TQ_OK;
+  if (T == 0) return fail(TQ_ERR_ARG, "T must be > 0 when M > 0");
+  if (!row_token || !expert_offsets) return fail(TQ_ERR_ARG, "row_token and expert_offsets needed");
+  if (!aligned(row_token, 4) || !aligned(expert_offsets, 4))
+    return fail(TQ_ERR_ALIGN, "row_token/expert_offsets misaligned");
+  const bool rotated = (flags & TQ_X_ROTATED) != 0;
+  if (rotated && x_dtype == TQ_BF16 && !aligned(x, 16))
+    return fail(TQ_ERR_ALIGN, "rotated bf16 x must be 16-byte aligned");
+  const size_t need = gather_qmm_workspace(a, M, T);
+  if (!ws || ws_bytes < need)
+    return fail(TQ_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  if (!aligned(ws, 256)) return fail(TQ_ERR_ALIGN, "workspace must be 256-byte aligned");
+  return hip_status(launch_gather_qmm(a, x, x_dtype, T, row_token, expert_offsets, M, rotated, y,
+                                      y_dtype, ws, static_cast<hipStream_t>(stream)),
+                    "tq_gather_qmm");
+}
+
+const char* tq_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

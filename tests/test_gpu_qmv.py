@@ -1,0 +1,266 @@
+"""GPU parity of the qmv family (tq_qmv, tq_gather_qmv, tq_multi_gather_qmv, tq_gather_qmm)
+against the oracle's dequantize-then-multiply in fp64, through the C ABI."""
+
+import numpy as np
+import pytest
+import torch
+
+import rotation_lloyd_max_amd as tq
+import workloads as wl
+from oracle import encode as oenc
+from oracle import hadamard as ohd
+from oracle import ops as oops
+from parity import as_f64, check_codes, check_outputs, qmv_reference, torch_to_np
+from test_gpu_encode import to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def encode_both(W_dev, levels, group, seed):
+    """GPU encode, and the oracle's encode of the same bytes."""
+    qw = tq.encode(W_dev, levels, group, seed)
+    torch.cuda.synchronize()
+    rows = W_dev.numel() // W_dev.shape[-1]
+    ref = oenc.encode(as_f64(W_dev).reshape(rows, -1), levels, group, seed)
+    return qw, ref
+
+
+def gpu_arrays(qw):
+    E = qw.E
+    return (torch_to_np(qw.codes).reshape(E, qw.N, -1), torch_to_np(qw.scales).reshape(E, qw.N, -1))
+
+
+def check_qmv_against_oracle(qw, ref, x_dev, y, tag):
+    codes, scales = gpu_arrays(qw)
+    x = as_f64(x_dev)
+    yg = as_f64(y)
+    want, bound = qmv_reference(codes[0], scales[0], qw.levels, qw.group, qw.K, qw.seed, x)
+    worst = check_outputs(yg, want, bound, tag + " (GPU codes)")
+    want2, bound2 = qmv_reference(ref.codes, ref.scales, qw.levels, qw.group, qw.K, qw.seed, x)
+    check_outputs(yg, want2, bound2, tag + " (oracle codes)")
+    return worst
+
+
+def test_single_layer_end_to_end():
+    # 256 x 512 fp32 weight, rotation signs from seed 0, 4-bit Lloyd-Max, group 64; one
+    # fp32 activation; the result equals dequantize-then-multiply
+    c = wl.C1
+    p = c.projs[0]
+    W = torch.from_numpy(wl.student_rows(wl.rng(c.cid, wl.T_W), p.N, p.K)).cuda()
+    x = torch.from_numpy(wl.gaussian(wl.rng(c.cid, wl.T_X), 1, p.K)[0]).cuda()
+    qw, ref = encode_both(W, p.levels, p.group, p.seed)
+    assert check_codes(torch_to_np(qw.codes).reshape(p.N, -1), ref, p.levels, p.K) == 0
+    y = tq.qmv(qw, x)
+    torch.cuda.synchronize()
+    check_qmv_against_oracle(qw, ref, x, y, "C1")
+    # brute force in the original basis: (R^T w'_hat) . x
+    yb = oops.qmv_unrotated(ref.codes, ref.scales, p.levels, p.group, p.K, p.seed, as_f64(x))
+    b = oops.row_bound(ref.codes, ref.scales, p.levels, p.group, p.K, as_f64(x))
+    check_outputs(as_f64(y), yb, b, "C1 unrotated")
+
+
+def test_dense_decode_full_size():
+    # 4096 x 4096 bf16, 3-bit g128, bf16 activation with 8 outlier channels x20
+    c = wl.C2
+    p = c.projs[0]
+    W = to_dev(wl.student_rows(wl.rng(c.cid, wl.T_W), p.N, p.K), torch.bfloat16)
+    x = to_dev(wl.gaussian(wl.rng(c.cid, wl.T_X), 1, p.K, outliers=8)[0], torch.bfloat16)
+    qw, ref = encode_both(W, p.levels, p.group, p.seed)
+    n = check_codes(torch_to_np(qw.codes).reshape(p.N, -1), ref, p.levels, p.K, "C2")
+    assert n <= 16
+    y = tq.qmv(qw, x)
+    torch.cuda.synchronize()
+    check_qmv_against_oracle(qw, ref, x, y, "C2")
+
+
+FORMATS = [(L, g) for L in (3, 4, 8, 16) for g in (16, 32, 64, 128)]
+
+
+@pytest.mark.parametrize("levels,group", FORMATS)
+@pytest.mark.parametrize("K,N", [(1536, 200), (640, 77), (7168, 64), (2048, 300)])
+def test_qmv_formats(levels, group, K, N):
+    g = wl.rng(910, levels * 1000 + group, K)
+    W = to_dev(wl.student_rows(g, N, K), torch.bfloat16)
+    x = to_dev(wl.gaussian(g, 1, K, outliers=4)[0], torch.bfloat16)
+    qw, ref = encode_both(W, levels, group, seed=11)
+    y = tq.qmv(qw, x)
+    torch.cuda.synchronize()
+    check_qmv_against_oracle(qw, ref, x, y, f"L{levels} g{group} K{K} N{N}")
+
+
+@pytest.mark.parametrize("xdt", [torch.float32, torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("ydt", [torch.float32, torch.bfloat16, torch.float16])
+def test_qmv_dtypes(xdt, ydt):
+    K, N, levels, group = 768, 130, 8, 32
+    g = wl.rng(911, 0)
+    W = to_dev(wl.student_rows(g, N, K), torch.bfloat16)
+    x = to_dev(wl.gaussian(g, 1, K)[0], xdt)
+    qw, ref = encode_both(W, levels, group, seed=2)
+    y = tq.qmv(qw, x, out_dtype=ydt)
+    torch.cuda.synchronize()
+    codes, scales = gpu_arrays(qw)
+    want, bound = qmv_reference(codes[0], scales[0], levels, group, K, 2, as_f64(x))
+    out_round = {torch.float32: 0.0, torch.bfloat16: 2.0 ** -8, torch.float16: 2.0 ** -11}[ydt]
+    check_outputs(as_f64(y), want, bound + out_round * np.abs(want), f"x {xdt} y {ydt}")
+
+
+def test_qmv_pre_rotated_input():
+    K, N, levels, group = 1536, 96, 16, 64
+    g = wl.rng(912, 0)
+    W = to_dev(wl.student_rows(g, N, K), torch.bfloat16)
+    x = wl.gaussian(g, 1, K)[0].astype(np.float64)
+    xr = torch.from_numpy(ohd.rotate(x, 4).astype(np.float32)).cuda()
+    qw, ref = encode_both(W, levels, group, seed=4)
+    y = tq.qmv(qw, xr, rotated=True)
+    torch.cuda.synchronize()
+    codes, scales = gpu_arrays(qw)
+    want, bound = qmv_reference(codes[0], scales[0], levels, group, K, 4, x)
+    check_outputs(as_f64(y), want, bound + 1e-6 * np.abs(want), "rotated input")
+
+
+def test_qmv_large_input_and_zero_input():
+    K, N, levels, group = 512, 64, 16, 64
+    g = wl.rng(913, 0)
+    W = to_dev(wl.student_rows(g, N, K), torch.float32)
+    qw, ref = encode_both(W, levels, group, seed=0)
+    for scale in (1e-30, 1e4, 1e30):
+        x = torch.from_numpy(wl.gaussian(g, 1, K)[0] * np.float32(scale)).cuda()
+        y = tq.qmv(qw, x)
+        torch.cuda.synchronize()
+        check_qmv_against_oracle(qw, ref, x, y, f"x*{scale}")
+    y = tq.qmv(qw, torch.zeros(K, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.all(y == 0)
+
+
+def make_experts(cfg, E, N, K, levels, group, seed, dtype=torch.bfloat16):
+    W = torch.stack([to_dev(wl.student_rows(wl.rng(cfg, 20, e), N, K), dtype) for e in range(E)])
+    return encode_both(W, levels, group, seed)
+
+
+@pytest.mark.parametrize("levels,group,K,N", [(4, 64, 7168, 96), (16, 64, 2048, 160),
+                                              (3, 16, 768, 64), (8, 128, 4096, 64)])
+def test_gather_qmv(levels, group, K, N):
+    E = 9
+    qw, ref = make_experts(914, E, N, K, levels, group, seed=0)
+    x = to_dev(wl.gaussian(wl.rng(914, 1), 1, K)[0], torch.bfloat16)
+    ids = torch.tensor([3, 8, 0, 3, 5, 1, 7, 2], dtype=torch.int32, device="cuda")
+    y = tq.gather_qmv(qw, ids, x)
+    torch.cuda.synchronize()
+    codes, scales = gpu_arrays(qw)
+    yg = as_f64(y)
+    for k, e in enumerate(ids.tolist()):
+        want, bound = qmv_reference(codes[e], scales[e], levels, group, K, 0, as_f64(x))
+        check_outputs(yg[k], want, bound, f"slot {k} expert {e}")
+    # each slot equals a dense qmv on that expert's weights
+    y0 = tq.qmv(qw.expert(3), x)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y[0]) and torch.equal(y0, y[3])
+
+
+def test_gather_qmv_bad_id_gives_nan_rows():
+    K, N, levels, group = 512, 40, 16, 64
+    qw, _ = make_experts(915, 3, N, K, levels, group, seed=0)
+    x = to_dev(wl.gaussian(wl.rng(915, 1), 1, K)[0], torch.bfloat16)
+    ids = torch.tensor([1, 3, -1, 0], dtype=torch.int32, device="cuda")
+    y = tq.gather_qmv(qw, ids, x)
+    torch.cuda.synchronize()
+    assert torch.isnan(y[1]).all() and torch.isnan(y[2]).all()
+    assert torch.isfinite(y[0]).all() and torch.isfinite(y[3]).all()
+
+
+@pytest.mark.parametrize("levels,group,K,N", [(3, 16, 2048, 96), (3, 16, 768, 160),
+                                              (16, 64, 1536, 64), (4, 32, 7168, 48)])
+def test_multi_gather(levels, group, K, N):
+    E = 12
+    qw, _ = make_experts(916, E, N, K, levels, group, seed=1)
+    g = wl.rng(916, 2)
+    # skewed pairs: expert 5 gets 19 inputs (three batches), some experts none
+    ids = np.concatenate([np.full(19, 5), g.integers(0, E, 30), [11, 0, 0]]).astype(np.int32)
+    g.shuffle(ids)
+    P = len(ids)
+    X = to_dev(wl.gaussian(g, P, K), torch.bfloat16)
+    y = tq.multi_gather_qmv(qw, torch.from_numpy(ids).cuda(), X)
+    torch.cuda.synchronize()
+    codes, scales = gpu_arrays(qw)
+    Xf = as_f64(X)
+    yg = as_f64(y)
+    for p_ in range(P):
+        e = ids[p_]
+        want, bound = qmv_reference(codes[e], scales[e], levels, group, K, 1, Xf[p_])
+        check_outputs(yg[p_], want, bound, f"pair {p_} expert {e}")
+
+
+def test_multi_gather_bad_ids_and_empty():
+    K, N, levels, group = 512, 32, 8, 64
+    qw, _ = make_experts(917, 4, N, K, levels, group, seed=0)
+    X = to_dev(wl.gaussian(wl.rng(917, 1), 5, K), torch.bfloat16)
+    ids = torch.tensor([0, 4, 2, -7, 2], dtype=torch.int32, device="cuda")
+    y = tq.multi_gather_qmv(qw, ids, X)
+    torch.cuda.synchronize()
+    assert torch.isnan(y[1]).all() and torch.isnan(y[3]).all()
+    assert torch.isfinite(y[[0, 2, 4]]).all()
+    y0 = tq.multi_gather_qmv(qw, ids[:0], X[:0])
+    torch.cuda.synchronize()
+    assert y0.shape == (0, N)
+
+
+def routing_case(T, E, k, cfg):
+    row_token, row_expert, offsets = wl.zipf_sorted_routing(cfg, T, E, k)
+    return row_token, row_expert, offsets
+
+
+@pytest.mark.parametrize("levels,group,K,N", [(16, 128, 4096, 192), (16, 128, 1536, 320),
+                                              (8, 64, 768, 100), (3, 16, 2048, 64),
+                                              (4, 32, 640, 130)])
+def test_gather_qmm(levels, group, K, N):
+    E, T, k = 10, 96, 3
+    qw, _ = make_experts(918, E, N, K, levels, group, seed=2)
+    row_token, row_expert, offsets = routing_case(T, E, k, 918 + K)
+    X = to_dev(wl.gaussian(wl.rng(918, 3), T, K), torch.bfloat16)
+    y = tq.gather_qmm(qw, X, torch.from_numpy(row_token).cuda(), torch.from_numpy(offsets).cuda())
+    torch.cuda.synchronize()
+    codes, scales = gpu_arrays(qw)
+    Xf = as_f64(X)
+    yg = as_f64(y)
+    for e in range(E):
+        a, b = offsets[e], offsets[e + 1]
+        if b == a:
+            continue
+        want, bound = qmv_reference(codes[e], scales[e], levels, group, K, 2, Xf[row_token[a:b]])
+        check_outputs(yg[a:b], want, bound, f"expert {e}")
+
+
+def test_gather_qmm_edges():
+    # experts with no rows, an expert with more rows than one tile, rows past the end of N,
+    # an out-of-range token id (NaN row), and a pre-rotated bf16 input
+    K, N, levels, group = 512, 70, 16, 64
+    E = 5
+    qw, _ = make_experts(919, E, N, K, levels, group, seed=0)
+    T = 40
+    X = to_dev(wl.gaussian(wl.rng(919, 1), T, K), torch.bfloat16)
+    counts = [0, 150, 0, 1, 3]
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    g = wl.rng(919, 2)
+    row_token = g.integers(0, T, offsets[-1]).astype(np.int32)
+    row_token[7] = T + 5
+    y = tq.gather_qmm(qw, X, torch.from_numpy(row_token).cuda(), torch.from_numpy(offsets).cuda())
+    torch.cuda.synchronize()
+    yg = as_f64(y)
+    assert np.isnan(yg[7]).all()
+    codes, scales = gpu_arrays(qw)
+    Xf = as_f64(X)
+    for e in range(E):
+        for m in range(offsets[e], offsets[e + 1]):
+            if m == 7:
+                continue
+            want, bound = qmv_reference(codes[e], scales[e], levels, group, K, 0, Xf[row_token[m]])
+            check_outputs(yg[m], want, bound, f"row {m}")
+    # pre-rotated bf16 input gives the same rows within bf16 rounding of x'
+    Xr = to_dev(ohd.rotate(Xf, 0).astype(np.float32), torch.bfloat16)
+    y2 = tq.gather_qmm(qw, Xr, torch.from_numpy(row_token).cuda(), torch.from_numpy(offsets).cuda(),
+                       rotated=True)
+    torch.cuda.synchronize()
+    ok = np.ones(offsets[-1], bool)
+    ok[7] = False
+    assert np.allclose(as_f64(y2)[ok], yg[ok], rtol=0, atol=2e-2 * np.abs(yg[ok]).max())

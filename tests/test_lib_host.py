@@ -1,0 +1,129 @@
+"""Host-side checks of libtq.so that need no GPU.
+
+* The shared library loads and exports every function declared in include/tq.h, and the
+  binding declares a signature for each of them (no kernel is launched here).
+* The library's Lloyd-Max codebook, computed by its own C++ Lloyd iteration, equals the
+  oracle's fp64 codebook rounded once to binary32, bit for bit (centroids and thresholds).
+* Argument validation rejects bad shapes, levels, groups, dtypes, null pointers,
+  misalignment and short workspaces with the documented status, before any launch.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import rotation_lloyd_max_amd as tq
+from oracle import codebook as ocb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tq.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(tq.LIB_PATH),
+                                reason="libtq.so not built (run __graft_entry__.build())")
+
+ERR_ARG, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE = -1, -2, -3, -4
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = header_functions()
+    assert len(names) == 11, names
+    handle = ctypes.CDLL(tq.LIB_PATH)
+    for n in names:
+        assert hasattr(handle, n), n
+    assert sorted(s[0] for s in tq.SIGNATURES) == names
+
+
+@pytest.mark.parametrize("L", [3, 4, 8, 16])
+def test_codebook_matches_oracle_bitwise(L):
+    c, t = tq.codebook(L)
+    oc, ot, _, _ = ocb.lloyd_max(L)
+    np.testing.assert_array_equal(c.view(np.uint32), oc.astype(np.float32).view(np.uint32))
+    np.testing.assert_array_equal(t.view(np.uint32), ot.astype(np.float32).view(np.uint32))
+
+
+def test_codebook_rejects_other_levels():
+    for L in (0, 1, 2, 5, 32):
+        with pytest.raises(tq.TqError) as e:
+            tq.codebook(L)
+        assert e.value.status == ERR_UNSUPPORTED
+
+
+def test_words_per_row():
+    assert tq.words_per_row(4096, 8) == 384
+    assert tq.words_per_row(7168, 4) == 448
+    assert tq.words_per_row(2048, 3) == 103
+    assert tq.words_per_row(512, 16) == 64
+    assert tq.words_per_row(512, 5) == 0
+
+
+def desc(**kw):
+    d = dict(codes=16, scales=16, signs=16, n_levels=16, group=64, K=512, N=4, E=1, seed=0)
+    d.update(kw)
+    return tq._QWeight(d["codes"], d["scales"], d["signs"], d["n_levels"], d["group"], d["K"],
+                       d["N"], d["E"], d["seed"])
+
+
+def qmv_status(d, x=16, xdt=0, y=16, ydt=0):
+    return tq.lib().tq_qmv(ctypes.byref(d) if d is not None else None, x, xdt, y, ydt, 0, None,
+                           0, None)
+
+
+def test_validation_statuses():
+    L = tq.lib()
+    assert qmv_status(None) == ERR_ARG
+    assert qmv_status(desc(n_levels=5)) == ERR_UNSUPPORTED
+    assert qmv_status(desc(group=8)) == ERR_UNSUPPORTED
+    assert qmv_status(desc(K=4864)) == ERR_UNSUPPORTED     # 4864 = 19 * 256
+    assert qmv_status(desc(K=16384)) == ERR_UNSUPPORTED    # above the size limit
+    assert qmv_status(desc(K=96, group=64)) == ERR_UNSUPPORTED  # group does not divide K
+    assert qmv_status(desc(codes=0)) == ERR_ARG
+    assert qmv_status(desc(codes=8)) == ERR_ALIGN
+    assert qmv_status(desc(E=2)) == ERR_ARG                # dense qmv needs E = 1
+    assert qmv_status(desc(), xdt=7) == ERR_ARG
+    assert qmv_status(desc(), x=0) == ERR_ARG
+    assert qmv_status(desc(), x=18, xdt=0) == ERR_ALIGN
+    assert b"group" in L.tq_last_error() or L.tq_last_error()
+    # multi_gather: short workspace
+    d = desc(E=4)
+    need = L.tq_workspace_bytes(3, ctypes.byref(d), 10, 0)
+    assert 0 < need < 1 << 20
+    assert L.tq_multi_gather_qmv(ctypes.byref(d), 16, 10, 16, 0, 16, 0, 0, 256, need - 1,
+                                 None) == ERR_WORKSPACE
+    # gather_qmm: workspace alignment and size
+    need = L.tq_workspace_bytes(4, ctypes.byref(d), 100, 50)
+    assert need >= 50 * 512 * 2
+    assert L.tq_gather_qmm(ctypes.byref(d), 16, 1, 50, 16, 16, 100, 16, 0, 0, 256, 10,
+                           None) == ERR_WORKSPACE
+    assert L.tq_gather_qmm(ctypes.byref(d), 16, 1, 50, 16, 16, 100, 16, 0, 0, 128, need,
+                           None) == ERR_ALIGN
+    # encode / fwht / signs
+    assert L.tq_encode(16, 0, 4, 500, 16, 64, 0, 16, 16, None) == ERR_UNSUPPORTED
+    assert L.tq_encode(0, 0, 4, 512, 16, 64, 0, 16, 16, None) == ERR_ARG
+    assert L.tq_encode(16, 0, -1, 512, 16, 64, 0, 16, 16, None) == ERR_ARG
+    assert L.tq_fwht(16, 0, 2, 100, 0, 16, 0, None) == ERR_UNSUPPORTED
+    assert L.tq_signs(0, 0, 16, None) == ERR_ARG
+    # workspace query with a bad descriptor
+    assert L.tq_workspace_bytes(3, None, 1, 0) == ctypes.c_size_t(-1).value
+    assert L.tq_workspace_bytes(9, ctypes.byref(desc()), 1, 0) == ctypes.c_size_t(-1).value
+
+
+def test_empty_calls_are_no_ops():
+    L = tq.lib()
+    # zero rows / zero ids / zero pairs return OK without touching the device
+    assert L.tq_encode(0, 0, 0, 512, 16, 64, 0, 0, 0, None) == 0
+    assert L.tq_fwht(0, 0, 0, 512, 0, 0, 0, None) == 0
+    d = desc(N=0, codes=0, scales=0, signs=0)
+    assert qmv_status(d, x=0, y=0) == 0
+    d = desc(E=3)
+    assert L.tq_gather_qmv(ctypes.byref(d), None, 0, 0, 1, 0, 0, 0, None, 0, None) == 0
+    assert L.tq_multi_gather_qmv(ctypes.byref(d), None, 0, 0, 1, 0, 0, 0, None, 0, None) == 0
+    assert L.tq_gather_qmm(ctypes.byref(d), 0, 1, 0, None, None, 0, 0, 0, 0, None, 0, None) == 0
