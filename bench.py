@@ -1,0 +1,348 @@
+"""Benchmark of the hot path on one MI355X: one JSON line on stdout.
+
+Default workload (the dense decode layer): a bf16 4096 x 4096 weight with Student-t rows,
+encoded to 3-bit Lloyd-Max codes with group-128 fp16 scales; one step = encode the weight
+once + 1000 qmv calls on a batch-1 bf16 activation (N(0,1), 8 outlier channels x20). The
+1000 calls cycle over 80 separately allocated copies of the packed weight (525 MB, twice
+the 256 MB last-level cache), so every call streams its codes from HBM. Encode and the
+1000 calls are each captured once in a HIP graph and replayed, so host launch overhead is
+not in the timed region.
+
+  metric  fused qmv HBM GB/s: algorithmic bytes (packed codes + fp16 scales + bf16
+          activation = 6,561,792 B per call) of the step's 1000 calls / the step's time
+  roofline.achieved  the same bytes per call / the average qmv launch duration, from HIP
+          events around the qmv graph (includes the gaps between back-to-back kernels)
+  encode_mweights_per_s  16,777,216 weights / the encode time of a step
+  cpu_baseline  the fp64 oracle (numpy, one BLAS thread) on a bounded sample of the same
+          layer, in the same unit
+
+Other workloads (--config 3, 4, 5) time gather_qmv, multi_gather_qmv and gather_qmm for
+reference; the default line is the dense decode layer.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calls", type=int, default=1000, help="qmv calls per step")
+    return ap.parse_args()
+
+
+def cpu_baseline_qmv(W_bits, x_bits, levels, group, seed, budget_s=12.0, rows=512):
+    """Oracle encode + qmv on the first `rows` rows of the layer; qmv timed, GB/s."""
+    from threadpoolctl import threadpool_limits
+    import numpy as np
+    import workloads as wl
+    from oracle import encode as oenc
+    from oracle import ops as oops
+
+    with threadpool_limits(limits=1):
+        W = wl.bf16_bits_to_f64(W_bits[:rows])
+        x = wl.bf16_bits_to_f64(x_bits)
+        K = W.shape[1]
+        t0 = time.perf_counter()
+        ref = oenc.encode(W, levels, group, seed)
+        t_enc = time.perf_counter() - t0
+        n, t_q = 0, 0.0
+        while t_q < budget_s and n < 50:
+            t0 = time.perf_counter()
+            oops.qmv(ref.codes, ref.scales, levels, group, K, seed, x)
+            t_q += time.perf_counter() - t0
+            n += 1
+    nbytes = ref.codes.nbytes + ref.scales.nbytes + x_bits.nbytes
+    return {
+        "value": round(nbytes * n / t_q / 1e9, 6),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"oracle (numpy fp64, 1 BLAS thread) qmv of the first {rows} of 4096 rows "
+                  f"of the layer, {n} calls in {t_q:.1f} s; oracle encode of those rows "
+                  f"{rows * K / t_enc / 1e6:.3f} Mweights/s",
+        "encode_mweights_per_s": round(rows * K / t_enc / 1e6, 6),
+    }
+
+
+def bench_dense(args):
+    import numpy as np
+    import torch
+
+    import rotation_lloyd_max_amd as tq
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    c = wl.C2
+    p = c.projs[0]
+    N, K, L, G = p.N, p.K, p.levels, p.group
+    W_bits = wl.f32_to_bf16_bits(wl.student_rows(wl.rng(c.cid, wl.T_W), N, K))
+    x_bits = wl.f32_to_bf16_bits(wl.gaussian(wl.rng(c.cid, wl.T_X), 1, K, outliers=8)[0])
+    W = torch.from_numpy(W_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    ncopy = 80
+    base = tq.encode(W, L, G, p.seed)
+    copies = [base] + [tq.QWeight(base.codes.clone(), base.scales.clone(), base.signs, L, G, K,
+                                  N, 1, p.seed) for _ in range(ncopy - 1)]
+    y = torch.empty(N, dtype=torch.float32, device=dev)
+    calls = args.calls
+
+    def run_encode():
+        tq.encode(W, L, G, p.seed, out=copies[0])
+
+    def run_qmv():
+        for i in range(calls):
+            tq.qmv(copies[i % ncopy], x, out=y)
+
+    # eager once (warms the library), then capture both phases
+    run_encode()
+    run_qmv()
+    torch.cuda.synchronize()
+    g_enc, g_qmv = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_enc):
+        run_encode()
+    with torch.cuda.graph(g_qmv):
+        run_qmv()
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        g_enc.replay()
+        g_qmv.replay()
+    torch.cuda.synchronize()
+
+    steps = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record()
+        g_enc.replay()
+        ev[s][1].record()
+        g_qmv.replay()
+        ev[s][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    enc_ms = sum(e[0].elapsed_time(e[1]) for e in ev)
+    qmv_ms = sum(e[1].elapsed_time(e[2]) for e in ev)
+    total_ms = ev[0][0].elapsed_time(ev[-1][2])
+    ms_per_step = total_ms / steps
+
+    bytes_call = (N * tq.words_per_row(K, L) * 4) + (N * (K // G) * 2) + K * 2
+    value = bytes_call * calls / (ms_per_step / 1e3) / 1e9
+    avg_qmv_s = qmv_ms / 1e3 / (steps * calls)
+    achieved = bytes_call / avg_qmv_s / 1e9
+    out = {
+        "metric": "fused qmv HBM GB/s (dense decode layer, encode + 1000 cold qmv per step)",
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16*f16->f32 (decode), f64 (encode)",
+        "data": "synthetic",
+        "config": {
+            "workload": "dense decode qmv: bf16 W 4096x4096 (Student-t df=4 x lognormal rows), "
+                        "3-bit Lloyd-Max, group 128, fp16 scales; bf16 x N(0,1) + 8 outliers x20; "
+                        "step = encode + 1000 qmv over 80 cold copies",
+            "N": N, "K": K, "bits": 3, "group": G, "qmv_per_step": calls, "cold_copies": ncopy,
+        },
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "bytes_per_qmv": bytes_call,
+        "qmv_avg_us": round(avg_qmv_s * 1e6, 4),
+        "encode_mweights_per_s": round(N * K / (enc_ms / 1e3 / steps) / 1e6, 3),
+        "wall_s": round(wall, 4),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 3),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_qmv(W_bits, x_bits, L, G, p.seed)
+    return out
+
+
+def encode_stack(E, N, K, levels, group, seed, cfg, tensor, dev, chunk=16):
+    """Encode an expert stack whose bf16 weights are drawn on the GPU, chunk by chunk."""
+    import torch
+    import rotation_lloyd_max_amd as tq
+    import workloads as wl
+    wpr = tq.words_per_row(K, levels)
+    codes = torch.empty((E, N, wpr), dtype=torch.int32, device=dev)
+    scales = torch.empty((E, N, K // group), dtype=torch.float16, device=dev)
+    sg = tq.signs(seed, K, dev)
+    for e0 in range(0, E, chunk):
+        e1 = min(E, e0 + chunk)
+        g = wl.torch_generator(dev, cfg, tensor, e0)
+        Wc = wl.torch_student_rows(g, (e1 - e0) * N, K, dev, torch.bfloat16).view(e1 - e0, N, K)
+        part = tq.QWeight(codes[e0:e1], scales[e0:e1], sg, levels, group, K, N, e1 - e0, seed)
+        tq.encode(Wc, levels, group, seed, out=part)
+        del Wc
+    torch.cuda.synchronize()
+    return tq.QWeight(codes, scales, sg, levels, group, K, N, E, seed)
+
+
+def bench_moe(args):
+    """gather_qmv (3), multi_gather_qmv (4) or gather_qmm (5) on the full expert stacks."""
+    import numpy as np
+    import torch
+    import rotation_lloyd_max_amd as tq
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    c = wl.CONFIGS[args.config]
+    ncopy = 3 if args.config == 4 else 1
+    layers = []
+    for _ in range(ncopy):
+        layers.append({pr.name: encode_stack(c.E, pr.N, pr.K, pr.levels, pr.group, pr.seed,
+                                             c.cid, wl.PROJ_TENSOR[pr.name], dev)
+                       for pr in c.projs})
+    wbytes = {pr.name: layers[0][pr.name].codes.numel() * 4 // c.E +
+              layers[0][pr.name].scales.numel() * 2 // c.E for pr in c.projs}
+    steps_per_graph = 20
+    if args.config == 3:
+        K1, K2 = c.projs[0].K, c.projs[2].K
+        ids = torch.from_numpy(np.stack([wl.decode_ids(c.cid, s, c.E, 8)
+                                         for s in range(steps_per_graph)])).to(dev)
+        x1 = torch.randn(K1, generator=wl.torch_generator(dev, c.cid, wl.T_X), device=dev).to(torch.bfloat16)
+        x2 = torch.randn(K2, generator=wl.torch_generator(dev, c.cid, wl.T_XD), device=dev).to(torch.bfloat16)
+        ys = {pr.name: torch.empty((8, pr.N), dtype=torch.float32, device=dev) for pr in c.projs}
+
+        def step(s):
+            L = layers[0]
+            tq.gather_qmv(L["gate"], ids[s], x1, out=ys["gate"])
+            tq.gather_qmv(L["up"], ids[s], x1, out=ys["up"])
+            tq.gather_qmv(L["down"], ids[s], x2, out=ys["down"])
+        bytes_step = 8 * sum(wbytes.values()) + 2 * K1 * 2 + K2 * 2
+        unit, metric = "GB/s", "gather_qmv HBM GB/s (MoE decode: gate+up+down of 8 routed experts)"
+    elif args.config == 4:
+        P = 64 * 8
+        ids_np = wl.topk_routing(c.cid, 64, c.E, 8)
+        ids = torch.from_numpy(ids_np).to(dev)
+        Kg, Kd = c.projs[0].K, c.projs[2].K
+        g = wl.torch_generator(dev, c.cid, wl.T_X)
+        xg = torch.randn((P, Kg), generator=g, device=dev).to(torch.bfloat16)
+        xu = torch.randn((P, Kg), generator=g, device=dev).to(torch.bfloat16)
+        xd = torch.randn((P, Kd), generator=g, device=dev).to(torch.bfloat16)
+        ys = {pr.name: torch.empty((P, pr.N), dtype=torch.float32, device=dev) for pr in c.projs}
+        wss = {pr.name: torch.empty((tq.workspace_bytes(tq.OP_MULTI_GATHER_QMV, layers[0][pr.name], P) + 7) // 8,
+                                    dtype=torch.int64, device=dev) for pr in c.projs}
+
+        def step(s):
+            L = layers[s % ncopy]
+            tq.multi_gather_qmv(L["gate"], ids, xg, out=ys["gate"], ws=wss["gate"])
+            tq.multi_gather_qmv(L["up"], ids, xu, out=ys["up"], ws=wss["up"])
+            tq.multi_gather_qmv(L["down"], ids, xd, out=ys["down"], ws=wss["down"])
+        touched = len(np.unique(ids_np))
+        bytes_step = touched * sum(wbytes.values()) + (xg.numel() + xu.numel() + xd.numel()) * 2
+        unit, metric = "GB/s", "multi_gather_qmv HBM GB/s (ternary MoE prefill: gate+up+down)"
+    else:
+        T, k = 4096, 8
+        row_token, _, offsets = wl.zipf_sorted_routing(c.cid, T, c.E, k)
+        M = len(row_token)
+        rt = torch.from_numpy(row_token).to(dev)
+        off = torch.from_numpy(offsets).to(dev)
+        ident = torch.arange(M, dtype=torch.int32, device=dev)
+        Kg, Kd = c.projs[0].K, c.projs[2].K
+        g = wl.torch_generator(dev, c.cid, wl.T_X)
+        x = torch.randn((T, Kg), generator=g, device=dev).to(torch.bfloat16)
+        xd = torch.randn((M, Kd), generator=g, device=dev).to(torch.bfloat16)
+        ys = {pr.name: torch.empty((M, pr.N), dtype=torch.bfloat16, device=dev) for pr in c.projs}
+        wsg = torch.empty((tq.workspace_bytes(tq.OP_GATHER_QMM, layers[0]["gate"], M, T) + 7) // 8,
+                          dtype=torch.int64, device=dev)
+        wsd = torch.empty((tq.workspace_bytes(tq.OP_GATHER_QMM, layers[0]["down"], M, M) + 7) // 8,
+                          dtype=torch.int64, device=dev)
+        steps_per_graph = 1
+
+        def step(s):
+            L = layers[0]
+            tq.gather_qmm(L["gate"], x, rt, off, out=ys["gate"], ws=wsg)
+            tq.gather_qmm(L["up"], x, rt, off, out=ys["up"], ws=wsg)
+            tq.gather_qmm(L["down"], xd, ident, off, out=ys["down"], ws=wsd)
+        flops_step = 2.0 * M * (2 * Kg * c.projs[0].N + Kd * c.projs[2].N)
+        bytes_step = c.E * sum(wbytes.values())
+        unit, metric = "TFLOP/s", "gather_qmm bf16 MFMA TFLOP/s (batched MoE: gate+up+down)"
+
+    for s in range(steps_per_graph):
+        step(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for s in range(steps_per_graph):
+            step(s)
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // steps_per_graph) if steps_per_graph > 1 else args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    nsteps = reps * steps_per_graph
+    ms_per_step = e0.elapsed_time(e1) / nsteps
+    if args.config == 5:
+        value = flops_step / (ms_per_step / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(value, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        value = bytes_step / (ms_per_step / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(value, 3), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None}
+    return {
+        "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": nsteps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 MFMA, f32 acc" if args.config == 5 else "f16*f16->f32",
+        "data": "synthetic", "config": {"workload": c.name, "bytes_per_step": bytes_step},
+        "wall_s": round(wall, 4), "roofline": roof,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the library has "
+              "no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import rotation_lloyd_max_amd as tq
+    if not os.path.exists(tq.LIB_PATH):
+        from rotation_lloyd_max_amd import build
+        build.build()
+    if args.config == 2:
+        out = bench_dense(args)
+    else:
+        out = bench_moe(args)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

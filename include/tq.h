@@ -53,7 +53,9 @@
  *             Paley's first construction (q = 11, 19), H_28 from Paley's second (q = 13),
  *             with Jacobsthal matrix Q[a][b] = chi(a - b).
  *   Dtypes    Activations and outputs are fp32, bf16 or fp16 (tq_dtype). Accumulation is
- *             fp32. Weights for tq_encode are fp32, bf16 or fp16.
+ *             fp32. Weights for tq_encode are fp32, bf16 or fp16. Activations x are read
+ *             with 16-byte loads and must be 16-byte aligned; outputs y need the alignment
+ *             of their dtype.
  */
 #ifndef TQ_H
 #define TQ_H

@@ -43,10 +43,16 @@ __device__ __forceinline__ uint32_t lut_entry(int e, const uint16_t* h) {
   return static_cast<uint32_t>(h[a]) | (static_cast<uint32_t>(h[b]) << 16);
 }
 
-template <int L>
+// Fill the replicated table from the fp16 centroids h (LDS); the caller synchronizes.
+// The trip count is a compile-time constant, so all reads are issued before the writes.
+template <int L, int NT = kBlock>
 __device__ __forceinline__ void build_lut(uint32_t* lut, const uint16_t* h) {
-  for (int i = threadIdx.x; i < Fmt<L>::entries * kLutCopies; i += blockDim.x)
-    lut[i] = lut_entry<L>(i / kLutCopies, h);
+  constexpr int total = Fmt<L>::entries * kLutCopies;
+#pragma unroll
+  for (int k = 0; k < (total + NT - 1) / NT; ++k) {
+    const int i = threadIdx.x + k * NT;
+    if (i < total) lut[i] = lut_entry<L>(i / kLutCopies, h);
+  }
 }
 
 // Table indices of the np pairs of a chunk.
@@ -87,6 +93,78 @@ __device__ __forceinline__ void chunk_indices(const uint32_t (&w)[Fmt<L>::cw], i
 __device__ __forceinline__ float dot2_h(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
                                 false);
+}
+
+// Words of chunk c of a packed row (c must be a valid chunk; rows are 16-byte aligned for
+// 4-bit codes and 8-byte aligned for 2-bit codes because K is a multiple of 32).
+template <int L>
+__device__ __forceinline__ void load_chunk_words(const uint32_t* crow, int c, uint32_t (&w)[Fmt<L>::cw]) {
+  const uint32_t* p = crow + c * Fmt<L>::cw;
+  if constexpr (L == 16) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  } else if constexpr (L == 4) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    w[0] = v.x; w[1] = v.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < Fmt<L>::cw; ++i) w[i] = p[i];
+  }
+}
+
+// The fp16 scale bits a chunk needs: low half = its first group, high half = the next
+// group (for 16-element groups of the bit formats, and for trit words, which may span two
+// groups; clamped to the row's last group).
+template <int L, bool G16>
+__device__ __forceinline__ uint32_t load_chunk_scales(const uint16_t* srow, int c, int group, int ngroups) {
+  if constexpr (L == 3) {
+    const int g0 = (c * 20) / group;
+    const int g1 = g0 + 1 < ngroups ? g0 + 1 : g0;
+    return static_cast<uint32_t>(srow[g0]) | (static_cast<uint32_t>(srow[g1]) << 16);
+  } else if constexpr (G16) {
+    return *reinterpret_cast<const uint32_t*>(srow + 2 * c);
+  } else {
+    return static_cast<uint32_t>(srow[(c * 32) / group]);
+  }
+}
+
+// Sum over a chunk of c[idx] * x' with x' pairs in registers, split at pair pb.
+template <int L>
+__device__ __forceinline__ void chunk_dot_regs(const uint32_t (&w)[Fmt<L>::cw], const uint32_t* lut,
+                                               int lane31, const uint32_t (&xp)[Fmt<L>::np], int pb,
+                                               float& a0, float& a1) {
+  int e[Fmt<L>::np];
+  chunk_indices<L>(w, e);
+#pragma unroll
+  for (int q = 0; q < Fmt<L>::np; ++q) {
+    const uint32_t cw = lut[e[q] * kLutCopies + lane31];
+    if (q < pb) a0 = dot2_h(cw, xp[q], a0);
+    else a1 = dot2_h(cw, xp[q], a1);
+  }
+}
+
+// Sum of v over aligned segments of 2^lg lanes (lg = 0..6) with DPP lane moves (no LDS
+// traffic). Afterwards the segment's last lane holds the segment's total (row_ror moves
+// data towards higher lanes: lane i receives lane (i - n) mod 16 of its row).
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_plus(float v) {
+  const int moved = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false);
+  return v + __int_as_float(moved);
+}
+
+__device__ __forceinline__ float segment_sum(float v, int lg) {
+  if (lg >= 1) v = dpp_plus<0xB1>(v);        // quad_perm [1,0,3,2]: partner lane ^ 1
+  if (lg >= 2) v = dpp_plus<0x4E>(v);        // quad_perm [2,3,0,1]: partner lane ^ 2
+  if (lg >= 3) v = dpp_plus<0x124>(v);       // row_ror:4: quads q and q+1 of the row
+  if (lg >= 4) v = dpp_plus<0x128>(v);       // row_ror:8: whole 16-lane row
+  if (lg >= 5) v = dpp_plus<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  if (lg >= 6) v = dpp_plus<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+__device__ __forceinline__ bool seg_sum_lane(int lane, int lg) {
+  const int seg = 1 << lg;
+  return (lane & (seg - 1)) == seg - 1;
 }
 
 }  // namespace tq

@@ -93,7 +93,7 @@ template <typename T, int R>
 __device__ __forceinline__ void sylvester_pass(T* buf, int total, int h) {
   constexpr int n = 1 << R;
   const int ngroups = total >> R;
-  for (int g = threadIdx.x; g < ngroups; g += blockDim.x) {
+  for (int g = threadIdx.x; g < ngroups; g += kBlock) {
     const int blk = g / h, off = g - blk * h;
     T* base = buf + blk * (h << R) + off;
     T v[n];
@@ -115,9 +115,10 @@ __device__ __forceinline__ void sylvester_pass(T* buf, int total, int h) {
   __syncthreads();
 }
 
+// Stages h0, 2*h0, ..., P/2 (the stages below h0 already applied by the caller).
 template <typename T>
-__device__ __forceinline__ void sylvester_lds(T* buf, int total, int P) {
-  int h = 1;
+__device__ __forceinline__ void sylvester_lds(T* buf, int total, int P, int h0 = 1) {
+  int h = h0;
   while (h < P) {
     const int left = __builtin_ctz(P / h);
     if (left >= 4) { sylvester_pass<T, 4>(buf, total, h); h <<= 4; }
@@ -135,7 +136,7 @@ template <typename T, int M>
 __device__ __forceinline__ void hadamard_m_lds(T* buf, int nrows, int P) {
   const float(*sgn)[M] = HadamardTable<M>::value.sgn;
   const int cols = nrows * P;
-  for (int col = threadIdx.x; col < cols; col += blockDim.x) {
+  for (int col = threadIdx.x; col < cols; col += kBlock) {
     const int r = col / P, b = col - r * P;
     T* base = buf + r * M * P + b;
     T x[M];
@@ -231,7 +232,7 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   if (lane == 0) red[wave] = v;
   __syncthreads();
   float m = red[0];
-  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) m = fmaxf(m, red[w]);
+  for (int w = 1; w < (int)(kBlock >> 6); ++w) m = fmaxf(m, red[w]);
   __syncthreads();
   return m;
 }

@@ -15,7 +15,7 @@ namespace tq {
 
 __device__ __forceinline__ void fill_sign_words(uint32_t* sb, int K, uint64_t seed) {
   const int nw = (K + 31) / 32;
-  for (int w = threadIdx.x; w < nw; w += blockDim.x) {
+  for (int w = threadIdx.x; w < nw; w += kBlock) {
     uint32_t b = 0;
     for (int j = 0; j < 32; ++j) {
       const int i = 32 * w + j;
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kBlock) void k_encode(const void* W, int64_t rows, 
 
   for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
     const int64_t base = row * K;
-    for (int i = threadIdx.x; i < K; i += blockDim.x) {
+    for (int i = threadIdx.x; i < K; i += kBlock) {
       const double w = static_cast<double>(load_elem<WDT>(W, base + i));
       v[i] = ((sb[i >> 5] >> (i & 31)) & 1u) ? -w : w;
     }
@@ -54,7 +54,7 @@ __global__ __launch_bounds__(kBlock) void k_encode(const void* W, int64_t rows, 
     hadamard_lds<double>(v, 1, m, P);
 
     // group sums of squares: partial sums over runs, then per group
-    for (int r = threadIdx.x; r < K / run; r += blockDim.x) {
+    for (int r = threadIdx.x; r < K / run; r += kBlock) {
       double s = 0.0;
       for (int j = 0; j < run; ++j) {
         const double a = v[r * run + j];
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kBlock) void k_encode(const void* W, int64_t rows, 
     }
     __syncthreads();
     const int per = group / run;
-    for (int g = threadIdx.x; g < ngroups; g += blockDim.x) {
+    for (int g = threadIdx.x; g < ngroups; g += kBlock) {
       double s = 0.0;
       for (int j = 0; j < per; ++j) s += part[g * per + j];
       const double rr = __builtin_sqrt(s / group);  // RMS of the unnormalized rotated group
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kBlock) void k_encode(const void* W, int64_t rows, 
     __syncthreads();
 
     // snap: count thresholds below u, in binary32
-    for (int i = threadIdx.x; i < K; i += blockDim.x) {
+    for (int i = threadIdx.x; i < K; i += kBlock) {
       const float u = static_cast<float>(v[i] * rinv[i / group]);
       int q = 0;
 #pragma unroll
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(kBlock) void k_encode(const void* W, int64_t rows, 
 
     // pack
     uint32_t* crow = codes + row * static_cast<int64_t>(wpr);
-    for (int wd = threadIdx.x; wd < wpr; wd += blockDim.x) {
+    for (int wd = threadIdx.x; wd < wpr; wd += kBlock) {
       uint32_t word = 0;
       if constexpr (LEVELS == 3) {
         for (int k = 19; k >= 0; --k) {

@@ -34,8 +34,8 @@ __global__ void k_schedule(const int32_t* offsets, int E, int32_t* tile_start) {
 }
 
 __global__ __launch_bounds__(kBlock) void k_to_bf16(const void* x, int xdt, int64_t n, uint16_t* out) {
-  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(kBlock) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * kBlock)
     out[i] = float_to_bf16_rne(load_any(x, xdt, i));
 }
 

@@ -27,9 +27,9 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* ids, i
                                                            void* y, int ydt, int N) {
   __shared__ int32_t cnt[kMaxExperts];
   __shared__ int32_t wsum[kBucketThreads / 64];
-  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+  for (int e = threadIdx.x; e < E; e += kBucketThreads) cnt[e] = 0;
   __syncthreads();
-  for (int64_t p = threadIdx.x; p < P; p += blockDim.x) {
+  for (int64_t p = threadIdx.x; p < P; p += kBucketThreads) {
     const int e = ids[p];
     if (e >= 0 && e < E) {
       atomicAdd(&cnt[e], 1);
@@ -38,9 +38,9 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* ids, i
     }
   }
   __syncthreads();
-  // exclusive scan of cnt[0..E) in chunks of blockDim.x, carried by thread 0's running sum
+  // exclusive scan of cnt[0..E) in chunks of kBucketThreads, carried by thread 0's running sum
   int carry = 0;
-  for (int base = 0; base < E; base += blockDim.x) {
+  for (int base = 0; base < E; base += kBucketThreads) {
     const int e = base + threadIdx.x;
     int v = e < E ? cnt[e] : 0;
     // inclusive wave scan
@@ -61,13 +61,13 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* ids, i
       cnt[e] = excl;  // becomes the scatter cursor
     }
     int total = carry;
-    for (int k = 0; k < static_cast<int>(blockDim.x >> 6); ++k) total += wsum[k];
+    for (int k = 0; k < static_cast<int>(kBucketThreads >> 6); ++k) total += wsum[k];
     carry = total;
     __syncthreads();
   }
   if (threadIdx.x == 0) offsets[E] = carry;
   __syncthreads();
-  for (int64_t p = threadIdx.x; p < P; p += blockDim.x) {
+  for (int64_t p = threadIdx.x; p < P; p += kBucketThreads) {
     const int e = ids[p];
     if (e >= 0 && e < E) {
       const int pos = atomicAdd(&cnt[e], 1);
@@ -95,7 +95,7 @@ template <int XDT>
 __device__ __forceinline__ float prepare_input_m(const void* x, int64_t xoff, int K, int m, int P,
                                         bool rotated, const uint32_t* sb, float* xf, float* red,
                                         uint32_t* xh2, int xwords, float inv_sqrt_k) {
-  for (int i = threadIdx.x; i < K; i += blockDim.x) {
+  for (int i = threadIdx.x; i < K; i += kBlock) {
     float v = load_elem<XDT>(x, xoff + i);
     if (!rotated && ((sb[i >> 5] >> (i & 31)) & 1u)) v = -v;
     xf[i] = v;
@@ -103,7 +103,7 @@ __device__ __forceinline__ float prepare_input_m(const void* x, int64_t xoff, in
   __syncthreads();
   if (!rotated) hadamard_lds<float>(xf, 1, m, P);
   float mx = 0.f;
-  for (int i = threadIdx.x; i < K; i += blockDim.x) mx = fmaxf(mx, fabsf(xf[i]));
+  for (int i = threadIdx.x; i < K; i += kBlock) mx = fmaxf(mx, fabsf(xf[i]));
   mx = block_max(mx, red);
   int ex = 0;
   if (mx > 0.f && mx <= 3.0e38f) {
@@ -111,7 +111,7 @@ __device__ __forceinline__ float prepare_input_m(const void* x, int64_t xoff, in
     ex = ex < -100 ? -100 : (ex > 100 ? 100 : ex);
   }
   const float sc = ldexpf(1.f, ex);
-  for (int q = threadIdx.x; q < xwords; q += blockDim.x) {
+  for (int q = threadIdx.x; q < xwords; q += kBlock) {
     const int i0 = 2 * q, i1 = 2 * q + 1;
     const float a = i0 < K ? xf[i0] * sc : 0.f;
     const float b = i1 < K ? xf[i1] * sc : 0.f;
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kBlock) void k_multi(MultiParams p) {
 
   build_lut<L>(lut, p.cb.h);
   if (!p.rotated)
-    for (int w = threadIdx.x; w < (p.K + 31) / 32; w += blockDim.x) sb[w] = p.signs[w];
+    for (int w = threadIdx.x; w < (p.K + 31) / 32; w += kBlock) sb[w] = p.signs[w];
   __syncthreads();
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lane31 = lane & 31;

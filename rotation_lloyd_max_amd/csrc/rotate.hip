@@ -11,7 +11,7 @@ namespace tq {
 
 __global__ __launch_bounds__(kBlock) void k_signs(uint64_t seed, int K, uint32_t* bits) {
   const int nw = (K + 31) / 32;
-  for (int w = blockIdx.x * blockDim.x + threadIdx.x; w < nw; w += gridDim.x * blockDim.x) {
+  for (int w = blockIdx.x * kBlock + threadIdx.x; w < nw; w += gridDim.x * kBlock) {
     uint32_t b = 0;
     for (int j = 0; j < 32; ++j) {
       const int i = 32 * w + j;
@@ -32,7 +32,7 @@ hipError_t launch_signs(uint64_t seed, int K, uint32_t* bits, hipStream_t s) {
 __device__ __forceinline__ void load_sign_words(uint32_t* sb, int K, const uint32_t* signbits,
                                        uint64_t seed) {
   const int nw = (K + 31) / 32;
-  for (int w = threadIdx.x; w < nw; w += blockDim.x) {
+  for (int w = threadIdx.x; w < nw; w += kBlock) {
     if (signbits) {
       sb[w] = signbits[w];
     } else {
@@ -58,13 +58,13 @@ __global__ __launch_bounds__(kBlock) void k_fwht(const void* x, int64_t rows, in
   __syncthreads();
   for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
     const int64_t base = row * K;
-    for (int i = threadIdx.x; i < K; i += blockDim.x) {
+    for (int i = threadIdx.x; i < K; i += kBlock) {
       const float v = load_elem<XDT>(x, base + i);
       buf[i] = ((sb[i >> 5] >> (i & 31)) & 1u) ? -v : v;
     }
     __syncthreads();
     hadamard_lds<float>(buf, 1, m, P);
-    for (int i = threadIdx.x; i < K; i += blockDim.x) store_any(out, odt, base + i, buf[i] * inv_sqrt_k);
+    for (int i = threadIdx.x; i < K; i += kBlock) store_any(out, odt, base + i, buf[i] * inv_sqrt_k);
     __syncthreads();
   }
 }

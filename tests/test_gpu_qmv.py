@@ -88,6 +88,21 @@ def test_qmv_formats(levels, group, K, N):
     check_qmv_against_oracle(qw, ref, x, y, f"L{levels} g{group} K{K} N{N}")
 
 
+@pytest.mark.parametrize("levels", [3, 4, 8, 16])
+@pytest.mark.parametrize("K", [64, 96, 128, 256, 224, 8192])
+def test_qmv_small_and_largest_k(levels, K):
+    # few chunks per row (2..13: lanes of a wave split over several rows) and the largest K
+    group = 16 if K % 32 else 32
+    N = 70
+    g = wl.rng(920, levels, K)
+    W = to_dev(wl.student_rows(g, N, K), torch.bfloat16)
+    x = to_dev(wl.gaussian(g, 1, K)[0], torch.float32)
+    qw, ref = encode_both(W, levels, group, seed=13)
+    y = tq.qmv(qw, x)
+    torch.cuda.synchronize()
+    check_qmv_against_oracle(qw, ref, x, y, f"L{levels} K{K}")
+
+
 @pytest.mark.parametrize("xdt", [torch.float32, torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("ydt", [torch.float32, torch.bfloat16, torch.float16])
 def test_qmv_dtypes(xdt, ydt):

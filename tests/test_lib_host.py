@@ -91,6 +91,7 @@ def test_validation_statuses():
     assert qmv_status(desc(), xdt=7) == ERR_ARG
     assert qmv_status(desc(), x=0) == ERR_ARG
     assert qmv_status(desc(), x=18, xdt=0) == ERR_ALIGN
+    assert qmv_status(desc(), x=20, xdt=0) == ERR_ALIGN  # x needs 16-byte alignment
     assert b"group" in L.tq_last_error() or L.tq_last_error()
     # multi_gather: short workspace
     d = desc(E=4)
