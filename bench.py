@@ -12,6 +12,9 @@ not in the timed region.
           activation = 6,561,792 B per call) of the step's 1000 calls / the step's time
   roofline.achieved  the same bytes per call / the average qmv launch duration, from HIP
           events around the qmv graph (includes the gaps between back-to-back kernels)
+  roofline.traffic  HBM bytes per qmv launch from the FETCH_SIZE / WRITE_SIZE counter
+          passes recorded in profiles/ (scaled by a copy kernel of known size); null
+          when the kernel sources no longer match the ones those counters were taken on
   encode_mweights_per_s  16,777,216 weights / the encode time of a step
   cpu_baseline  the fp64 oracle (numpy, one BLAS thread) on a bounded sample of the same
           layer, in the same unit
@@ -41,6 +44,9 @@ def parse():
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calls", type=int, default=1000, help="qmv calls per step")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-MiB device buffer 5 times (a plain copy kernel of "
+                         "known size, to scale the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -76,6 +82,43 @@ def cpu_baseline_qmv(W_bits, x_bits, levels, group, seed, budget_s=12.0, rows=51
                   f"{rows * K / t_enc / 1e6:.3f} Mweights/s",
         "encode_mweights_per_s": round(rows * K / t_enc / 1e6, 6),
     }
+
+
+QMV_SOURCES = ["qmv.hip", "prologue.hpp", "decode_common.hpp", "fwht_block.hpp",
+               "device_common.hpp", "internal.hpp"]
+
+
+def recorded_traffic(profile, sources):
+    """HBM bytes per launch measured by the FETCH_SIZE / WRITE_SIZE passes recorded in
+    profiles/<profile>, or None when the kernel sources have changed since (sha256)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", profile)
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "source_sha256"):
+            k, v = line.split(":", 1)
+            rec[k] = v.strip()
+    h = hashlib.sha256()
+    for f in sources:
+        with open(os.path.join(ROOT, "rotation_lloyd_max_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if rec.get("source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in rec:
+        return None
+    return int(rec["traffic_bytes_per_launch"])
+
+
+def copy_calibration(mib):
+    """Five device-to-device copies of `mib` MiB by an elementwise kernel (y = 1 * x, fp32)."""
+    import torch
+    n = mib << 20
+    src = torch.rand(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    return {"copy_bytes_read": n, "copy_bytes_written": n, "copies": 5}
 
 
 def bench_dense(args):
@@ -175,7 +218,7 @@ def bench_dense(args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic("k_qmv_dense_4096x4096_3bit_g128.md", QMV_SOURCES),
         },
     }
     if not args.no_cpu_baseline:
@@ -337,7 +380,9 @@ def main():
     if not os.path.exists(tq.LIB_PATH):
         from rotation_lloyd_max_amd import build
         build.build()
-    if args.config == 2:
+    if args.copy_calibration:
+        out = copy_calibration(args.copy_calibration)
+    elif args.config == 2:
         out = bench_dense(args)
     else:
         out = bench_moe(args)

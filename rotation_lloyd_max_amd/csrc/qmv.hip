@@ -145,7 +145,8 @@ __global__ __launch_bounds__(qmv_threads<CPL>()) void k_qmv(QmvParams p) {
   // the first ones while the codes stream in.
   InputLoad<X32, kQmvThreads> xin;
   xin.issue(p.x, p.xdt, 0, p.K, p.signs);
-  // without ids, a harmless word of the sign array is read and ignored (no branch)
+  // without ids, a harmless word of the sign array is read and ignored (no branch); the
+  // address is uniform, so this is a scalar load that no vector load has to wait for
   const int eraw = *(p.ids ? p.ids + slot : reinterpret_cast<const int32_t*>(p.signs));
   const int e = p.ids ? eraw : 0;
   const bool bad = e < 0 || e >= p.E;
