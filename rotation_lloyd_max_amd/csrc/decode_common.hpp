@@ -112,20 +112,26 @@ __device__ __forceinline__ void load_chunk_words(const uint32_t* crow, int c, ui
   }
 }
 
-// The fp16 scale bits a chunk needs: low half = its first group, high half = the next
-// group (for 16-element groups of the bit formats, and for trit words, which may span two
-// groups; clamped to the row's last group).
+// The fp16 scales a chunk needs: .x = its first group, .y = the next group (for 16-element
+// groups of the bit formats, and for trit words, which may span two groups; clamped to the
+// row's last group). Each half is loaded straight into its half of the register (no
+// shift or mask after the load), so nothing waits for the load before the value is used.
 template <int L, bool G16>
-__device__ __forceinline__ uint32_t load_chunk_scales(const uint16_t* srow, int c, int group, int ngroups) {
+__device__ __forceinline__ half2_t load_chunk_scales(const uint16_t* srow, int c, int group, int ngroups) {
+  const _Float16* sh = reinterpret_cast<const _Float16*>(srow);
+  half2_t r;
   if constexpr (L == 3) {
     const int g0 = (c * 20) / group;
     const int g1 = g0 + 1 < ngroups ? g0 + 1 : g0;
-    return static_cast<uint32_t>(srow[g0]) | (static_cast<uint32_t>(srow[g1]) << 16);
+    r.x = sh[g0];
+    r.y = sh[g1];
   } else if constexpr (G16) {
-    return *reinterpret_cast<const uint32_t*>(srow + 2 * c);
+    r = *reinterpret_cast<const half2_t*>(sh + 2 * c);
   } else {
-    return static_cast<uint32_t>(srow[(c * 32) / group]);
+    r.x = sh[(c * 32) / group];
+    // .y unused (one group per chunk)
   }
+  return r;
 }
 
 // Sum over a chunk of c[idx] * x' with x' pairs in registers, split at pair pb.
@@ -152,6 +158,25 @@ __device__ __forceinline__ float dpp_plus(float v) {
   return v + __int_as_float(moved);
 }
 
+// segment_sum without branches: every step is done, and the moved value is dropped (a
+// select on a uniform condition) when the step is beyond lg. Straight-line code keeps the
+// compiler's accounting of outstanding loads exact inside streaming loops.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_plus_if(float v, bool on) {
+  const int moved = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false);
+  return v + (on ? __int_as_float(moved) : 0.f);
+}
+
+__device__ __forceinline__ float segment_sum_flat(float v, int lg) {
+  v = dpp_plus_if<0xB1>(v, lg >= 1);
+  v = dpp_plus_if<0x4E>(v, lg >= 2);
+  v = dpp_plus_if<0x124>(v, lg >= 3);
+  v = dpp_plus_if<0x128>(v, lg >= 4);
+  v = dpp_plus_if<0x142, 0xA>(v, lg >= 5);
+  v = dpp_plus_if<0x143, 0xC>(v, lg >= 6);
+  return v;
+}
+
 __device__ __forceinline__ float segment_sum(float v, int lg) {
   if (lg >= 1) v = dpp_plus<0xB1>(v);        // quad_perm [1,0,3,2]: partner lane ^ 1
   if (lg >= 2) v = dpp_plus<0x4E>(v);        // quad_perm [2,3,0,1]: partner lane ^ 2
@@ -159,6 +184,24 @@ __device__ __forceinline__ float segment_sum(float v, int lg) {
   if (lg >= 4) v = dpp_plus<0x128>(v);       // row_ror:8: whole 16-lane row
   if (lg >= 5) v = dpp_plus<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
   if (lg >= 6) v = dpp_plus<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// Maximum of non-negative v over the wave, left in lane 63 (same lane moves as
+// segment_sum; lanes without a source lane see 0, which leaves a non-negative max as is).
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_max(float v) {
+  const int moved = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false);
+  return fmaxf(v, __int_as_float(moved));
+}
+
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+  v = dpp_max<0xB1>(v);
+  v = dpp_max<0x4E>(v);
+  v = dpp_max<0x124>(v);
+  v = dpp_max<0x128>(v);
+  v = dpp_max<0x142, 0xA>(v);
+  v = dpp_max<0x143, 0xC>(v);
   return v;
 }
 

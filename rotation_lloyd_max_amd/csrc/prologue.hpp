@@ -4,10 +4,10 @@
 // input of its chunks as scaled fp16 pairs.
 //
 // The rotation is x' = H_K diag(s) x / sqrt(K) (turboquant-mlx "How it works", "Running a
-// quantized layer": the input gets the weights' rotation). Every |x'_j| is at most
-// ||x'|| = ||x||, so x' is kept in fp16 after multiplying by 2^e with e chosen from ||x||
-// (computed in fp64 from the loaded registers): no entry can overflow and each keeps
-// fp16's 11 significant bits. The factor 2^-e (and 1/sqrt(K)) is applied to the row sums.
+// quantized layer": the input gets the weights' rotation). The unnormalized H_K s x is kept
+// in fp16 after multiplying by a power of two 2^e chosen from max |x_i| and K, so that no
+// entry can overflow and each keeps fp16's 11 significant bits. The factor 2^-e (and
+// 1/sqrt(K)) is applied to the row sums.
 #pragma once
 
 #include "decode_common.hpp"
@@ -61,14 +61,19 @@ struct InputLoad {
     }
   }
 
-  // Write s * x into xf (padded layout) with the small butterflies applied, reduce ||x||^2,
-  // then finish H_K in LDS unless `rotated`. `red` holds NT / 64 doubles of LDS scratch. Ends
-  // synchronized. Returns the power of two sc for the fp16 conversion; *out_scale gets
-  // 1 / sc, times 1 / sqrt(K) when the rotation was applied here.
-  __device__ __forceinline__ float finish(float* xf, double* red, int K, int m, int P,
+  // Write s * x into xf (padded layout) with the butterflies of stride < 16 applied, find
+  // max |x_i| (one float per wave in `red`, NT / 64 floats of LDS), then finish H_K in LDS
+  // unless `rotated`. Ends synchronized. Returns the power of two sc for the fp16
+  // conversion; *out_scale gets 1 / sc, times 1 / sqrt(K) when the rotation was applied.
+  //
+  // Every entry of the unnormalized H_K s x is a sum of K terms of size at most
+  // max |x_i| < 2^(e + 1), e = ilogb(max |x_i|), so with K <= 2^lk it is below
+  // 2^(e + 1 + lk), and sc = 2^(14 - e - lk) keeps every scaled entry below 2^15 (fp16 holds
+  // up to 65504). A rotated input is its own bound (lk = 0).
+  __device__ __forceinline__ float finish(float* xf, float* red, int K, int lk, int m, int P,
                                           bool rotated, float inv_sqrt_k, float* out_scale) {
     const int nseg = K >> 4;
-    double ss = 0.0;
+    float mx = 0.f;
 #pragma unroll
     for (int j = 0; j < kSeg16; ++j) {
       const int sgi = threadIdx.x + NT * j;
@@ -78,30 +83,27 @@ struct InputLoad {
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const float a = elem(j, k);
-        v[k] = ((bits >> k) & 1u) ? -a : a;
-        ss += static_cast<double>(a) * static_cast<double>(a);
+        mx = fmaxf(mx, fabsf(a));
+        v[k] = __uint_as_float(__float_as_uint(a) ^ (((bits >> k) & 1u) << 31));
       }
       if (!rotated) seg16_butterflies<float>(v, P);
       float* dst = xf + 17 * sgi;  // pidx(16 * sgi + k) = 17 * sgi + k
 #pragma unroll
       for (int k = 0; k < 16; ++k) dst[k] = v[k];
     }
-    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    mx = wave_max_nonneg(mx);
+    if ((threadIdx.x & 63) == 63) red[threadIdx.x >> 6] = mx;
     __syncthreads();
-    double tot = 0.0;
+    float mall = 0.f;
 #pragma unroll
-    for (int w = 0; w < NT / 64; ++w) tot += red[w];
+    for (int w = 0; w < NT / 64; ++w) mall = fmaxf(mall, red[w]);
     if (!rotated) {
-      sylvester_rest<float, NT>(xf, K, P, P < 16 ? P : 16);
+      sylvester_from16<float, NT>(xf, K, __builtin_ctz(P));
       hadamard_factor<float, NT>(xf, m, P);
     }
-    // |x'_j| <= ||x'||; unnormalized, ||H_K s x|| = sqrt(K) ||x||
-    const double bound =
-        __builtin_sqrt(tot) * (rotated ? 1.0 : __builtin_sqrt(static_cast<double>(K)));
     int ex = 0;
-    if (bound > 0.0 && bound < 1e300) {
-      ex = 14 - ilogb(bound);
+    if (mall > 0.f && mall <= 3.4028234663852886e38f) {
+      ex = 14 - ilogbf(mall) - (rotated ? 0 : lk);
       ex = ex < -120 ? -120 : (ex > 120 ? 120 : ex);
     }
     *out_scale = ldexpf(1.f, -ex) * (rotated ? 1.f : inv_sqrt_k);
@@ -109,27 +111,58 @@ struct InputLoad {
   }
 };
 
-// The rotated input of a lane's chunks (chunk c = c0 + j * lpr) as fp16 pairs, read from
-// the padded fp32 row; zero past K and for chunks past the row.
-template <int L, int CPL>
-__device__ __forceinline__ void lane_pairs(const float* xf, int K, int Q, int c0, int lpr, float sc,
-                                           uint32_t (&xr)[CPL][Fmt<L>::np]) {
+// Words between the fp16 pair slices of consecutive chunks in LDS: the chunk's pairs plus
+// padding, so that the 16-byte reads of 16 consecutive lanes (one chunk each) fall on 16
+// disjoint groups of 4 banks (stride 20 words for 16 pairs, 12 words for 10 pairs).
+template <int L>
+constexpr int pair_stride() {
+  return Fmt<L>::np == 16 ? 20 : 12;
+}
+
+// Convert the rotated row (padded fp32 in xf) once per workgroup to scaled fp16 pairs laid
+// out chunk by chunk in xh (Q chunks of pair_stride words, 16-byte aligned); pairs past K
+// are zero. Pair k holds elements 2k and 2k + 1, which is pair k % np of chunk k / np
+// because a chunk holds 2 np consecutive elements. Ends synchronized.
+template <int L, int NT>
+__device__ __forceinline__ void pairs_to_lds(const float* xf, uint32_t* xh, int K, int Q, float sc) {
   using F = Fmt<L>;
+  constexpr int S = pair_stride<L>();
+  const int total = Q * F::np;
+  for (int k = threadIdx.x; k < total; k += NT) {
+    const int c = k / F::np, q = k - c * F::np;
+    const int e0 = 2 * k;
+    const float ra = xf[pidx(e0 < K ? e0 : K - 1)];
+    const float rb = xf[pidx(e0 + 1 < K ? e0 + 1 : K - 1)];
+    const float a = e0 < K ? ra * sc : 0.f;
+    const float b = e0 + 1 < K ? rb * sc : 0.f;
+    xh[c * S + q] = static_cast<uint32_t>(float_to_half_rne(a)) |
+                    (static_cast<uint32_t>(float_to_half_rne(b)) << 16);
+  }
+  __syncthreads();
+}
+
+// The fp16 pairs of a lane's chunks (chunk cbase + c0 + j * lpr of the slice of slice_q
+// chunks starting at cbase; positions past the slice read its last chunk, whose products
+// the caller discards), with 16-byte LDS reads.
+template <int L, int CPL>
+__device__ __forceinline__ void lane_pairs(const uint32_t* xh, int cbase, int c0, int lpr,
+                                           int slice_q, uint32_t (&xr)[CPL][Fmt<L>::np]) {
+  using F = Fmt<L>;
+  constexpr int S = pair_stride<L>();
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
-    const int c = c0 + j * lpr;
-    const bool okc = c < Q;
-    const int cc = okc ? c : 0;
+    const int cr = c0 + j * lpr;
+    const int c = cbase + (cr < slice_q ? cr : slice_q - 1);
+    const uint4* src = reinterpret_cast<const uint4*>(xh + c * S);
 #pragma unroll
-    for (int q = 0; q < F::np; ++q) {
-      // unconditional reads at clamped addresses, then a select: no branch per element
-      const int e0 = cc * F::ce + 2 * q;
-      const float ra = xf[pidx(e0 < K ? e0 : K - 1)];
-      const float rb = xf[pidx(e0 + 1 < K ? e0 + 1 : K - 1)];
-      const float a = (okc && e0 < K) ? ra * sc : 0.f;
-      const float b = (okc && e0 + 1 < K) ? rb * sc : 0.f;
-      xr[j][q] = static_cast<uint32_t>(float_to_half_rne(a)) |
-                 (static_cast<uint32_t>(float_to_half_rne(b)) << 16);
+    for (int v = 0; v < F::np / 4; ++v) {
+      const uint4 a = src[v];
+      xr[j][4 * v + 0] = a.x; xr[j][4 * v + 1] = a.y;
+      xr[j][4 * v + 2] = a.z; xr[j][4 * v + 3] = a.w;
+    }
+    if constexpr (F::np % 4 == 2) {
+      const uint2 a = reinterpret_cast<const uint2*>(src + F::np / 4)[0];
+      xr[j][F::np - 2] = a.x; xr[j][F::np - 1] = a.y;
     }
   }
 }
