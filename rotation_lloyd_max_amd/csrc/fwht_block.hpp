@@ -23,16 +23,30 @@ namespace tq {
 __device__ __forceinline__ int pidx(int i) { return i + (i >> 4); }
 __host__ __device__ constexpr int padded_len(int n) { return n + n / 16 + 1; }
 
+// Where the last stage of the transform may put its results instead of the fp32 row: the
+// fp16 chunk layout of the decode kernels, scaled by sc. Element e is half e % 32 of chunk
+// e / 32, and chunks are kChunkHalves halves apart (32 used, 8 of padding).
+constexpr int kChunkHalves = 40;
+struct HalfSink {
+  _Float16* h;  // LDS
+  float sc;
+  __device__ __forceinline__ static int idx(int e) { return (e >> 5) * kChunkHalves + (e & 31); }
+  __device__ __forceinline__ void put_at(int hi, float v) const {
+    h[hi] = static_cast<_Float16>(v * sc);
+  }
+};
+
 // One radix-2^R pass pairing elements at stride 2^LH (LH >= 4) over `total` elements. The
 // padded distance of 2^LH elements is the constant 17 * 2^(LH-4) words, so every access of
 // a group is a fixed offset from its first element.
-template <typename T, int R, int LH, int NT>
-__device__ __forceinline__ void sylvester_pass_c(T* buf, int total) {
+template <typename T, int R, int LH, int NT, bool OUT = false>
+__device__ __forceinline__ void sylvester_pass_c(T* buf, int total, HalfSink sink = {}) {
   constexpr int n = 1 << R, h = 1 << LH, step = 17 * (h / 16);
   const int ngroups = total >> R;
   for (int g = threadIdx.x; g < ngroups; g += NT) {
     const int blk = g >> LH, off = g & (h - 1);
-    T* base = buf + pidx((blk << (LH + R)) + off);
+    const int e0 = (blk << (LH + R)) + off;
+    T* base = buf + pidx(e0);
     T v[n];
 #pragma unroll
     for (int j = 0; j < n; ++j) v[j] = base[j * step];
@@ -45,37 +59,51 @@ __device__ __forceinline__ void sylvester_pass_c(T* buf, int total) {
         v[j] = a + b;
         v[j + (1 << s)] = a - b;
       }
+    if constexpr (OUT) {
+      // e0 % 32 < 16 when h == 16, and j * h is a multiple of 32 when h >= 32, so the
+      // half index of element e0 + j * h is a fixed offset from that of e0
+      const int h0 = HalfSink::idx(e0);
 #pragma unroll
-    for (int j = 0; j < n; ++j) base[j * step] = v[j];
+      for (int j = 0; j < n; ++j) {
+        const int d = h >= 32 ? (j * h / 32) * kChunkHalves
+                              : ((j * 16) >> 5) * kChunkHalves + ((j * 16) & 31);
+        sink.put_at(h0 + d, v[j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < n; ++j) base[j * step] = v[j];
+    }
   }
   __syncthreads();
 }
 
 // STAGES butterfly stages starting at stride 2^LH, in ceil(STAGES / 4) passes of nearly
 // equal radix.
-template <typename T, int NT, int LH, int STAGES>
-__device__ __forceinline__ void sylvester_stages(T* buf, int total) {
+// With OUT the last pass writes its results to the sink.
+template <typename T, int NT, int LH, int STAGES, bool OUT>
+__device__ __forceinline__ void sylvester_stages(T* buf, int total, HalfSink sink) {
   if constexpr (STAGES > 0) {
     constexpr int passes = (STAGES + 3) / 4;
     constexpr int R = (STAGES + passes - 1) / passes;
-    sylvester_pass_c<T, R, LH, NT>(buf, total);
-    sylvester_stages<T, NT, LH + R, STAGES - R>(buf, total);
+    sylvester_pass_c<T, R, LH, NT, OUT && (STAGES == R)>(buf, total, sink);
+    sylvester_stages<T, NT, LH + R, STAGES - R, OUT>(buf, total, sink);
   }
 }
 
-// The Sylvester stages of stride 16 .. P/2 on runs of length P = 2^lp.
-template <typename T, int NT>
-__device__ __forceinline__ void sylvester_from16(T* buf, int total, int lp) {
+// The Sylvester stages of stride 16 .. P/2 on runs of length P = 2^lp (lp >= 5 when OUT,
+// so that there is a last pass to write the sink).
+template <typename T, int NT, bool OUT = false>
+__device__ __forceinline__ void sylvester_from16(T* buf, int total, int lp, HalfSink sink = {}) {
   switch (lp) {
-    case 5: sylvester_stages<T, NT, 4, 1>(buf, total); break;
-    case 6: sylvester_stages<T, NT, 4, 2>(buf, total); break;
-    case 7: sylvester_stages<T, NT, 4, 3>(buf, total); break;
-    case 8: sylvester_stages<T, NT, 4, 4>(buf, total); break;
-    case 9: sylvester_stages<T, NT, 4, 5>(buf, total); break;
-    case 10: sylvester_stages<T, NT, 4, 6>(buf, total); break;
-    case 11: sylvester_stages<T, NT, 4, 7>(buf, total); break;
-    case 12: sylvester_stages<T, NT, 4, 8>(buf, total); break;
-    case 13: sylvester_stages<T, NT, 4, 9>(buf, total); break;
+    case 5: sylvester_stages<T, NT, 4, 1, OUT>(buf, total, sink); break;
+    case 6: sylvester_stages<T, NT, 4, 2, OUT>(buf, total, sink); break;
+    case 7: sylvester_stages<T, NT, 4, 3, OUT>(buf, total, sink); break;
+    case 8: sylvester_stages<T, NT, 4, 4, OUT>(buf, total, sink); break;
+    case 9: sylvester_stages<T, NT, 4, 5, OUT>(buf, total, sink); break;
+    case 10: sylvester_stages<T, NT, 4, 6, OUT>(buf, total, sink); break;
+    case 11: sylvester_stages<T, NT, 4, 7, OUT>(buf, total, sink); break;
+    case 12: sylvester_stages<T, NT, 4, 8, OUT>(buf, total, sink); break;
+    case 13: sylvester_stages<T, NT, 4, 9, OUT>(buf, total, sink); break;
     default: break;  // P <= 16: done in registers
   }
 }
@@ -86,8 +114,13 @@ __device__ __forceinline__ void sylvester_from16(T* buf, int total, int lp) {
 //
 // H_12 and H_20 (Paley I) are applied row by row (m - 1 additions per output). H_28 is
 // Paley II, S (x) [[1, 1], [1, -1]] + I (x) [[1, -1], [-1, -1]] with S the symmetric
-// conference matrix of order 14, which needs fewer additions: with u_C = x_2C + x_2C+1 and
-// v_C = x_2C - x_2C+1,  y_2R = sum_C S[R][C] u_C + v_R  and  y_2R+1 = sum_C S[R][C] v_C - u_R.
+// conference matrix of order 14: with u_C = x_2C + x_2C+1 and v_C = x_2C - x_2C+1,
+//   y_2R = sum_C S[R][C] u_C + v_R   and   y_2R+1 = sum_C S[R][C] v_C - u_R.
+// The 13 x 13 core of S is the circulant chi(R - C) of the quadratic character mod 13,
+// whose +1 set {1, 3, 4, 9, 10, 12} is symmetric, so with w_c = a_{c+1} and W = sum_c w_c,
+//   sum_C S[r+1][C] a_C = a_0 - W + w_r + 2 (w_{r-4} + w_{r-3} + w_{r+3} + w_{r+4} + w_{r-1} + w_{r+1})
+// (indices mod 13), and the pair sums w_k + w_{k+1} are shared between rows: about 105
+// additions per side instead of 14 * 13.
 template <int M, int A, int C>
 inline constexpr int kHad = hadamard_entry(M, A, C);
 
@@ -111,68 +144,126 @@ __device__ __forceinline__ T conference_row(const T (&u)[14], std::integer_seque
   return acc;
 }
 
-// TPC threads per column (a power of two, the same for a whole wave when P >= 64): thread
-// part q computes the outputs a (or row pairs R) with a % TPC == q. All inputs are read
-// before any output is written; the function synchronizes at the end.
-template <typename T, int M, int TPC, int NT>
-__device__ __forceinline__ void hadamard_factor_split(T* buf, int P) {
+// One side of H_28 x (SIDE 0: the 14 outputs y_2R; SIDE 1: the outputs y_2R+1).
+template <typename T, int SIDE>
+__device__ __forceinline__ void hadamard28_side(const T (&x)[28], T (&out)[14]) {
+  T u[14], v[14];
+#pragma unroll
+  for (int c = 0; c < 14; ++c) { u[c] = x[2 * c] + x[2 * c + 1]; v[c] = x[2 * c] - x[2 * c + 1]; }
+  const T(&a)[14] = SIDE == 0 ? u : v;
+  T W = a[1];
+#pragma unroll
+  for (int c = 2; c < 14; ++c) W += a[c];
+  T pr[13];  // pr[k] = w_k + w_{k+1}
+#pragma unroll
+  for (int k = 0; k < 13; ++k) pr[k] = a[1 + k] + a[1 + (k + 1) % 13];
+  const T base = a[0] - W;
+  out[0] = SIDE == 0 ? W + v[0] : W - u[0];
+#pragma unroll
+  for (int r = 0; r < 13; ++r) {
+    const T q = a[1 + (r + 12) % 13] + a[1 + (r + 1) % 13];
+    const T A = pr[(r + 9) % 13] + pr[(r + 3) % 13] + q;
+    const T sum = 2 * A + (base + a[1 + r]);
+    out[r + 1] = SIDE == 0 ? sum + v[r + 1] : sum - u[r + 1];
+  }
+}
+
+// Outputs of part Q of TPC parts of one column: rows a (or row pairs R) with
+// a % TPC == Q. Q is a template constant, so only this part's rows are computed. For H_28
+// TPC is 1 or 2, and part Q computes side Q.
+template <typename T, int M, int TPC, int Q, bool OUT>
+__device__ __forceinline__ void hadamard_part(T* col, int pstride, const T (&x)[M], int b,
+                                              int P, HalfSink sink) {
+  auto put = [&](int a, T v) {
+    if constexpr (OUT) sink.put_at(HalfSink::idx(a * P + b), v);
+    else col[a * pstride] = v;
+  };
+  if constexpr (M == 28) {
+    static_assert(TPC <= 2, "H_28 is split into at most two sides");
+    T out[14];
+    if constexpr (TPC == 1 || Q == 0) {
+      hadamard28_side<T, 0>(x, out);
+#pragma unroll
+      for (int R = 0; R < 14; ++R) put(2 * R, out[R]);
+    }
+    if constexpr (TPC == 1 || Q == 1) {
+      hadamard28_side<T, 1>(x, out);
+#pragma unroll
+      for (int R = 0; R < 14; ++R) put(2 * R + 1, out[R]);
+    }
+  } else {
+    [&]<int... A>(std::integer_sequence<int, A...>) {
+      ((A % TPC == Q ? (put(A, hadamard_row<T, M, A>(x, std::make_integer_sequence<int, M>{})), 0)
+                     : 0),
+       ...);
+    }(std::make_integer_sequence<int, M>{});
+  }
+}
+
+// TPC threads per column (a power of two, the same for a whole wave when P >= 64); thread
+// part q = t / P computes the outputs of its part. All inputs are read before any output is
+// written; the function synchronizes at the end. With OUT the outputs go to the sink.
+template <typename T, int M, int TPC, int NT, bool OUT>
+__device__ __forceinline__ void hadamard_factor_split(T* buf, int P, HalfSink sink) {
   const int t = threadIdx.x;
   const bool active = t < P * TPC;
   const int q = t / P, b = t - q * P;
   T x[M];
-  if (active) {
+  if (P % 16 == 0) {
+    // element (a, b) is at pidx(a * P + b) = pidx(b) + a * (P + P / 16)
+    const int pstride = P + (P >> 4);
+    T* col = buf + pidx(b);
+    if (active) {
+#pragma unroll
+      for (int a = 0; a < M; ++a) x[a] = col[a * pstride];
+    }
+    if constexpr (TPC > 1) __syncthreads();  // the other parts read the same inputs
+    if (active) {
+      [&]<int... Q>(std::integer_sequence<int, Q...>) {
+        ((q == Q ? (hadamard_part<T, M, TPC, Q, OUT>(col, pstride, x, b, P, sink), 0) : 0), ...);
+      }(std::make_integer_sequence<int, TPC>{});
+    }
+  } else if (active) {
+    // rows shorter than 16 (only with TPC == 1): general indexing
 #pragma unroll
     for (int a = 0; a < M; ++a) x[a] = buf[pidx(a * P + b)];
-  }
-  if constexpr (TPC > 1) __syncthreads();  // other parts of the column read the same inputs
-  if (active) {
-    if constexpr (M == 28) {
-      T u[14], v[14];
+    T y[M];
+    [&]<int... A>(std::integer_sequence<int, A...>) {
+      ((y[A] = hadamard_row<T, M, A>(x, std::make_integer_sequence<int, M>{})), ...);
+    }(std::make_integer_sequence<int, M>{});
 #pragma unroll
-      for (int c = 0; c < 14; ++c) { u[c] = x[2 * c] + x[2 * c + 1]; v[c] = x[2 * c] - x[2 * c + 1]; }
-      [&]<int... R>(std::integer_sequence<int, R...>) {
-        (((R % TPC) == q
-              ? (buf[pidx(2 * R * P + b)] =
-                     conference_row<T, R>(u, std::make_integer_sequence<int, 14>{}) + v[R],
-                 buf[pidx((2 * R + 1) * P + b)] =
-                     conference_row<T, R>(v, std::make_integer_sequence<int, 14>{}) - u[R],
-                 0)
-              : 0),
-         ...);
-      }(std::make_integer_sequence<int, 14>{});
-    } else {
-      [&]<int... A>(std::integer_sequence<int, A...>) {
-        (((A % TPC) == q
-              ? (buf[pidx(A * P + b)] =
-                     hadamard_row<T, M, A>(x, std::make_integer_sequence<int, M>{}),
-                 0)
-              : 0),
-         ...);
-      }(std::make_integer_sequence<int, M>{});
+    for (int a = 0; a < M; ++a) {
+      if constexpr (OUT) sink.put_at(HalfSink::idx(a * P + b), y[a]);
+      else buf[pidx(a * P + b)] = y[a];
     }
   }
   __syncthreads();
 }
 
-template <typename T, int M, int NT>
-__device__ __forceinline__ void hadamard_factor_m(T* buf, int P) {
+template <typename T, int M, int NT, bool OUT>
+__device__ __forceinline__ void hadamard_factor_m(T* buf, int P, HalfSink sink) {
   if (P < 64) {
-    hadamard_factor_split<T, M, 1, NT>(buf, P);
+    hadamard_factor_split<T, M, 1, NT, OUT>(buf, P, sink);
     return;
   }
   const int tpc = NT / P;  // 1 .. NT / 64, a power of two
-  if (tpc >= 8) hadamard_factor_split<T, M, 8, NT>(buf, P);
-  else if (tpc == 4) hadamard_factor_split<T, M, 4, NT>(buf, P);
-  else if (tpc == 2) hadamard_factor_split<T, M, 2, NT>(buf, P);
-  else hadamard_factor_split<T, M, 1, NT>(buf, P);
+  if constexpr (M == 28) {
+    if (tpc >= 2) hadamard_factor_split<T, M, 2, NT, OUT>(buf, P, sink);
+    else hadamard_factor_split<T, M, 1, NT, OUT>(buf, P, sink);
+  } else {
+    if (tpc >= 8) hadamard_factor_split<T, M, 8, NT, OUT>(buf, P, sink);
+    else if (tpc == 4) hadamard_factor_split<T, M, 4, NT, OUT>(buf, P, sink);
+    else if (tpc == 2) hadamard_factor_split<T, M, 2, NT, OUT>(buf, P, sink);
+    else hadamard_factor_split<T, M, 1, NT, OUT>(buf, P, sink);
+  }
 }
 
-template <typename T, int NT>
-__device__ __forceinline__ void hadamard_factor(T* buf, int m, int P) {
+template <typename T, int NT, bool OUT = false>
+__device__ __forceinline__ void hadamard_factor(T* buf, int m, int P, HalfSink sink = {}) {
   switch (m) {
-    case 12: hadamard_factor_m<T, 12, NT>(buf, P); break;
-    case 20: hadamard_factor_m<T, 20, NT>(buf, P); break;
-    case 28: hadamard_factor_m<T, 28, NT>(buf, P); break;
+    case 12: hadamard_factor_m<T, 12, NT, OUT>(buf, P, sink); break;
+    case 20: hadamard_factor_m<T, 20, NT, OUT>(buf, P, sink); break;
+    case 28: hadamard_factor_m<T, 28, NT, OUT>(buf, P, sink); break;
     default: break;
   }
 }

@@ -26,6 +26,7 @@ struct InputLoad {
   static constexpr int kW = X32 ? 16 : 8;
   uint32_t raw[kSeg16][kW];
   uint32_t sw[kSeg16];  // the sign word holding each segment's 16 sign bits
+  float v[kSeg16][16];  // the segments after signs and small butterflies
   int dt;
 
   // Segment j of thread t covers elements 16 * (t + NT * j) + 0..15 of row `row`.
@@ -61,17 +62,20 @@ struct InputLoad {
     }
   }
 
-  // Write s * x into xf (padded layout) with the butterflies of stride < 16 applied, find
-  // max |x_i| (one float per wave in `red`, NT / 64 floats of LDS), then finish H_K in LDS
-  // unless `rotated`. Ends synchronized. Returns the power of two sc for the fp16
-  // conversion; *out_scale gets 1 / sc, times 1 / sqrt(K) when the rotation was applied.
+  // First half of the rotation: apply the signs and the butterflies of stride < 16 to
+  // every segment in registers and write them to xf (padded layout; a rotated input that
+  // goes straight to the fp16 layout stays in registers), and find max |x_i| (one float per
+  // wave in `red`, NT / 64 floats of LDS). Ends with a barrier. Returns the power of two sc
+  // for the fp16 conversion; *out_scale gets 1 / sc, times 1 / sqrt(K) when the rotation
+  // is applied here.
   //
   // Every entry of the unnormalized H_K s x is a sum of K terms of size at most
   // max |x_i| < 2^(e + 1), e = ilogb(max |x_i|), so with K <= 2^lk it is below
   // 2^(e + 1 + lk), and sc = 2^(14 - e - lk) keeps every scaled entry below 2^15 (fp16 holds
   // up to 65504). A rotated input is its own bound (lk = 0).
-  __device__ __forceinline__ float finish(float* xf, float* red, int K, int lk, int m, int P,
-                                          bool rotated, float inv_sqrt_k, float* out_scale) {
+  template <bool HALF>
+  __device__ __forceinline__ float finish_a(float* xf, float* red, int K, int lk, int P,
+                                            bool rotated, float inv_sqrt_k, float* out_scale) {
     const int nseg = K >> 4;
     float mx = 0.f;
 #pragma unroll
@@ -79,17 +83,18 @@ struct InputLoad {
       const int sgi = threadIdx.x + NT * j;
       if (sgi >= nseg) continue;
       const uint32_t bits = rotated ? 0u : (sw[j] >> (16 * (sgi & 1))) & 0xffffu;
-      float v[16];
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const float a = elem(j, k);
         mx = fmaxf(mx, fabsf(a));
-        v[k] = __uint_as_float(__float_as_uint(a) ^ (((bits >> k) & 1u) << 31));
+        v[j][k] = __uint_as_float(__float_as_uint(a) ^ (((bits >> k) & 1u) << 31));
       }
-      if (!rotated) seg16_butterflies<float>(v, P);
-      float* dst = xf + 17 * sgi;  // pidx(16 * sgi + k) = 17 * sgi + k
+      if (!rotated) seg16_butterflies<float>(v[j], P);
+      if (!(HALF && rotated)) {
+        float* dst = xf + 17 * sgi;  // pidx(16 * sgi + k) = 17 * sgi + k
 #pragma unroll
-      for (int k = 0; k < 16; ++k) dst[k] = v[k];
+        for (int k = 0; k < 16; ++k) dst[k] = v[j][k];
+      }
     }
     mx = wave_max_nonneg(mx);
     if ((threadIdx.x & 63) == 63) red[threadIdx.x >> 6] = mx;
@@ -97,10 +102,6 @@ struct InputLoad {
     float mall = 0.f;
 #pragma unroll
     for (int w = 0; w < NT / 64; ++w) mall = fmaxf(mall, red[w]);
-    if (!rotated) {
-      sylvester_from16<float, NT>(xf, K, __builtin_ctz(P));
-      hadamard_factor<float, NT>(xf, m, P);
-    }
     int ex = 0;
     if (mall > 0.f && mall <= 3.4028234663852886e38f) {
       ex = 14 - ilogbf(mall) - (rotated ? 0 : lk);
@@ -109,14 +110,53 @@ struct InputLoad {
     *out_scale = ldexpf(1.f, -ex) * (rotated ? 1.f : inv_sqrt_k);
     return ldexpf(1.f, ex);
   }
+
+  // Second half: the remaining stages of H_K in LDS (none for a rotated input). With HALF
+  // the results go, scaled by sc and rounded to fp16, to the chunk layout xh (bit formats:
+  // 32 elements per chunk); otherwise they stay in xf. Ends with a barrier.
+  template <bool HALF>
+  __device__ __forceinline__ void finish_b(float* xf, uint32_t* xh, int K, int m, int P,
+                                           bool rotated, float sc) {
+    const HalfSink sink{reinterpret_cast<_Float16*>(xh), sc};
+    if (rotated) {
+      if constexpr (HALF) {
+        const int nseg = K >> 4;
+#pragma unroll
+        for (int j = 0; j < kSeg16; ++j) {
+          const int sgi = threadIdx.x + NT * j;
+          if (sgi >= nseg) continue;
+          // the 16 elements of a segment are one half of chunk sgi / 2
+          uint32_t hw[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            hw[k] = static_cast<uint32_t>(float_to_half_rne(v[j][2 * k] * sc)) |
+                    (static_cast<uint32_t>(float_to_half_rne(v[j][2 * k + 1] * sc)) << 16);
+          uint4* dst = reinterpret_cast<uint4*>(
+              reinterpret_cast<_Float16*>(xh) + (sgi >> 1) * kChunkHalves + (sgi & 1) * 16);
+          dst[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+          dst[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+        }
+        __syncthreads();
+      }
+      return;
+    }
+    const int lp = __builtin_ctz(P);
+    if (m == 1) {
+      sylvester_from16<float, NT, HALF>(xf, K, lp, sink);
+    } else {
+      sylvester_from16<float, NT, false>(xf, K, lp);
+      hadamard_factor<float, NT, HALF>(xf, m, P, sink);
+    }
+  }
 };
 
 // Words between the fp16 pair slices of consecutive chunks in LDS: the chunk's pairs plus
 // padding, so that the 16-byte reads of 16 consecutive lanes (one chunk each) fall on 16
-// disjoint groups of 4 banks (stride 20 words for 16 pairs, 12 words for 10 pairs).
+// disjoint groups of 4 banks (stride 20 words for 16 pairs, 12 words for 10 pairs). The
+// bit formats' stride is the HalfSink layout the rotation can write directly.
 template <int L>
 constexpr int pair_stride() {
-  return Fmt<L>::np == 16 ? 20 : 12;
+  return Fmt<L>::np == 16 ? kChunkHalves / 2 : 12;
 }
 
 // Convert the rotated row (padded fp32 in xf) once per workgroup to scaled fp16 pairs laid
