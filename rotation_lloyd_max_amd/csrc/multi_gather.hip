@@ -1,26 +1,44 @@
 // multi_gather_qmv: y[p] = W_{ids[p]} R x[p] for P (input, expert) pairs.
 //
 // turboquant-mlx "How it works", "Running a quantized layer", kernel table, second row:
-// prefill with a different input per expert. Pairs are first bucketed by expert on the
-// device (counting sort into the workspace); then each workgroup owns one (expert, row
-// block), rotates the inputs routed to that expert in batches of up to kBatch, and streams
-// the expert's rows once per batch, decoding each chunk once and multiplying it against
-// every input of the batch.
-#include "decode_common.hpp"
+// prefill with a different input per expert. Three launches:
+//   k_bucket   counting sort of the pairs by expert into the workspace (offsets, order);
+//              pairs with an expert id outside [0, E) get a row of NaN
+//   k_rot16    every input rotated once into fp16 rows (rot16.hpp), plus one zero row
+//   k_mg       one workgroup per (expert, block of 64 output rows): each wave decodes the
+//              codes of 16 rows straight into matrix-core operands (mfma_decode.hpp) and
+//              multiplies them by the rotated inputs of up to 16 of the expert's pairs at a
+//              time with v_mfma_f32_16x16x32_f16, so every code word is read from memory
+//              and decoded once per 16 pairs, whatever the number of pairs.
 #include "internal.hpp"
+#include "mfma_decode.hpp"
+#include "rot16.hpp"
 
 namespace tq {
 
-constexpr int kBatch = 8;
 constexpr int kBucketThreads = 1024;
 constexpr int kMaxExperts = 8192;
+constexpr int kMgWaves = 4;
+constexpr int kMgThreads = 64 * kMgWaves;
 
-// Workspace layout: offsets [E+1] int32 | order [P] int32 (16-byte aligned sections).
-static size_t align16(size_t v) { return (v + 15) & ~static_cast<size_t>(15); }
+static size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
-size_t multi_gather_workspace(const WeightArgs& w, int64_t P) {
-  return align16(static_cast<size_t>(w.E + 1) * 4) + align16(static_cast<size_t>(P) * 4);
+// Workspace: offsets [E+1] int32 | order [P] int32 | scale [P+1] float |
+// rotated rows [P+1][rot16_row_halves(K)] fp16 (row P all zero); 256-byte aligned sections.
+struct MgLayout {
+  size_t offsets, order, scale, rows, total;
+};
+static MgLayout mg_layout(const WeightArgs& w, int64_t P) {
+  MgLayout l{};
+  l.offsets = 0;
+  l.order = align256(static_cast<size_t>(w.E + 1) * 4);
+  l.scale = l.order + align256(static_cast<size_t>(P) * 4);
+  l.rows = l.scale + align256(static_cast<size_t>(P + 1) * 4);
+  l.total = l.rows + align256(static_cast<size_t>(P + 1) * rot16_row_halves(w.K) * 2);
+  return l;
 }
+
+size_t multi_gather_workspace(const WeightArgs& w, int64_t P) { return mg_layout(w, P).total; }
 
 __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* ids, int64_t P, int E,
                                                            int32_t* offsets, int32_t* order,
@@ -76,236 +94,248 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* ids, i
   }
 }
 
-struct MultiParams {
+struct MgParams {
   const uint32_t* codes;
   const uint16_t* scales;
-  const uint32_t* signs;
   const int32_t* offsets;
   const int32_t* order;
-  const void* x;
+  const _Float16* xh;  // rotated rows
+  const float* xs;     // their scales
   void* y;
-  int K, N, E, wpr, group, m, P;
-  int xdt, ydt, rotated;
-  int Q, lpr_log, rows_per_block;
-  float inv_sqrt_k;
+  int64_t rowh;        // halves per rotated row
+  int64_t zero_row;    // index of the all-zero row
+  int K, N, E, wpr, lg_group, ngk, ydt;
   CodebookArgs cb;
 };
 
-template <int XDT>
-__device__ __forceinline__ float prepare_input_m(const void* x, int64_t xoff, int K, int m, int P,
-                                        bool rotated, const uint32_t* sb, float* xf, float* red,
-                                        uint32_t* xh2, int xwords, float inv_sqrt_k) {
-  for (int i = threadIdx.x; i < K; i += kBlock) {
-    float v = load_elem<XDT>(x, xoff + i);
-    if (!rotated && ((sb[i >> 5] >> (i & 31)) & 1u)) v = -v;
-    xf[i] = v;
+// k_mg works through K in chunks of 4 super-blocks (4 spans of 4 lane groups each: 512
+// elements for the bit formats, 640 for trits). A chunk's code words and scales of the
+// workgroup's 64 rows, and the rotated inputs of its pairs, are first copied to LDS with
+// loads in which consecutive lanes read consecutive words of a row (each cache line is
+// touched once per chunk); the next chunk's loads are held in registers meanwhile. The
+// matrix-core operands are then read from LDS, where each lane's span is contiguous.
+template <int L>
+struct MgChunk {
+  static constexpr int SB = 4 * Span<L>::elems;  // elements per super-block
+  static constexpr int KC = 4 * SB;              // elements per chunk
+  static constexpr int WPC = L == 3 ? KC / 20 : KC * (L == 16 ? 4 : L == 8 ? 3 : 2) / 32;
+  static constexpr int CST = WPC + 4;            // LDS words per row of codes
+  static constexpr int AST = KC + 8;             // LDS halves per row of inputs
+  static constexpr int ROWS = 16 * kMgWaves;     // weight rows per workgroup
+  static constexpr int CW = ROWS * WPC / kMgThreads;        // code words per thread
+  static constexpr int AU = 16 * (KC / 8) / kMgThreads;     // 16-byte input units per thread
+};
+
+constexpr int kMaxScalesPerChunk = 640 / 16;  // groups of a chunk at most (trits, g16)
+
+template <int L>
+struct MgStage {
+  uint32_t c[MgChunk<L>::CW];
+  uint32_t s[(MgChunk<L>::ROWS * kMaxScalesPerChunk + kMgThreads - 1) / kMgThreads];
+  u32x4_t a[MgChunk<L>::AU];
+};
+
+struct MgTile {
+  int row0;    // first weight row of the workgroup
+  int cnt;     // pairs of this tile (<= 16)
+  int spc;     // scale groups per chunk (KC / group, at least 1)
+  int sst;     // LDS halves per row of scales
+  const uint32_t* cexp;   // the expert's codes
+  const uint16_t* sexp;   // the expert's scales
+  const int32_t* pairs;   // the tile's pair indices
+};
+
+// Global -> registers for chunk c.
+template <int L>
+__device__ __forceinline__ void mg_fetch(MgStage<L>& st, const MgParams& p, const MgTile& t, int c) {
+  using C = MgChunk<L>;
+  const int w0 = c * C::WPC;
+  // the thread index is made opaque so that the per-load offsets are recomputed for every
+  // chunk instead of being kept in registers for the whole loop
+  int tid = static_cast<int>(threadIdx.x);
+  __asm__ volatile("" : "+v"(tid));
+#pragma unroll
+  for (int j = 0; j < C::CW; ++j) {
+    const int i = tid + j * kMgThreads;
+    const int r = i / C::WPC, w = i - r * C::WPC;
+    int row = t.row0 + r;
+    row = row < p.N ? row : p.N - 1;
+    int wi = w0 + w;
+    wi = wi < p.wpr ? wi : p.wpr - 1;
+    st.c[j] = ld_at<uint32_t>(t.cexp, (static_cast<uint32_t>(row) * p.wpr + wi) * 4u);
   }
-  __syncthreads();
-  if (!rotated) hadamard_lds<float>(xf, 1, m, P);
-  float mx = 0.f;
-  for (int i = threadIdx.x; i < K; i += kBlock) mx = fmaxf(mx, fabsf(xf[i]));
-  mx = block_max(mx, red);
-  int ex = 0;
-  if (mx > 0.f && mx <= 3.0e38f) {
-    ex = 14 - ilogbf(mx);
-    ex = ex < -100 ? -100 : (ex > 100 ? 100 : ex);
+  const int g0 = (c * C::KC) >> p.lg_group;
+  constexpr int NS = sizeof(st.s) / sizeof(st.s[0]);
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int i = tid + j * kMgThreads;
+    const int r = i / t.spc, k = i - r * t.spc;
+    int row = t.row0 + (r < C::ROWS ? r : C::ROWS - 1);
+    row = row < p.N ? row : p.N - 1;
+    int gi = g0 + k;
+    gi = gi < p.ngk ? gi : p.ngk - 1;
+    st.s[j] = ld_at<uint16_t>(t.sexp, (static_cast<uint32_t>(row) * p.ngk + gi) * 2u);
   }
-  const float sc = ldexpf(1.f, ex);
-  for (int q = threadIdx.x; q < xwords; q += kBlock) {
-    const int i0 = 2 * q, i1 = 2 * q + 1;
-    const float a = i0 < K ? xf[i0] * sc : 0.f;
-    const float b = i1 < K ? xf[i1] * sc : 0.f;
-    xh2[q] = static_cast<uint32_t>(float_to_half_rne(a)) |
-             (static_cast<uint32_t>(float_to_half_rne(b)) << 16);
+#pragma unroll
+  for (int j = 0; j < C::AU; ++j) {
+    const int i = tid + j * kMgThreads;
+    const int m = i / (C::KC / 8), u = i - m * (C::KC / 8);
+    const int e = c * C::KC + 8 * u;
+    if (m < t.cnt) {
+      const uint32_t row = static_cast<uint32_t>(t.pairs[m]);
+      const int ec = e < p.K ? e : p.K - 8;
+      const u32x4_t v = ld_at<u32x4_t>(p.xh, (row * static_cast<uint32_t>(p.rowh) + ec) * 2u);
+      st.a[j] = e < p.K ? v : u32x4_t{0u, 0u, 0u, 0u};
+    }
   }
-  __syncthreads();
-  return ldexpf(1.f, -ex) * (rotated ? 1.f : inv_sqrt_k);
+}
+
+// Registers -> LDS.
+template <int L>
+__device__ __forceinline__ void mg_stash(const MgStage<L>& st, const MgTile& t, uint32_t* lc,
+                                         uint16_t* ls, _Float16* la) {
+  using C = MgChunk<L>;
+#pragma unroll
+  for (int j = 0; j < C::CW; ++j) {
+    const int i = threadIdx.x + j * kMgThreads;
+    const int r = i / C::WPC, w = i - r * C::WPC;
+    lc[r * C::CST + w] = st.c[j];
+  }
+  constexpr int NS = sizeof(st.s) / sizeof(st.s[0]);
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int i = threadIdx.x + j * kMgThreads;
+    const int r = i / t.spc, k = i - r * t.spc;
+    if (r < C::ROWS) ls[r * t.sst + k] = static_cast<uint16_t>(st.s[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < C::AU; ++j) {
+    const int i = threadIdx.x + j * kMgThreads;
+    const int m = i / (C::KC / 8), u = i - m * (C::KC / 8);
+    if (m < t.cnt) *reinterpret_cast<u32x4_t*>(la + m * C::AST + 8 * u) = st.a[j];
+  }
 }
 
 template <int L>
-__device__ __forceinline__ void load_chunk_m(const uint32_t* crow, int c, bool ok, uint32_t (&w)[Fmt<L>::cw]) {
-  using F = Fmt<L>;
-  if (!ok) {
-#pragma unroll
-    for (int i = 0; i < F::cw; ++i) w[i] = 0;
-    return;
-  }
-  const uint32_t* p = crow + c * F::cw;
-#pragma unroll
-  for (int i = 0; i < F::cw; ++i) w[i] = p[i];
-}
-
-template <int L, int CPL, int XDT>
-__global__ __launch_bounds__(kBlock) void k_multi(MultiParams p) {
-  using F = Fmt<L>;
+__global__ __launch_bounds__(kMgThreads) void k_mg(MgParams p) {
+  using S = Span<L>;
+  using C = MgChunk<L>;
+  // the table is the only static LDS array: it starts at address 0
+  __shared__ __attribute__((aligned(16))) uint32_t lut[mlut_bytes<L>() / 4];
+  __shared__ __attribute__((aligned(16))) uint32_t lc[C::ROWS * C::CST];
+  __shared__ __attribute__((aligned(16))) _Float16 la[16 * C::AST];
+  __shared__ uint16_t ls[C::ROWS * (kMaxScalesPerChunk + 2)];
+  __shared__ uint16_t hs[16];
   const int e = blockIdx.y;
-  const int off = p.offsets[e];
-  const int cnt = p.offsets[e + 1] - off;
-  if (cnt <= 0) return;
-  const int64_t row_begin = static_cast<int64_t>(blockIdx.x) * p.rows_per_block;
-  if (row_begin >= p.N) return;
-  int64_t row_end = row_begin + p.rows_per_block;
-  if (row_end > p.N) row_end = p.N;
+  const int off0 = p.offsets[e], cnt_all = p.offsets[e + 1] - off0;
+  if (cnt_all <= 0) return;  // uniform per workgroup
 
-  extern __shared__ uint32_t smem_u[];
-  const int xwords = p.Q * F::ce / 2;
-  uint32_t* lut = smem_u;
-  uint32_t* xh2 = lut + F::entries * kLutCopies;           // kBatch * xwords
-  float* xf = reinterpret_cast<float*>(xh2 + kBatch * xwords);  // K
-  float* red = xf + p.K;                                   // 32
-  float* oscale = red + 32;                                // kBatch
-  int* pidx = reinterpret_cast<int*>(oscale + kBatch);     // kBatch
-  uint32_t* sb = reinterpret_cast<uint32_t*>(pidx + kBatch);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, col = lane & 15;
+  const uint32_t slot = mlut_slot<L>(lane);
+  MgTile t;
+  t.row0 = blockIdx.x * C::ROWS;
+  t.spc = (C::KC >> p.lg_group) > 0 ? (C::KC >> p.lg_group) : 1;
+  t.sst = t.spc + 2;
+  t.cexp = p.codes + static_cast<int64_t>(e) * p.N * p.wpr;
+  t.sexp = p.scales + static_cast<int64_t>(e) * p.N * p.ngk;
+  const int nrow = wave * 16 + col;  // this lane's weight row within the workgroup
+  const int n = t.row0 + nrow;
+  const int nchunk = (p.K + C::KC - 1) / C::KC;
+  // fragment f of a span uses scale ((e0 + 8 f) >> lg) - (chunk start >> lg) of the chunk
+  MgStage<L> st;
 
-  build_lut<L>(lut, p.cb.h);
-  if (!p.rotated)
-    for (int w = threadIdx.x; w < (p.K + 31) / 32; w += kBlock) sb[w] = p.signs[w];
-  __syncthreads();
-
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lane31 = lane & 31;
-  const int lpr = 1 << p.lpr_log;
-  const int sub = lane >> p.lpr_log, c0 = lane & (lpr - 1);
-  const int rpw = 64 >> p.lpr_log;
-  const int ngroups = p.K / p.group;
-
-  for (int b0 = 0; b0 < cnt; b0 += kBatch) {
-    const int nb = cnt - b0 < kBatch ? cnt - b0 : kBatch;
-    for (int j = 0; j < nb; ++j) {
-      const int pp = p.order[off + b0 + j];
-      const float os = prepare_input_m<XDT>(p.x, static_cast<int64_t>(pp) * p.K, p.K, p.m, p.P,
-                                            p.rotated != 0, sb, xf, red, xh2 + j * xwords, xwords,
-                                            p.inv_sqrt_k);
-      if (threadIdx.x == 0) { oscale[j] = os; pidx[j] = pp; }
+  if (threadIdx.x < 16) hs[threadIdx.x] = p.cb.h[threadIdx.x];
+  for (int m0 = 0; m0 < cnt_all; m0 += 16) {
+    t.cnt = cnt_all - m0 < 16 ? cnt_all - m0 : 16;
+    t.pairs = p.order + off0 + m0;
+    mg_fetch<L>(st, p, t, 0);
+    if (m0 == 0) {
+      __syncthreads();
+      build_mlut<L, kMgThreads>(lut, hs);
     }
-    __syncthreads();
-
-    for (int64_t rb = row_begin + wave * rpw; rb < row_end; rb += 4 * rpw) {
-      const int64_t n = rb + sub;
-      const bool active = n < row_end;
-      const int64_t wrow = active ? static_cast<int64_t>(e) * p.N + n : 0;
-      const uint32_t* crow = p.codes + wrow * p.wpr;
-      const uint16_t* srow = p.scales + wrow * ngroups;
-      float acc[kBatch];
+    const bool valid = col < t.cnt;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < nchunk; ++c) {
+      __syncthreads();  // previous chunk's LDS reads are done
+      mg_stash<L>(st, t, lc, ls, la);
+      __syncthreads();
+      if (c + 1 < nchunk) mg_fetch<L>(st, p, t, c + 1);
+      // super-blocks of this chunk that hold elements below K
+      const int kc0 = c * C::KC;
+      const int nsb = (p.K - kc0 + C::SB - 1) / C::SB < 4 ? (p.K - kc0 + C::SB - 1) / C::SB : 4;
+#pragma unroll 1
+      for (int sb = 0; sb < nsb; ++sb) {
+        const int e0 = sb * C::SB + g * S::elems;  // within the chunk
+        uint32_t w[S::words];
+        const uint32_t* src = lc + nrow * C::CST + span_first_word<L>(e0);
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) acc[j] = 0.f;
+        for (int i = 0; i < S::words; ++i) w[i] = src[i];
+        uint32_t s2[S::mf];
 #pragma unroll
-      for (int jc = 0; jc < CPL; ++jc) {
-        const int c = c0 + jc * lpr;
-        const bool ok = active && c < p.Q;
-        if (!ok) continue;
-        uint32_t w[F::cw];
-        load_chunk_m<L>(crow, c, true, w);
-        int g0, g1, pb;
-        {
-          const int e0 = c * F::ce;
-          g0 = e0 / p.group;
-          const int bound = (g0 + 1) * p.group - e0;
-          pb = bound >= F::ce ? F::np : bound / 2;
-          g1 = g0 + 1 < ngroups ? g0 + 1 : g0;
+        for (int f = 0; f < S::mf; ++f) {
+          const int gi = (kc0 + e0 + 8 * f) >> p.lg_group;
+          const int gl = gi - (kc0 >> p.lg_group);
+          s2[f] = __umul24(static_cast<uint32_t>(ls[nrow * t.sst + gl]), 0x10001u);
         }
-        const float s0 = half_bits_to_float(srow[g0]);
-        const float s1 = half_bits_to_float(srow[g1]);
-        int idx[F::np];
-        chunk_indices<L>(w, idx);
-        uint32_t cwv[F::np];
+        u32x4_t b[S::mf];
+        span_fragments<L>(w, lut, slot, s2, b);
 #pragma unroll
-        for (int q = 0; q < F::np; ++q) cwv[q] = lut[idx[q] * kLutCopies + lane31];
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-          if (j < nb) {
-            const uint32_t* xp = xh2 + j * xwords + c * (F::ce / 2);
-            float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-            for (int q = 0; q < F::np; ++q) {
-              if (q < pb) a0 = dot2_h(cwv[q], xp[q], a0);
-              else a1 = dot2_h(cwv[q], xp[q], a1);
-            }
-            acc[j] += a0 * s0 + a1 * s1;
-          }
+        for (int f = 0; f < S::mf; ++f) {
+          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(la + col * C::AST + e0 + 8 * f);
+          acc = mfma_f16(valid ? a : u32x4_t{0u, 0u, 0u, 0u}, b[f], acc);
         }
       }
+    }
+    // D[4 g + r][col] = output row n of pair m0 + 4 g + r
+    if (n < p.N) {
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        float a = acc[j];
-        for (int o = lpr >> 1; o >= 1; o >>= 1) a += __shfl_xor(a, o, 64);
-        if (active && c0 == 0 && j < nb)
-          store_any(p.y, p.ydt, static_cast<int64_t>(pidx[j]) * p.N + n, a * oscale[j]);
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * g + r;
+        if (m < t.cnt) {
+          const int pr = t.pairs[m];
+          store_any(p.y, p.ydt, static_cast<int64_t>(pr) * p.N + n, acc[r] * p.xs[pr]);
+        }
       }
     }
-    __syncthreads();
   }
-}
-
-static int pow2_ceil_log_m(int v) {
-  int l = 0;
-  while ((1 << l) < v) ++l;
-  return l;
-}
-
-template <int L>
-static hipError_t launch_multi_l(MultiParams& p, hipStream_t s) {
-  using F = Fmt<L>;
-  p.Q = (p.wpr + F::cw - 1) / F::cw;
-  int lpr_log = pow2_ceil_log_m(p.Q);
-  if (lpr_log > 6) lpr_log = 6;
-  p.lpr_log = lpr_log;
-  const int lpr = 1 << lpr_log;
-  const int cpl_need = (p.Q + lpr - 1) / lpr;
-  const int rpw = 64 / lpr;
-  // row blocks per expert: aim for ~8 blocks per expert, at least one row step per wave
-  int rpb = (p.N + 7) / 8;
-  const int step = 4 * rpw;
-  rpb = ((rpb + step - 1) / step) * step;
-  p.rows_per_block = rpb;
-  const int gx = (p.N + rpb - 1) / rpb;
-  const size_t lds = (F::entries * kLutCopies + kBatch * (p.Q * F::ce / 2)) * 4 +
-                     (p.K + 32 + 2 * kBatch) * 4 + ((p.K + 31) / 32) * 4;
-  void (*kern)(MultiParams) = nullptr;
-#define TQ_PICK(C)                                                  \
-  switch (p.xdt) {                                                  \
-    case 0: kern = k_multi<L, C, 0>; break;                         \
-    case 1: kern = k_multi<L, C, 1>; break;                         \
-    default: kern = k_multi<L, C, 2>; break;                        \
-  }
-  if (cpl_need <= 1) { TQ_PICK(1) }
-  else if (cpl_need <= 2) { TQ_PICK(2) }
-  else if (cpl_need <= 4) { TQ_PICK(4) }
-  else { TQ_PICK(8) }
-#undef TQ_PICK
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(kern, dim3(gx, p.E), dim3(kBlock), lds, s, p);
-  return hipGetLastError();
 }
 
 hipError_t launch_multi_gather(const WeightArgs& w, const int32_t* ids, int64_t P, const void* x,
                                int xdt, bool x_rotated, void* y, int ydt, void* ws,
                                hipStream_t s) {
   if (P == 0 || w.N == 0) return hipSuccess;
-  int32_t* offsets = static_cast<int32_t*>(ws);
-  int32_t* order = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
-                                              align16(static_cast<size_t>(w.E + 1) * 4));
+  const MgLayout lay = mg_layout(w, P);
+  char* base = static_cast<char*>(ws);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + lay.offsets);
+  int32_t* order = reinterpret_cast<int32_t*>(base + lay.order);
+  float* xs = reinterpret_cast<float*>(base + lay.scale);
+  _Float16* xh = reinterpret_cast<_Float16*>(base + lay.rows);
   hipLaunchKernelGGL(k_bucket, dim3(1), dim3(kBucketThreads), 0, s, ids, P, w.E, offsets, order, y,
                      ydt, w.N);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  MultiParams p{};
-  p.codes = w.codes; p.scales = w.scales; p.signs = w.signs; p.offsets = offsets; p.order = order;
-  p.x = x; p.y = y;
-  p.K = w.K; p.N = w.N; p.E = w.E; p.wpr = w.wpr; p.group = w.group; p.m = w.m; p.P = w.P;
-  p.xdt = xdt; p.ydt = ydt; p.rotated = x_rotated ? 1 : 0;
-  p.inv_sqrt_k = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(w.K)));
+
+  err = launch_rot16(x, xdt, nullptr, P, /*zero_rows=*/1, w, x_rotated, xh, xs, s);
+  if (err != hipSuccess) return err;
+
+  MgParams p{};
+  p.codes = w.codes; p.scales = w.scales; p.offsets = offsets; p.order = order;
+  p.xh = xh; p.xs = xs; p.y = y;
+  p.rowh = rot16_row_halves(w.K);
+  p.zero_row = P;
+  p.K = w.K; p.N = w.N; p.E = w.E; p.wpr = w.wpr; p.ngk = w.K / w.group;
+  p.lg_group = __builtin_ctz(w.group);
+  p.ydt = ydt;
   p.cb = *codebook_for(w.levels);
+  const dim3 grid((w.N + 16 * kMgWaves - 1) / (16 * kMgWaves), w.E);
   switch (w.levels) {
-    case 16: return launch_multi_l<16>(p, s);
-    case 8: return launch_multi_l<8>(p, s);
-    case 4: return launch_multi_l<4>(p, s);
-    default: return launch_multi_l<3>(p, s);
+    case 16: hipLaunchKernelGGL(k_mg<16>, grid, dim3(kMgThreads), 0, s, p); break;
+    case 8: hipLaunchKernelGGL(k_mg<8>, grid, dim3(kMgThreads), 0, s, p); break;
+    case 4: hipLaunchKernelGGL(k_mg<4>, grid, dim3(kMgThreads), 0, s, p); break;
+    default: hipLaunchKernelGGL(k_mg<3>, grid, dim3(kMgThreads), 0, s, p); break;
   }
+  return hipGetLastError();
 }
 
 }  // namespace tq
