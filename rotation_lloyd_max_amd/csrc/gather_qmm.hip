@@ -3,220 +3,464 @@
 //
 // turboquant-mlx "How it works", "Running a quantized layer", kernel table, third row (a
 // large batch sorted by expert). Three launches on the caller's stream:
-//   1. rotate the T input rows once into a bf16 workspace (x' = R x);
-//   2. a tile schedule: tile_start[e] = sum over experts before e of ceil(rows_e / BM);
-//   3. the GEMM: one workgroup per (row tile of one expert, BN output columns). Weights
-//      are decoded (centroid * group scale, rounded to bf16) into an LDS tile, the routed
-//      input rows are gathered into another, and bf16 MFMA 16x16x32 accumulates in fp32.
-#include "device_common.hpp"
+//   1. k_rot16: the T input rows rotated once into an fp16 workspace with a power-of-two
+//      scale per row (rot16.hpp), plus one zero row;
+//   2. k_schedule: the table of (expert, 128-row tile) pairs;
+//   3. k_gqmm: one workgroup per (tile of 128 rows of one expert, 512 output columns).
+//
+// k_gqmm. The 8 waves of a workgroup share the tile's 128 gathered input rows, staged
+// through LDS one K step at a time (double-buffered, loaded a step ahead with coalesced
+// 16-byte loads). Each wave owns 64 output columns: its lanes load and decode their own
+// packed codes straight into matrix-core operands (mfma_decode.hpp, the same decoder as
+// multi_gather_qmv) and multiply them with v_mfma_f32_32x32x16_f16, so a weight element
+// is decoded once per tile and never goes through LDS. Experts with fewer rows than a
+// tile run only the 32-row sub-tiles that hold rows.
+//
+// For v_mfma_f32_32x32x16_f16 lane l holds A[l % 32][8 (l / 32) + j], B[8 (l / 32) + j][l % 32]
+// (j < 8) and gets D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32] (r < 16). As in multi_gather,
+// the K order inside an instruction is free: lane group g = l / 32 takes a contiguous span
+// of SPAN elements of the step (Span<L>), fed to MF consecutive instructions 8 at a time.
+#include <type_traits>
+
 #include "internal.hpp"
+#include "mfma_decode.hpp"
+#include "rot16.hpp"
 
 namespace tq {
 
-constexpr int kBM = 64, kBN = 64, kBK = 32, kLdsK = kBK + 8;
+constexpr int kQmmWaves = 8;
+constexpr int kQmmThreads = 64 * kQmmWaves;
+constexpr int kQmmBM = 128;                      // rows per tile: 4 sub-tiles of 32
+constexpr int kQmmWN = 64;                       // output columns per wave: 2 tiles of 32
+constexpr int kQmmBN = kQmmWN * kQmmWaves;       // output columns per workgroup
+
+template <int L>
+struct QmmStep {
+  static constexpr int BK = 2 * Span<L>::elems;                 // elements per K step
+  static constexpr int AST = BK + 8;                            // LDS halves per input row
+  static constexpr int UPR = BK / 8;                            // 16-byte units per row
+  static constexpr int AU = (kQmmBM * UPR + kQmmThreads - 1) / kQmmThreads;
+};
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 static size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
+constexpr int kMaxExpertsQmm = 8192;
+__device__ __forceinline__ int64_t max_tiles_dev(int64_t M, int E) { return (M + kQmmBM - 1) / kQmmBM + E; }
+
+// Workspace: rotated rows [T+1][K] fp16 (row T all zero) | row scales [T+1] float |
+// tile count int32 | tile table int4 [M / 128 + E] ({expert, first row, rows, 0});
+// 256-byte aligned sections.
+struct QmmLayout {
+  size_t rows, scale, count, tiles, total;
+};
+static int64_t max_tiles(int64_t M, int E) { return (M + kQmmBM - 1) / kQmmBM + E; }
+static QmmLayout qmm_layout(const WeightArgs& w, int64_t M, int64_t T) {
+  QmmLayout l{};
+  l.rows = 0;
+  l.scale = align256(static_cast<size_t>(T + 1) * rot16_row_halves(w.K) * 2);
+  l.count = l.scale + align256(static_cast<size_t>(T + 1) * 4);
+  l.tiles = l.count + 256;
+  l.total = l.tiles + align256(static_cast<size_t>(max_tiles(M, w.E)) * 16);
+  return l;
+}
+
 size_t gather_qmm_workspace(const WeightArgs& w, int64_t M, int64_t T) {
-  (void)M;
-  return align256(static_cast<size_t>(T) * w.K * 2) + align256(static_cast<size_t>(w.E + 1) * 4);
+  return qmm_layout(w, M, T).total;
 }
 
-__global__ void k_schedule(const int32_t* offsets, int E, int32_t* tile_start) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  int acc = 0;
-  for (int e = 0; e < E; ++e) {
-    tile_start[e] = acc;
+constexpr int kSchedThreads = 1024;
+
+// The tile table: expert e's rows offsets[e] .. offsets[e+1] - 1 are cut into tiles of
+// 128; tiles are listed expert by expert. Experts with no rows (or inconsistent offsets)
+// get no tile; the table never holds more than max_tiles entries.
+__global__ __launch_bounds__(kSchedThreads) void k_schedule(const int32_t* offsets, int E,
+                                                           int64_t M, int32_t* count,
+                                                           int4* tiles) {
+  __shared__ int32_t start[kMaxExpertsQmm + 1];
+  for (int e = threadIdx.x; e < E; e += kSchedThreads) {
     const int rows = offsets[e + 1] - offsets[e];
-    acc += rows > 0 ? (rows + kBM - 1) / kBM : 0;
+    start[e + 1] = rows > 0 ? (rows + kQmmBM - 1) / kQmmBM : 0;
   }
-  tile_start[E] = acc;
-}
-
-__global__ __launch_bounds__(kBlock) void k_to_bf16(const void* x, int xdt, int64_t n, uint16_t* out) {
-  for (int64_t i = blockIdx.x * static_cast<int64_t>(kBlock) + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * kBlock)
-    out[i] = float_to_bf16_rne(load_any(x, xdt, i));
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int64_t cap = max_tiles_dev(M, E);
+    int acc = 0;
+    start[0] = 0;
+    for (int e = 0; e < E; ++e) {
+      int n = start[e + 1];
+      n = acc + n <= cap ? n : static_cast<int>(cap - acc);
+      acc += n;
+      start[e + 1] = acc;
+    }
+    *count = acc;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kSchedThreads) {
+    const int o0 = offsets[e], o1 = offsets[e + 1];
+    for (int k = start[e]; k < start[e + 1]; ++k) {
+      const int m0 = o0 + (k - start[e]) * kQmmBM;
+      const int rows = o1 - m0 < kQmmBM ? o1 - m0 : kQmmBM;
+      tiles[k] = make_int4(e, m0, rows, 0);
+    }
+  }
 }
 
 struct QmmParams {
   const uint32_t* codes;
   const uint16_t* scales;
-  const uint16_t* xr;  // bf16 [T][K], rotated
+  const _Float16* xh;     // rotated rows [T+1][K]
+  const float* xs;        // their scales
   const int32_t* row_token;
-  const int32_t* offsets;
-  const int32_t* tile_start;
+  const int32_t* count;
+  const int4* tiles;
   void* y;
   int64_t T, M;
-  int K, N, E, wpr, group, ydt;
+  int K, N, E, wpr, lg_group, ngk, ydt;
   CodebookArgs cb;
 };
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x16_t mfma32_f16(const u32x4_t& a, const u32x4_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
 
-// Codebook indices of the 8 elements j0 .. j0+7 of a packed row (j0 a multiple of 8).
-template <int L>
-__device__ __forceinline__ void decode8(const uint32_t* crow, int j0, int (&idx)[8]) {
-  if constexpr (L == 16) {
-    const uint32_t w = crow[j0 >> 3];
+// Scales a lane needs per span: one for the bit formats with groups of 32 or more (a
+// 32-element span lies in one group), two with groups of 16, one per fragment for trits
+// (40-element spans are not aligned to groups).
+template <int L, bool G16>
+constexpr int span_scales() {
+  return L == 3 ? Span<L>::mf : (G16 ? 2 : 1);
+}
+
+// Registers of one pipeline stage: the codes and scales of both column tiles of a lane
+// for one K step, and the thread's share of the step's input tile.
+template <int L, bool G16>
+struct QmmStage {
+  uint32_t w[2][Span<L>::words];
+  uint16_t s[2][span_scales<L, G16>()];
+  u32x4_t a[QmmStep<L>::AU];
+};
+
+template <typename T>
+__device__ __forceinline__ T to_out(float v) {
+  return static_cast<T>(v);  // bf16: v_cvt_pk_bf16_f32 (round to nearest even)
+}
+
+// Stores of one wave's results: column n (and n + 32) of rows m0 + 32 mt + 8 q + 4 g + i.
+template <typename T, int MT>
+__device__ __forceinline__ void qmm_store(const QmmParams& p, const f32x16_t (&acc)[MT][2], int m0,
+                                          int mrows, int n, int g, const float* txs) {
+  T* y = static_cast<T*>(p.y);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) idx[k] = (w >> (4 * k)) & 15;
-  } else if constexpr (L == 4) {
-    const uint32_t w = crow[j0 >> 4] >> (2 * (j0 & 15));
+  for (int mt = 0; mt < MT; ++mt) {
+    float sc[16];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) idx[k] = (w >> (2 * k)) & 3;
-  } else if constexpr (L == 8) {
-    const int bit = 3 * j0, lo = bit >> 5, sh = bit & 31;
-    uint64_t v = crow[lo] >> sh;
-    if (sh > 8) v |= static_cast<uint64_t>(crow[lo + 1]) << (32 - sh);
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = *reinterpret_cast<const float4*>(txs + 32 * mt + 8 * q + 4 * g);
+      sc[4 * q] = v.x; sc[4 * q + 1] = v.y; sc[4 * q + 2] = v.z; sc[4 * q + 3] = v.w;
+    }
+    const bool full = 32 * mt + 32 <= mrows;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) idx[k] = static_cast<int>((v >> (3 * k)) & 7);
-  } else {
+    for (int j = 0; j < 2; ++j) {
+      const int col = n + 32 * j;
+      if (col >= p.N) continue;
+      T* base = y + static_cast<int64_t>(m0 + 32 * mt + 4 * g) * p.N + col;
+      if (full) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int j = j0 + k;
-      uint32_t w = crow[j / 20];
-      for (int d = j % 20; d > 0; --d) w /= 3u;
-      idx[k] = static_cast<int>(w % 3u);
+        for (int r = 0; r < 16; ++r)
+          base[(8 * (r >> 2) + (r & 3)) * p.N] = to_out<T>(acc[mt][j][r] * sc[r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 8 * (r >> 2) + (r & 3);
+          if (32 * mt + 4 * g + row < mrows) base[row * p.N] = to_out<T>(acc[mt][j][r] * sc[r]);
+        }
+      }
     }
   }
 }
 
-template <int L>
-__global__ __launch_bounds__(kBlock) void k_gqmm(QmmParams p) {
-  const int t = blockIdx.x;
-  const int total = p.tile_start[p.E];
-  if (t >= total) return;
-  int lo = 0, hi = p.E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (p.tile_start[mid] <= t) lo = mid;
-    else hi = mid - 1;
+template <int L, int MT, bool G16>
+__device__ __forceinline__ void qmm_tile(const QmmParams& p, int e, int m0, int mrows, int n0,
+                                         const uint32_t* lut, _Float16* la, const int32_t* tok,
+                                         const float* txs) {
+  using S = Span<L>;
+  using Q = QmmStep<L>;
+  constexpr int NSC = span_scales<L, G16>();
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 5, c32 = lane & 31;
+  const uint32_t slot = mlut_slot<L>(lane);
+
+  // this lane's two packed rows (output columns), clamped to the last row, as 32-bit offsets
+  // from the expert's codes and scales
+  const uint32_t* cexp = p.codes + static_cast<int64_t>(e) * p.N * p.wpr;
+  const uint16_t* sexp = p.scales + static_cast<int64_t>(e) * p.N * p.ngk;
+  uint32_t coff[2], soff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    int n = n0 + wave * kQmmWN + 32 * j + c32;
+    n = n < p.N ? n : p.N - 1;
+    coff[j] = static_cast<uint32_t>(n) * p.wpr * 4u;
+    soff[j] = static_cast<uint32_t>(n) * p.ngk * 2u;
   }
-  const int e = lo;
-  const int m0 = p.offsets[e] + (t - p.tile_start[e]) * kBM;
-  int mrows = p.offsets[e + 1] - m0;
-  if (mrows > kBM) mrows = kBM;
-  if (m0 < 0 || m0 >= p.M) return;  // inconsistent offsets: never touch memory past y
-  if (mrows > p.M - m0) mrows = static_cast<int>(p.M - m0);
-  const int n0 = blockIdx.y * kBN;
-
-  __shared__ uint16_t As[kBM * kLdsK];
-  __shared__ uint16_t Bs[kBN * kLdsK];
-  __shared__ int tok[kBM];
-  __shared__ float cent[16];
-  const int tid = threadIdx.x;
-  if (tid < kBM) {
-    int v = -1;  // -1: padding row of the tile; -2: token id out of range (row of NaN)
-    if (tid < mrows) {
-      v = p.row_token[m0 + tid];
-      if (v < 0 || v >= p.T) v = -2;
-    }
-    tok[tid] = v;
+  // this thread's 16-byte units of the input tile (a unit past the tile, which only the
+  // trit format has, loads the tile's first unit and is not stored)
+  const _Float16* asrc[Q::AU];
+  int aoff[Q::AU], ak[Q::AU];
+  bool aon[Q::AU];
+#pragma unroll
+  for (int j = 0; j < Q::AU; ++j) {
+    const int i = threadIdx.x + j * kQmmThreads;
+    aon[j] = i < kQmmBM * Q::UPR;
+    const int ic = aon[j] ? i : 0;
+    const int r = ic / Q::UPR, u = ic - r * Q::UPR;
+    asrc[j] = p.xh + static_cast<int64_t>(tok[r]) * rot16_row_halves(p.K) + 8 * u;
+    aoff[j] = r * Q::AST + 8 * u;
+    ak[j] = 8 * u;
   }
-  if (tid < 16) cent[tid] = tid < p.cb.levels ? p.cb.c[tid] : 0.f;
-  __syncthreads();
+  // an even number of steps, so that the loop below runs both halves every time; steps
+  // past K read zero inputs
+  const int nsteps = ((p.K + 2 * Q::BK - 1) / (2 * Q::BK)) * 2;
+  const int last = (p.K - 1) / Q::BK;  // last step holding elements
 
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  f32x4_t acc[2][2];
+  // Loads are issued unconditionally (indices clamped) so that every loop iteration has the
+  // same memory operations and the compiler's count of outstanding loads stays exact.
+  auto load_codes = [&](QmmStage<L, G16>& st, int step) {
+    step = step < last ? step : last;
+    const int e0 = step * Q::BK + g * S::elems;
+    const int fw = span_first_word<L>(e0);
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 2; ++j) {
+      if constexpr (L == 16) {
+        const u32x4_t v = ld_at<u32x4_t>(cexp, coff[j] + fw * 4u);
+        st.w[j][0] = v[0]; st.w[j][1] = v[1]; st.w[j][2] = v[2]; st.w[j][3] = v[3];
+      } else if constexpr (L == 4) {
+        const uint2 v = ld_at<uint2>(cexp, coff[j] + fw * 4u);
+        st.w[j][0] = v.x; st.w[j][1] = v.y;
+      } else {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int lr = tid >> 2, seg = tid & 3;  // loader row and 8-element segment
-  const int ngroups = p.K / p.group;
-  const int nrow = n0 + lr;
-  const bool nvalid = nrow < p.N;
-  const int64_t wrow = static_cast<int64_t>(e) * p.N + (nvalid ? nrow : 0);
-  const uint32_t* crow = p.codes + wrow * p.wpr;
-  const uint16_t* srow = p.scales + wrow * ngroups;
-  const int tk = tok[lr];
-
-  for (int k0 = 0; k0 < p.K; k0 += kBK) {
-    const int j0 = k0 + 8 * seg;
-    uint4 a = {0u, 0u, 0u, 0u};
-    if (tk >= 0) a = *reinterpret_cast<const uint4*>(p.xr + static_cast<int64_t>(tk) * p.K + j0);
-    *reinterpret_cast<uint4*>(&As[lr * kLdsK + 8 * seg]) = a;
-    uint32_t packed[4] = {0u, 0u, 0u, 0u};
-    if (nvalid) {
-      int idx[8];
-      decode8<L>(crow, j0, idx);
-      const float sc = half_bits_to_float(srow[j0 / p.group]);
+        for (int i = 0; i < S::words; ++i) {
+          const int wi = fw + i < p.wpr ? fw + i : p.wpr - 1;  // spans may run past the row
+          st.w[j][i] = ld_at<uint32_t>(cexp, coff[j] + wi * 4u);
+        }
+      }
 #pragma unroll
-      for (int k = 0; k < 8; k += 2) {
-        const uint32_t lo16 = float_to_bf16_rne(cent[idx[k]] * sc);
-        const uint32_t hi16 = float_to_bf16_rne(cent[idx[k + 1]] * sc);
-        packed[k >> 1] = lo16 | (hi16 << 16);
+      for (int k = 0; k < NSC; ++k) {
+        // first element of the k-th scale's fragment(s): fragment k (trits), 16 k (g16)
+        const int ek = L == 3 ? e0 + 8 * k : e0 + 16 * k;
+        int gi = ek >> p.lg_group;
+        gi = gi < p.ngk ? gi : p.ngk - 1;
+        st.s[j][k] = ld_at<uint16_t>(sexp, soff[j] + gi * 2u);
       }
     }
-    *reinterpret_cast<uint4*>(&Bs[lr * kLdsK + 8 * seg]) = uint4{packed[0], packed[1], packed[2], packed[3]};
-    __syncthreads();
+  };
+  auto fetch_a = [&](QmmStage<L, G16>& st, int step) {
+    const int k0 = step * Q::BK;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int arow = 32 * wm + 16 * i + (lane & 15);
-      const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&As[arow * kLdsK + 8 * (lane >> 4)]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int brow = 32 * wn + 16 * j + (lane & 15);
-        const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(&Bs[brow * kLdsK + 8 * (lane >> 4)]);
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[i][j], 0, 0, 0);
-      }
+    for (int j = 0; j < Q::AU; ++j) {
+      const int kc = k0 + ak[j] < p.K ? k0 : 0;
+      st.a[j] = *reinterpret_cast<const u32x4_t*>(asrc[j] + kc);
     }
-    __syncthreads();
-  }
+  };
+  auto stash_a = [&](const QmmStage<L, G16>& st, int buf, int step) {
+    const int k0 = step * Q::BK;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < Q::AU; ++j) {
+      const u32x4_t v = k0 + ak[j] < p.K ? st.a[j] : u32x4_t{0u, 0u, 0u, 0u};
+      if (aon[j]) *reinterpret_cast<u32x4_t*>(la + buf * (kQmmBM * Q::AST) + aoff[j]) = v;
+    }
+  };
+
+  f32x16_t acc[MT][2];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 32 * wm + 16 * i + 4 * (lane >> 4) + r;
-        const int col = n0 + 32 * wn + 16 * j + (lane & 15);
-        if (row < mrows && col < p.N)
-          store_any(p.y, p.ydt, static_cast<int64_t>(m0 + row) * p.N + col,
-                    tok[row] == -2 ? __builtin_nanf("") : acc[i][j][r]);
+      for (int r = 0; r < 16; ++r) acc[mt][j][r] = 0.f;
+
+  // Two stages in flight: step t's codes and inputs live in stage t % 2 and are loaded two
+  // steps ahead; step t's inputs are copied to LDS buffer t % 2 at the end of step t - 1.
+  QmmStage<L, G16> st[2];
+  fetch_a(st[0], 0);
+  load_codes(st[0], 0);
+  fetch_a(st[1], 1);
+  load_codes(st[1], 1);
+  stash_a(st[0], 0, 0);
+  fetch_a(st[0], 2);
+  __syncthreads();
+
+  auto body = [&](auto parity, int step) {
+    constexpr int P = decltype(parity)::value;
+    QmmStage<L, G16>& cur = st[P];
+    // this step's table indices and scales
+    SpanIdx<L> xi[2];
+    uint32_t s2[2][S::mf];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      span_index<L>(cur.w[j], xi[j]);
+#pragma unroll
+      for (int f = 0; f < S::mf; ++f) {
+        const int k = L == 3 ? f : (G16 ? f >> 1 : 0);
+        s2[j][f] = __umul24(static_cast<uint32_t>(cur.s[j][k]), 0x10001u);
       }
+    }
+    // Per fragment f: read its inputs from LDS, issue the table lookups of fragment f + 1,
+    // scale fragment f's entries (looked up one fragment earlier), then the matrix
+    // multiplies; the lookups of f + 1 stay in flight while the matrix cores work.
+    const _Float16* abuf = la + P * (kQmmBM * Q::AST);
+    u32x4_t raw[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) raw[j][0] = span_lookup<L>(xi[j], 0, lut, slot);
+#pragma unroll
+    for (int f = 0; f < S::mf; ++f) {
+      u32x4_t a[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        a[mt] = *reinterpret_cast<const u32x4_t*>(abuf + (32 * mt + c32) * Q::AST + g * S::elems + 8 * f);
+      if (f + 1 < S::mf) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) raw[j][(f + 1) & 1] = span_lookup<L>(xi[j], f + 1, lut, slot);
+      } else {
+        load_codes(cur, step + 2);  // the step's indices are no longer needed
+      }
+      // keep the compiler from pulling fragment f + 1's scaling (and its wait) forward
+      __builtin_amdgcn_sched_barrier(0);
+      u32x4_t b[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = scale_pairs(raw[j][f & 1], s2[j][f]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[mt][j] = mfma32_f16(a[mt], b[j], acc[mt][j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    stash_a(st[P ^ 1], P ^ 1, step + 1);
+    fetch_a(st[P ^ 1], step + 3);
+    __syncthreads();
+  };
+  for (int step = 0; step < nsteps; step += 2) {
+    body(std::integral_constant<int, 0>{}, step);
+    body(std::integral_constant<int, 1>{}, step + 1);
+  }
+
+  // D[8 (r / 4) + 4 g + r % 4][c32] of sub-tile (mt, j), times the row's input scale
+  switch (p.ydt) {
+    case 0: qmm_store<float, MT>(p, acc, m0, mrows, n0 + wave * kQmmWN + c32, g, txs); break;
+    case 1: qmm_store<__bf16, MT>(p, acc, m0, mrows, n0 + wave * kQmmWN + c32, g, txs); break;
+    default: qmm_store<_Float16, MT>(p, acc, m0, mrows, n0 + wave * kQmmWN + c32, g, txs); break;
+  }
+}
+
+template <int L, bool G16>
+__global__ __launch_bounds__(kQmmThreads) void k_gqmm(QmmParams p) {
+  using Q = QmmStep<L>;
+  // the table is the first static LDS array: it starts at address 0
+  __shared__ __attribute__((aligned(16))) uint32_t lut[mlut_bytes<L>() / 4];
+  __shared__ __attribute__((aligned(16))) _Float16 la[2 * kQmmBM * Q::AST];
+  __shared__ int32_t tok[kQmmBM];
+  __shared__ __attribute__((aligned(16))) float txs[kQmmBM];
+  __shared__ uint16_t hs[16];
+
+  // Tile order: consecutive virtual ids run on one XCD (workgroups are dealt to the 8 XCDs
+  // in turn), so the column tiles of one row tile, and the row tiles of one expert, share
+  // that XCD's L2.
+  const int total_mt = *p.count;
+  const int nt = (p.N + kQmmBN - 1) / kQmmBN;
+  const int G = total_mt * nt;
+  const int per = (G + 7) >> 3;
+  const int b = blockIdx.x;
+  if ((b >> 3) >= per) return;
+  const int v = (b & 7) * per + (b >> 3);
+  if (v >= G) return;  // uniform per workgroup
+  const int t = v / nt, ntile = v - t * nt;
+  const int4 te = p.tiles[t];
+  const int e = te.x, m0 = te.y;
+  if (e < 0 || e >= p.E || m0 < 0 || m0 >= p.M) return;  // never touch memory past y
+  int mrows = te.z;
+  mrows = mrows < p.M - m0 ? mrows : static_cast<int>(p.M - m0);
+  if (mrows <= 0) return;
+  const int n0 = ntile * kQmmBN;
+
+  if (threadIdx.x < kQmmBM) {
+    // padding rows read the zero row T; an out-of-range token reads it too and gives NaN
+    int tk = static_cast<int>(p.T);
+    float sc = 0.f;
+    if (static_cast<int>(threadIdx.x) < mrows) {
+      const int v2 = p.row_token[m0 + threadIdx.x];
+      if (v2 >= 0 && v2 < p.T) {
+        tk = v2;
+        sc = p.xs[v2];
+      } else {
+        sc = __builtin_nanf("");
+      }
+    }
+    tok[threadIdx.x] = tk;
+    txs[threadIdx.x] = sc;
+  }
+  if (threadIdx.x < 16) hs[threadIdx.x] = p.cb.h[threadIdx.x];
+  __syncthreads();
+  build_mlut<L, kQmmThreads>(lut, hs);
+  // (the first barrier inside qmm_tile orders the table writes before any lookup)
+  switch ((mrows + 31) >> 5) {
+    case 1: qmm_tile<L, 1, G16>(p, e, m0, mrows, n0, lut, la, tok, txs); break;
+    case 2: qmm_tile<L, 2, G16>(p, e, m0, mrows, n0, lut, la, tok, txs); break;
+    case 3: qmm_tile<L, 3, G16>(p, e, m0, mrows, n0, lut, la, tok, txs); break;
+    default: qmm_tile<L, 4, G16>(p, e, m0, mrows, n0, lut, la, tok, txs); break;
+  }
 }
 
 hipError_t launch_gather_qmm(const WeightArgs& w, const void* x, int xdt, int64_t T,
                              const int32_t* row_token, const int32_t* offsets, int64_t M,
                              bool x_rotated, void* y, int ydt, void* ws, hipStream_t s) {
   if (M == 0 || w.N == 0) return hipSuccess;
-  uint16_t* xr = static_cast<uint16_t*>(ws);
-  int32_t* tile_start = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
-                                                   align256(static_cast<size_t>(T) * w.K * 2));
-  hipError_t err;
-  if (!x_rotated) {
-    err = launch_fwht(x, xdt, T, w.K, w.m, w.P, w.signs, 0, xr, 1, s);
-  } else if (xdt == 1) {
-    xr = const_cast<uint16_t*>(static_cast<const uint16_t*>(x));
-    err = hipSuccess;
-  } else {
-    const int64_t n = T * w.K;
-    const int grid = static_cast<int>((n + kBlock - 1) / kBlock < 65536 ? (n + kBlock - 1) / kBlock : 65536);
-    hipLaunchKernelGGL(k_to_bf16, dim3(grid > 0 ? grid : 1), dim3(kBlock), 0, s, x, xdt, n, xr);
-    err = hipGetLastError();
-  }
+  if (w.E > kMaxExpertsQmm) return hipErrorInvalidValue;
+  // one expert's codes and scales are addressed with 32-bit byte offsets
+  if (static_cast<uint64_t>(w.N) * w.wpr * 4 > 0xffffffffull) return hipErrorInvalidValue;
+  const QmmLayout lay = qmm_layout(w, M, T);
+  char* base = static_cast<char*>(ws);
+  _Float16* xh = reinterpret_cast<_Float16*>(base + lay.rows);
+  float* xs = reinterpret_cast<float*>(base + lay.scale);
+  int32_t* count = reinterpret_cast<int32_t*>(base + lay.count);
+  int4* tiles = reinterpret_cast<int4*>(base + lay.tiles);
+
+  hipError_t err = launch_rot16(x, xdt, nullptr, T, /*zero_rows=*/1, w, x_rotated, xh, xs, s);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_schedule, dim3(1), dim3(64), 0, s, offsets, w.E, tile_start);
+  hipLaunchKernelGGL(k_schedule, dim3(1), dim3(kSchedThreads), 0, s, offsets, w.E, M, count, tiles);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
+
   QmmParams p{};
-  p.codes = w.codes; p.scales = w.scales; p.xr = xr; p.row_token = row_token;
-  p.offsets = offsets; p.tile_start = tile_start; p.y = y;
-  p.K = w.K; p.N = w.N; p.E = w.E; p.wpr = w.wpr; p.group = w.group; p.ydt = ydt;
+  p.codes = w.codes; p.scales = w.scales; p.xh = xh; p.xs = xs; p.row_token = row_token;
+  p.count = count; p.tiles = tiles; p.y = y;
   p.T = T; p.M = M;
+  p.K = w.K; p.N = w.N; p.E = w.E; p.wpr = w.wpr; p.ydt = ydt;
+  p.ngk = w.K / w.group;
+  p.lg_group = __builtin_ctz(w.group);
   p.cb = *codebook_for(w.levels);
-  const int gx = static_cast<int>((M + kBM - 1) / kBM + w.E);
-  const int gy = (w.N + kBN - 1) / kBN;
+  // enough workgroups for any schedule, rounded up to a multiple of 8 for the XCD-major order
+  const int64_t nt = (w.N + kQmmBN - 1) / kQmmBN;
+  const int64_t gx = (max_tiles(M, w.E) * nt + 7) / 8 * 8;
+  if (gx > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(gx));
+  const bool g16 = w.group == 16;
+  const dim3 blk(kQmmThreads);
   switch (w.levels) {
-    case 16: hipLaunchKernelGGL(k_gqmm<16>, dim3(gx, gy), dim3(kBlock), 0, s, p); break;
-    case 8: hipLaunchKernelGGL(k_gqmm<8>, dim3(gx, gy), dim3(kBlock), 0, s, p); break;
-    case 4: hipLaunchKernelGGL(k_gqmm<4>, dim3(gx, gy), dim3(kBlock), 0, s, p); break;
-    default: hipLaunchKernelGGL(k_gqmm<3>, dim3(gx, gy), dim3(kBlock), 0, s, p); break;
+    case 16:
+      if (g16) hipLaunchKernelGGL((k_gqmm<16, true>), grid, blk, 0, s, p);
+      else hipLaunchKernelGGL((k_gqmm<16, false>), grid, blk, 0, s, p);
+      break;
+    case 8:
+      if (g16) hipLaunchKernelGGL((k_gqmm<8, true>), grid, blk, 0, s, p);
+      else hipLaunchKernelGGL((k_gqmm<8, false>), grid, blk, 0, s, p);
+      break;
+    case 4:
+      if (g16) hipLaunchKernelGGL((k_gqmm<4, true>), grid, blk, 0, s, p);
+      else hipLaunchKernelGGL((k_gqmm<4, false>), grid, blk, 0, s, p);
+      break;
+    default: hipLaunchKernelGGL((k_gqmm<3, false>), grid, blk, 0, s, p); break;
   }
   return hipGetLastError();
 }

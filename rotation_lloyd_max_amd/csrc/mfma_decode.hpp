@@ -123,72 +123,94 @@ __device__ __forceinline__ uint32_t pk_mul_h(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, a) * __builtin_bit_cast(half2_t, b));
 }
 
-// B fragments of one span: for each of the MF instructions, 8 fp16 weights (4 pairs) of
-// the lane's row, already multiplied by their scale; s2[f] is fragment f's fp16 scale in
-// both halves.
+// Table indices of one span: the code words themselves for the bit formats, the ten base-81
+// digits for trits (computed once per span and shared by its five fragments).
+template <int L>
+struct SpanIdx {
+  uint32_t v[L == 3 ? 10 : Span<L>::words];
+};
+
+template <int L>
+__device__ __forceinline__ void span_index(const uint32_t (&w)[Span<L>::words], SpanIdx<L>& x) {
+  if constexpr (L == 3) {
+    uint32_t q[5];
+    trit_digits81(w[0], q);
+#pragma unroll
+    for (int k = 0; k < 5; ++k) x.v[k] = q[k];
+    trit_digits81(w[1], q);
+#pragma unroll
+    for (int k = 0; k < 5; ++k) x.v[5 + k] = q[k];
+  } else {
+#pragma unroll
+    for (int i = 0; i < Span<L>::words; ++i) x.v[i] = w[i];
+  }
+}
+
+// Table entries of fragment f of a span: 8 fp16 centroids (4 pairs) of the lane's row, not
+// yet scaled. f must be a compile-time constant after unrolling.
+template <int L>
+__device__ __forceinline__ u32x4_t span_lookup(const SpanIdx<L>& x, int f, const uint32_t* lut,
+                                               uint32_t slot) {
+  u32x4_t b;
+  if constexpr (L == 16) {
+    b[0] = lds_u32(lut, byte_addr<0>(x.v[f], slot));
+    b[1] = lds_u32(lut, byte_addr<1>(x.v[f], slot));
+    b[2] = lds_u32(lut, byte_addr<2>(x.v[f], slot));
+    b[3] = lds_u32(lut, byte_addr<3>(x.v[f], slot));
+  } else if constexpr (L == 8) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int bit = 24 * f + 6 * j, lo = bit >> 5, sh = bit & 31;
+      uint32_t fld;
+      if (sh <= 26) fld = __builtin_amdgcn_ubfe(x.v[lo], sh, 6);
+      else fld = __builtin_amdgcn_alignbit(x.v[lo + 1], x.v[lo], sh) & 63u;
+      b[j] = lds_u32(lut, (fld << 8) | slot);
+    }
+  } else if constexpr (L == 4) {
+    const uint32_t wf = x.v[f >> 1];
+    uint2 e0, e1;
+    if (f & 1) {
+      e0 = lds_u64(lut, byte_addr<2>(wf, slot));
+      e1 = lds_u64(lut, byte_addr<3>(wf, slot));
+    } else {
+      e0 = lds_u64(lut, byte_addr<0>(wf, slot));
+      e1 = lds_u64(lut, byte_addr<1>(wf, slot));
+    }
+    b[0] = e0.x; b[1] = e0.y; b[2] = e1.x; b[3] = e1.y;
+  } else {
+    const uint2 e0 = lds_u64(lut, (x.v[2 * f] << 8) | slot);
+    const uint2 e1 = lds_u64(lut, (x.v[2 * f + 1] << 8) | slot);
+    b[0] = e0.x; b[1] = e0.y; b[2] = e1.x; b[3] = e1.y;
+  }
+  return b;
+}
+
+// Pairs times the fragment's fp16 scale s2 (the scale in both halves).
+__device__ __forceinline__ u32x4_t scale_pairs(const u32x4_t& r, uint32_t s2) {
+  u32x4_t b;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) b[k] = pk_mul_h(r[k], s2);
+  return b;
+}
+
+// B fragment f of a span: 8 fp16 weights (4 pairs) of the lane's row, multiplied by their
+// scale s2.
+template <int L>
+__device__ __forceinline__ u32x4_t span_fragment(const SpanIdx<L>& x, int f, const uint32_t* lut,
+                                                 uint32_t slot, uint32_t s2) {
+  return scale_pairs(span_lookup<L>(x, f, lut, slot), s2);
+}
+
+// All MF fragments of one span; s2[f] is fragment f's fp16 scale in both halves.
 template <int L>
 __device__ __forceinline__ void span_fragments(const uint32_t (&w)[Span<L>::words],
                                                const uint32_t* lut, uint32_t slot,
                                                const uint32_t (&s2)[Span<L>::mf],
                                                u32x4_t (&b)[Span<L>::mf]) {
-  if constexpr (L == 16) {
+  SpanIdx<L> x;
+  span_index<L>(w, x);
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      b[f][0] = pk_mul_h(lds_u32(lut, byte_addr<0>(w[f], slot)), s2[f]);
-      b[f][1] = pk_mul_h(lds_u32(lut, byte_addr<1>(w[f], slot)), s2[f]);
-      b[f][2] = pk_mul_h(lds_u32(lut, byte_addr<2>(w[f], slot)), s2[f]);
-      b[f][3] = pk_mul_h(lds_u32(lut, byte_addr<3>(w[f], slot)), s2[f]);
-    }
-  } else if constexpr (L == 8) {
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int bit = 24 * f + 6 * j, lo = bit >> 5, sh = bit & 31;
-        uint32_t fld;
-        if (sh <= 26) fld = __builtin_amdgcn_ubfe(w[lo], sh, 6);
-        else fld = __builtin_amdgcn_alignbit(w[lo + 1], w[lo], sh) & 63u;
-        b[f][j] = pk_mul_h(lds_u32(lut, (fld << 8) | slot), s2[f]);
-      }
-    }
-  } else if constexpr (L == 4) {
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const uint32_t wf = w[f >> 1];
-      uint2 e0, e1;
-      if (f & 1) {
-        e0 = lds_u64(lut, byte_addr<2>(wf, slot));
-        e1 = lds_u64(lut, byte_addr<3>(wf, slot));
-      } else {
-        e0 = lds_u64(lut, byte_addr<0>(wf, slot));
-        e1 = lds_u64(lut, byte_addr<1>(wf, slot));
-      }
-      b[f][0] = pk_mul_h(e0.x, s2[f]);
-      b[f][1] = pk_mul_h(e0.y, s2[f]);
-      b[f][2] = pk_mul_h(e1.x, s2[f]);
-      b[f][3] = pk_mul_h(e1.y, s2[f]);
-    }
-  } else {
-    uint32_t d[10];
-    {
-      uint32_t q[5];
-      trit_digits81(w[0], q);
-#pragma unroll
-      for (int k = 0; k < 5; ++k) d[k] = q[k];
-      trit_digits81(w[1], q);
-#pragma unroll
-      for (int k = 0; k < 5; ++k) d[5 + k] = q[k];
-    }
-#pragma unroll
-    for (int f = 0; f < 5; ++f) {
-      const uint2 e0 = lds_u64(lut, (d[2 * f] << 8) | slot);
-      const uint2 e1 = lds_u64(lut, (d[2 * f + 1] << 8) | slot);
-      b[f][0] = pk_mul_h(e0.x, s2[f]);
-      b[f][1] = pk_mul_h(e0.y, s2[f]);
-      b[f][2] = pk_mul_h(e1.x, s2[f]);
-      b[f][3] = pk_mul_h(e1.y, s2[f]);
-    }
-  }
+  for (int f = 0; f < Span<L>::mf; ++f) b[f] = span_fragment<L>(x, f, lut, slot, s2[f]);
 }
 
 __device__ __forceinline__ f32x4_t mfma_f16(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
