@@ -152,8 +152,10 @@ int tq_multi_gather_qmv(const tq_qweight *w, const int32_t *ids, int64_t P, cons
  * table, third row): for offsets[e] <= m < offsets[e+1], y[m] = W_e R x[row_token[m]].
  * x device [T][K]; row_token device int32 [M]; expert_offsets device int32 [E+1],
  * non-decreasing, offsets[0] = 0, offsets[E] = M; y device [M][N] in sorted-row order.
- * Rows are multiplied with bf16 MFMA (weights decoded to bf16, inputs rotated to bf16),
- * accumulated in fp32. Workspace: tq_workspace_bytes. */
+ * Inputs are rotated once into fp16 rows (each scaled by a power of two), weights are
+ * decoded to fp16 (centroid times group scale) and multiplied on the matrix cores with fp32
+ * accumulation. A row_token outside [0, T) yields a row of NaN. Workspace:
+ * tq_workspace_bytes (it depends on M, T and E). */
 int tq_gather_qmm(const tq_qweight *w, const void *x, tq_dtype x_dtype, int64_t T,
                   const int32_t *row_token, const int32_t *expert_offsets, int64_t M, void *y,
                   tq_dtype y_dtype, uint32_t flags, void *ws, size_t ws_bytes, void *stream);
