@@ -33,7 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_16BIT_PEAK_TFLOPS = 2500.0
 
 
 def parse():
@@ -351,8 +351,8 @@ def bench_moe(args):
     ms_per_step = e0.elapsed_time(e1) / nsteps
     if args.config == 5:
         value = flops_step / (ms_per_step / 1e3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(value, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+        roof = {"bound": "mfma", "achieved": round(value, 3), "peak": MFMA_16BIT_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(value / MFMA_16BIT_PEAK_TFLOPS, 4), "traffic": None}
     else:
         value = bytes_step / (ms_per_step / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(value, 3), "peak": HBM_PEAK_GBS,

@@ -33,6 +33,8 @@ constexpr int kQmmThreads = 64 * kQmmWaves;
 constexpr int kQmmBM = 128;                      // rows per tile: 4 sub-tiles of 32
 constexpr int kQmmWN = 64;                       // output columns per wave: 2 tiles of 32
 constexpr int kQmmBN = kQmmWN * kQmmWaves;       // output columns per workgroup
+// Scales of a tile's rows are staged in LDS when a row has at most this many groups.
+constexpr int kQmmMaxLdsGroups = 32;
 
 template <int L>
 struct QmmStep {
@@ -182,10 +184,10 @@ __device__ __forceinline__ void qmm_store(const QmmParams& p, const f32x16_t (&a
   }
 }
 
-template <int L, int MT, bool G16>
+template <int L, int MT, bool G16, bool SL>
 __device__ __forceinline__ void qmm_tile(const QmmParams& p, int e, int m0, int mrows, int n0,
                                          const uint32_t* lut, _Float16* la, const int32_t* tok,
-                                         const float* txs) {
+                                         const float* txs, uint16_t* ls) {
   using S = Span<L>;
   using Q = QmmStep<L>;
   constexpr int NSC = span_scales<L, G16>();
@@ -198,12 +200,23 @@ __device__ __forceinline__ void qmm_tile(const QmmParams& p, int e, int m0, int 
   const uint32_t* cexp = p.codes + static_cast<int64_t>(e) * p.N * p.wpr;
   const uint16_t* sexp = p.scales + static_cast<int64_t>(e) * p.N * p.ngk;
   uint32_t coff[2], soff[2];
+  const int sst = p.ngk + 1;  // LDS halves per row of staged scales (odd: no bank conflicts)
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     int n = n0 + wave * kQmmWN + 32 * j + c32;
     n = n < p.N ? n : p.N - 1;
     coff[j] = static_cast<uint32_t>(n) * p.wpr * 4u;
-    soff[j] = static_cast<uint32_t>(n) * p.ngk * 2u;
+    soff[j] = SL ? static_cast<uint32_t>((n - n0) * sst) : static_cast<uint32_t>(n) * p.ngk * 2u;
+  }
+  if constexpr (SL) {
+    // the tile's rows' scales are one contiguous block: copy it once with coalesced loads
+    const int rows = p.N - n0 < kQmmBN ? p.N - n0 : kQmmBN;
+    const int total = rows * p.ngk;
+    const uint16_t* src = sexp + static_cast<int64_t>(n0) * p.ngk;
+    for (int i = threadIdx.x; i < total; i += kQmmThreads) {
+      const int r = i / p.ngk;
+      ls[r * sst + (i - r * p.ngk)] = src[i];
+    }
   }
   // this thread's 16-byte units of the input tile (a unit past the tile, which only the
   // trit format has, loads the tile's first unit and is not stored)
@@ -246,13 +259,15 @@ __device__ __forceinline__ void qmm_tile(const QmmParams& p, int e, int m0, int 
           st.w[j][i] = ld_at<uint32_t>(cexp, coff[j] + wi * 4u);
         }
       }
+      if constexpr (!SL) {
 #pragma unroll
-      for (int k = 0; k < NSC; ++k) {
-        // first element of the k-th scale's fragment(s): fragment k (trits), 16 k (g16)
-        const int ek = L == 3 ? e0 + 8 * k : e0 + 16 * k;
-        int gi = ek >> p.lg_group;
-        gi = gi < p.ngk ? gi : p.ngk - 1;
-        st.s[j][k] = ld_at<uint16_t>(sexp, soff[j] + gi * 2u);
+        for (int k = 0; k < NSC; ++k) {
+          // first element of the k-th scale's fragment(s): fragment k (trits), 16 k (g16)
+          const int ek = L == 3 ? e0 + 8 * k : e0 + 16 * k;
+          int gi = ek >> p.lg_group;
+          gi = gi < p.ngk ? gi : p.ngk - 1;
+          st.s[j][k] = ld_at<uint16_t>(sexp, soff[j] + gi * 2u);
+        }
       }
     }
   };
@@ -292,51 +307,76 @@ __device__ __forceinline__ void qmm_tile(const QmmParams& p, int e, int m0, int 
   fetch_a(st[0], 2);
   __syncthreads();
 
+  // Table lookups run LA fragments ahead of the multiplies that use them, across step
+  // boundaries: slot f of `raw` holds fragment f of the current step, refilled with fragment
+  // f of the next step once consumed. Deeper look-ahead where registers allow it.
+  constexpr int MF = S::mf;
+  constexpr int LA = SL ? 2 : 1;
+  SpanIdx<L> xc[2], xn[2];  // table indices of this step and of the next one
+  u32x4_t raw[MF][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    span_index<L>(st[0].w[j], xc[j]);
+#pragma unroll
+    for (int q = 0; q < LA; ++q) raw[q][j] = span_lookup<L>(xc[j], q, lut, slot);
+  }
+
   auto body = [&](auto parity, int step) {
     constexpr int P = decltype(parity)::value;
     QmmStage<L, G16>& cur = st[P];
-    // this step's table indices and scales
-    SpanIdx<L> xi[2];
-    uint32_t s2[2][S::mf];
+    uint32_t s2[2][MF];
+    const int e0 = (step < last ? step : last) * Q::BK + g * S::elems;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      span_index<L>(cur.w[j], xi[j]);
 #pragma unroll
-      for (int f = 0; f < S::mf; ++f) {
+      for (int f = 0; f < MF; ++f) {
         const int k = L == 3 ? f : (G16 ? f >> 1 : 0);
-        s2[j][f] = __umul24(static_cast<uint32_t>(cur.s[j][k]), 0x10001u);
+        uint32_t sv;
+        if constexpr (SL) {
+          const int ek = L == 3 ? e0 + 8 * k : e0 + 16 * k;
+          int gi = ek >> p.lg_group;
+          gi = gi < p.ngk ? gi : p.ngk - 1;
+          sv = ls[soff[j] + gi];
+        } else {
+          sv = cur.s[j][k];
+        }
+        s2[j][f] = __umul24(sv, 0x10001u);
       }
     }
-    // Per fragment f: read its inputs from LDS, issue the table lookups of fragment f + 1,
-    // scale fragment f's entries (looked up one fragment earlier), then the matrix
-    // multiplies; the lookups of f + 1 stay in flight while the matrix cores work.
+    // Per fragment f: read its inputs from LDS, issue the lookups of fragment f + LA (of
+    // this step or the next), scale fragment f's entries, then the matrix multiplies.
     const _Float16* abuf = la + P * (kQmmBM * Q::AST);
-    u32x4_t raw[2][2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) raw[j][0] = span_lookup<L>(xi[j], 0, lut, slot);
-#pragma unroll
-    for (int f = 0; f < S::mf; ++f) {
+    for (int f = 0; f < MF; ++f) {
       u32x4_t a[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
         a[mt] = *reinterpret_cast<const u32x4_t*>(abuf + (32 * mt + c32) * Q::AST + g * S::elems + 8 * f);
-      if (f + 1 < S::mf) {
+      const int q = f + LA;
+      if (q < MF) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) raw[j][(f + 1) & 1] = span_lookup<L>(xi[j], f + 1, lut, slot);
+        for (int j = 0; j < 2; ++j) raw[q][j] = span_lookup<L>(xc[j], q, lut, slot);
       } else {
-        load_codes(cur, step + 2);  // the step's indices are no longer needed
+        if (q == MF) {
+          // the next step's codes (loaded two steps ago) become table indices
+#pragma unroll
+          for (int j = 0; j < 2; ++j) span_index<L>(st[P ^ 1].w[j], xn[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) raw[q - MF][j] = span_lookup<L>(xn[j], q - MF, lut, slot);
       }
-      // keep the compiler from pulling fragment f + 1's scaling (and its wait) forward
-      __builtin_amdgcn_sched_barrier(0);
       u32x4_t b[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = scale_pairs(raw[j][f & 1], s2[j][f]);
+      for (int j = 0; j < 2; ++j) b[j] = scale_pairs(raw[f][j], s2[j][f]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[mt][j] = mfma32_f16(a[mt], b[j], acc[mt][j]);
-      __builtin_amdgcn_sched_barrier(0);
     }
+    // this step's indices are consumed: its code registers take step + 2
+    load_codes(cur, step + 2);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) xc[j] = xn[j];
     stash_a(st[P ^ 1], P ^ 1, step + 1);
     fetch_a(st[P ^ 1], step + 3);
     __syncthreads();
@@ -354,7 +394,7 @@ __device__ __forceinline__ void qmm_tile(const QmmParams& p, int e, int m0, int 
   }
 }
 
-template <int L, bool G16>
+template <int L, bool G16, bool SL>
 __global__ __launch_bounds__(kQmmThreads) void k_gqmm(QmmParams p) {
   using Q = QmmStep<L>;
   // the table is the first static LDS array: it starts at address 0
@@ -363,6 +403,7 @@ __global__ __launch_bounds__(kQmmThreads) void k_gqmm(QmmParams p) {
   __shared__ int32_t tok[kQmmBM];
   __shared__ __attribute__((aligned(16))) float txs[kQmmBM];
   __shared__ uint16_t hs[16];
+  __shared__ uint16_t ls[SL ? kQmmBN * (kQmmMaxLdsGroups + 1) : 1];
 
   // Tile order: consecutive virtual ids run on one XCD (workgroups are dealt to the 8 XCDs
   // in turn), so the column tiles of one row tile, and the row tiles of one expert, share
@@ -405,10 +446,10 @@ __global__ __launch_bounds__(kQmmThreads) void k_gqmm(QmmParams p) {
   build_mlut<L, kQmmThreads>(lut, hs);
   // (the first barrier inside qmm_tile orders the table writes before any lookup)
   switch ((mrows + 31) >> 5) {
-    case 1: qmm_tile<L, 1, G16>(p, e, m0, mrows, n0, lut, la, tok, txs); break;
-    case 2: qmm_tile<L, 2, G16>(p, e, m0, mrows, n0, lut, la, tok, txs); break;
-    case 3: qmm_tile<L, 3, G16>(p, e, m0, mrows, n0, lut, la, tok, txs); break;
-    default: qmm_tile<L, 4, G16>(p, e, m0, mrows, n0, lut, la, tok, txs); break;
+    case 1: qmm_tile<L, 1, G16, SL>(p, e, m0, mrows, n0, lut, la, tok, txs, ls); break;
+    case 2: qmm_tile<L, 2, G16, SL>(p, e, m0, mrows, n0, lut, la, tok, txs, ls); break;
+    case 3: qmm_tile<L, 3, G16, SL>(p, e, m0, mrows, n0, lut, la, tok, txs, ls); break;
+    default: qmm_tile<L, 4, G16, SL>(p, e, m0, mrows, n0, lut, la, tok, txs, ls); break;
   }
 }
 
@@ -446,21 +487,29 @@ hipError_t launch_gather_qmm(const WeightArgs& w, const void* x, int xdt, int64_
   if (gx > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(gx));
   const bool g16 = w.group == 16;
+  // scales staged in LDS per tile when a row has few enough groups (never with groups of 16)
+  const bool sl = !g16 && p.ngk <= kQmmMaxLdsGroups;
   const dim3 blk(kQmmThreads);
   switch (w.levels) {
     case 16:
-      if (g16) hipLaunchKernelGGL((k_gqmm<16, true>), grid, blk, 0, s, p);
-      else hipLaunchKernelGGL((k_gqmm<16, false>), grid, blk, 0, s, p);
+      if (g16) hipLaunchKernelGGL((k_gqmm<16, true, false>), grid, blk, 0, s, p);
+      else if (sl) hipLaunchKernelGGL((k_gqmm<16, false, true>), grid, blk, 0, s, p);
+      else hipLaunchKernelGGL((k_gqmm<16, false, false>), grid, blk, 0, s, p);
       break;
     case 8:
-      if (g16) hipLaunchKernelGGL((k_gqmm<8, true>), grid, blk, 0, s, p);
-      else hipLaunchKernelGGL((k_gqmm<8, false>), grid, blk, 0, s, p);
+      if (g16) hipLaunchKernelGGL((k_gqmm<8, true, false>), grid, blk, 0, s, p);
+      else if (sl) hipLaunchKernelGGL((k_gqmm<8, false, true>), grid, blk, 0, s, p);
+      else hipLaunchKernelGGL((k_gqmm<8, false, false>), grid, blk, 0, s, p);
       break;
     case 4:
-      if (g16) hipLaunchKernelGGL((k_gqmm<4, true>), grid, blk, 0, s, p);
-      else hipLaunchKernelGGL((k_gqmm<4, false>), grid, blk, 0, s, p);
+      if (g16) hipLaunchKernelGGL((k_gqmm<4, true, false>), grid, blk, 0, s, p);
+      else if (sl) hipLaunchKernelGGL((k_gqmm<4, false, true>), grid, blk, 0, s, p);
+      else hipLaunchKernelGGL((k_gqmm<4, false, false>), grid, blk, 0, s, p);
       break;
-    default: hipLaunchKernelGGL((k_gqmm<3, false>), grid, blk, 0, s, p); break;
+    default:
+      if (sl) hipLaunchKernelGGL((k_gqmm<3, false, true>), grid, blk, 0, s, p);
+      else hipLaunchKernelGGL((k_gqmm<3, false, false>), grid, blk, 0, s, p);
+      break;
   }
   return hipGetLastError();
 }
