@@ -76,35 +76,54 @@ constexpr int kSchedThreads = 1024;
 
 // The tile table: expert e's rows offsets[e] .. offsets[e+1] - 1 are cut into tiles of
 // 128; tiles are listed expert by expert. Experts with no rows (or inconsistent offsets)
-// get no tile; the table never holds more than max_tiles entries.
+// get no tile; the table never holds more than max_tiles entries. Each thread takes a
+// block of consecutive experts; a block-wide scan of the per-thread tile counts gives
+// every expert its first table index.
 __global__ __launch_bounds__(kSchedThreads) void k_schedule(const int32_t* offsets, int E,
                                                            int64_t M, int32_t* count,
                                                            int4* tiles) {
-  __shared__ int32_t start[kMaxExpertsQmm + 1];
-  for (int e = threadIdx.x; e < E; e += kSchedThreads) {
-    const int rows = offsets[e + 1] - offsets[e];
-    start[e + 1] = rows > 0 ? (rows + kQmmBM - 1) / kQmmBM : 0;
+  constexpr int PER = (kMaxExpertsQmm + kSchedThreads - 1) / kSchedThreads;
+  __shared__ int32_t wsum[kSchedThreads / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e0 = threadIdx.x * PER;
+  int n[PER];
+  int local = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int e = e0 + k;
+    int rows = e < E ? offsets[e + 1] - offsets[e] : 0;
+    n[k] = rows > 0 ? (rows + kQmmBM - 1) / kQmmBM : 0;
+    local += n[k];
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int64_t cap = max_tiles_dev(M, E);
-    int acc = 0;
-    start[0] = 0;
-    for (int e = 0; e < E; ++e) {
-      int n = start[e + 1];
-      n = acc + n <= cap ? n : static_cast<int>(cap - acc);
-      acc += n;
-      start[e + 1] = acc;
-    }
-    *count = acc;
+  // inclusive scan within the wave, then across the waves
+  int v = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(v, off, 64);
+    if (lane >= off) v += t;
   }
+  if (lane == 63) wsum[wave] = v;
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kSchedThreads) {
-    const int o0 = offsets[e], o1 = offsets[e + 1];
-    for (int k = start[e]; k < start[e + 1]; ++k) {
-      const int m0 = o0 + (k - start[e]) * kQmmBM;
-      const int rows = o1 - m0 < kQmmBM ? o1 - m0 : kQmmBM;
-      tiles[k] = make_int4(e, m0, rows, 0);
+  int before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kSchedThreads / 64; ++w) {
+    const int x = wsum[w];
+    before += w < wave ? x : 0;
+    total += x;
+  }
+  const int64_t cap = max_tiles_dev(M, E);
+  int idx = before + v - local;  // first table index of this thread's experts
+  if (threadIdx.x == 0) *count = static_cast<int>(total < cap ? total : cap);
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int e = e0 + k;
+    if (n[k] > 0) {
+      const int o0 = offsets[e], o1 = offsets[e + 1];
+      for (int t = 0; t < n[k]; ++t, ++idx) {
+        if (idx >= cap) break;
+        const int m0 = o0 + t * kQmmBM;
+        tiles[idx] = make_int4(e, m0, o1 - m0 < kQmmBM ? o1 - m0 : kQmmBM, 0);
+      }
     }
   }
 }
