@@ -224,17 +224,4 @@ __device__ __forceinline__ void store_any(void* p, int dt, int64_t i, float v) {
   else static_cast<uint16_t*>(p)[i] = float_to_half_rne(v);
 }
 
-// Block-wide max of non-negative floats; `red` is LDS scratch of at least 32 floats.
-__device__ __forceinline__ float block_max(float v, float* red) {
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float m = red[0];
-  for (int w = 1; w < (int)(kBlock >> 6); ++w) m = fmaxf(m, red[w]);
-  __syncthreads();
-  return m;
-}
-
 }  // namespace tq

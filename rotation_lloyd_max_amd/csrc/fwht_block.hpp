@@ -124,23 +124,10 @@ __device__ __forceinline__ void sylvester_from16(T* buf, int total, int lp, Half
 template <int M, int A, int C>
 inline constexpr int kHad = hadamard_entry(M, A, C);
 
-constexpr int conference14(int r, int c) {
-  return r == c ? 0 : (r == 0 || c == 0) ? 1 : qchar((r - 1) - (c - 1), 13);
-}
-template <int R, int C>
-inline constexpr int kConf = conference14(R, C);
-
 template <typename T, int M, int A, int... C>
 __device__ __forceinline__ T hadamard_row(const T (&x)[M], std::integer_sequence<int, C...>) {
   T acc = 0;
   ((acc = (kHad<M, A, C> > 0) ? acc + x[C] : acc - x[C]), ...);
-  return acc;
-}
-
-template <typename T, int R, int... C>
-__device__ __forceinline__ T conference_row(const T (&u)[14], std::integer_sequence<int, C...>) {
-  T acc = 0;
-  ((acc = kConf<R, C> == 0 ? acc : (kConf<R, C> > 0 ? acc + u[C] : acc - u[C])), ...);
   return acc;
 }
 

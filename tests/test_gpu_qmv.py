@@ -279,3 +279,30 @@ def test_gather_qmm_edges():
     ok = np.ones(offsets[-1], bool)
     ok[7] = False
     assert np.allclose(as_f64(y2)[ok], yg[ok], rtol=0, atol=2e-2 * np.abs(yg[ok]).max())
+
+
+def test_gather_qmm_many_experts():
+    # more experts than the schedule kernel's threads hold one by one (blocks of experts per
+    # thread), most of them empty, an expert whose rows span several 128-row tiles, and a
+    # column count that leaves the last 512-column tile partial
+    K, N, levels, group = 256, 600, 16, 64
+    E = 1500
+    g = wl.rng(921, 1)
+    codes = torch.from_numpy(g.integers(0, 2**31 - 1, (E, N, K // 8), dtype=np.int64).astype(np.int32)).cuda()
+    scales = torch.from_numpy((g.random((E, N, K // group)) * 0.02 + 0.005).astype(np.float16)).cuda()
+    qw = tq.QWeight(codes, scales, tq.signs(0, K, torch.device("cuda")), levels, group, K, N, E, 0)
+    counts = np.zeros(E, np.int64)
+    counts[[3, 700, 1024, 1025, 1499]] = [5, 300, 1, 17, 2]
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    T = 50
+    row_token = g.integers(0, T, offsets[-1]).astype(np.int32)
+    X = to_dev(wl.gaussian(wl.rng(921, 2), T, K), torch.bfloat16)
+    y = tq.gather_qmm(qw, X, torch.from_numpy(row_token).cuda(), torch.from_numpy(offsets).cuda())
+    torch.cuda.synchronize()
+    cs, ss = gpu_arrays(qw)
+    Xf = as_f64(X)
+    yg = as_f64(y)
+    for e in np.nonzero(counts)[0]:
+        a, b = offsets[e], offsets[e + 1]
+        want, bound = qmv_reference(cs[e], ss[e], levels, group, K, 0, Xf[row_token[a:b]])
+        check_outputs(yg[a:b], want, bound, f"expert {e}")
