@@ -86,44 +86,33 @@ __device__ __forceinline__ uint32_t byte_addr(uint32_t w, uint32_t slot) {
   return __builtin_amdgcn_perm(w, slot, 0x0c0c0000u | ((4u + K) << 8));
 }
 
-// Pair products of one chunk against the lane's rotated input pairs xp: pairs before pb
-// accumulate into a0 and the rest into a1 (pb = np when the chunk lies in one group).
-template <int L, bool SPLIT>
-__device__ __forceinline__ void chunk_dot_v(const uint32_t (&w)[Fmt<L>::cw], const uint32_t* lut,
-                                            uint32_t slot, const uint32_t (&xp)[Fmt<L>::np],
-                                            int pb, float& a0, float& a1) {
+// Table entries of one chunk: np fp16 centroid pairs, pair p = elements 2p, 2p + 1.
+template <int L>
+__device__ __forceinline__ void chunk_lookup(const uint32_t (&w)[Fmt<L>::cw], const uint32_t* lut,
+                                             uint32_t slot, uint32_t (&cw)[Fmt<L>::np]) {
   if constexpr (L == 16) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint32_t cw[4];
-      cw[0] = lds_u32(lut, byte_addr<0>(w[i], slot));
-      cw[1] = lds_u32(lut, byte_addr<1>(w[i], slot));
-      cw[2] = lds_u32(lut, byte_addr<2>(w[i], slot));
-      cw[3] = lds_u32(lut, byte_addr<3>(w[i], slot));
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        // with groups of 16 the chunk's first two words belong to the first group
-        if (SPLIT && i >= 2) a1 = dot2_h(cw[k], xp[4 * i + k], a1);
-        else a0 = dot2_h(cw[k], xp[4 * i + k], a0);
-      }
+      cw[4 * i + 0] = lds_u32(lut, byte_addr<0>(w[i], slot));
+      cw[4 * i + 1] = lds_u32(lut, byte_addr<1>(w[i], slot));
+      cw[4 * i + 2] = lds_u32(lut, byte_addr<2>(w[i], slot));
+      cw[4 * i + 3] = lds_u32(lut, byte_addr<3>(w[i], slot));
     }
   } else if constexpr (L == 4) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      uint2 cw[4];
-      cw[0] = lds_u64(lut, byte_addr<0>(w[i], slot));
-      cw[1] = lds_u64(lut, byte_addr<1>(w[i], slot));
-      cw[2] = lds_u64(lut, byte_addr<2>(w[i], slot));
-      cw[3] = lds_u64(lut, byte_addr<3>(w[i], slot));
+      uint2 e[4];
+      e[0] = lds_u64(lut, byte_addr<0>(w[i], slot));
+      e[1] = lds_u64(lut, byte_addr<1>(w[i], slot));
+      e[2] = lds_u64(lut, byte_addr<2>(w[i], slot));
+      e[3] = lds_u64(lut, byte_addr<3>(w[i], slot));
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        float& a = (SPLIT && i >= 1) ? a1 : a0;
-        a = dot2_h(cw[k].x, xp[8 * i + 2 * k], a);
-        a = dot2_h(cw[k].y, xp[8 * i + 2 * k + 1], a);
+        cw[8 * i + 2 * k] = e[k].x;
+        cw[8 * i + 2 * k + 1] = e[k].y;
       }
     }
   } else if constexpr (L == 8) {
-    uint32_t cw[16];
 #pragma unroll
     for (int p = 0; p < 16; ++p) {
       const int bit = 6 * p, lo = bit >> 5, sh = bit & 31;
@@ -132,16 +121,10 @@ __device__ __forceinline__ void chunk_dot_v(const uint32_t (&w)[Fmt<L>::cw], con
       else f = __builtin_amdgcn_alignbit(w[lo + 1], w[lo], sh) & 63u;
       cw[p] = lds_u32(lut, (f << 8) | slot);
     }
-#pragma unroll
-    for (int p = 0; p < 16; ++p) {
-      if (SPLIT && p >= 8) a1 = dot2_h(cw[p], xp[p], a1);
-      else a0 = dot2_h(cw[p], xp[p], a0);
-    }
   } else {
     // twenty base-3 digits, least significant first; pair p = digits 2p, 2p + 1 is the
     // base-9 digit p of the word
     uint32_t v = w[0];
-    uint32_t cw[10];
 #pragma unroll
     for (int p = 0; p < 10; ++p) {
       const uint32_t q = v / 9u;
@@ -149,12 +132,31 @@ __device__ __forceinline__ void chunk_dot_v(const uint32_t (&w)[Fmt<L>::cw], con
       v = q;
       cw[p] = lds_u32(lut, (e << 8) | slot);
     }
-#pragma unroll
-    for (int p = 0; p < 10; ++p) {
-      if (p < pb) a0 = dot2_h(cw[p], xp[p], a0);
-      else a1 = dot2_h(cw[p], xp[p], a1);
-    }
   }
+}
+
+// Pair products of one chunk's entries against the lane's rotated input pairs xp: pairs
+// before pb accumulate into a0 and the rest into a1. With SPLIT (groups of 16) the split
+// is after pair 8; trit words split at pb (pb = np when the word lies in one group).
+template <int L, bool SPLIT>
+__device__ __forceinline__ void chunk_dot_pairs(const uint32_t (&cw)[Fmt<L>::np],
+                                                const uint32_t (&xp)[Fmt<L>::np], int pb,
+                                                float& a0, float& a1) {
+#pragma unroll
+  for (int q = 0; q < Fmt<L>::np; ++q) {
+    const bool second = L == 3 ? q >= pb : (SPLIT && q >= 8);
+    if (second) a1 = dot2_h(cw[q], xp[q], a1);
+    else a0 = dot2_h(cw[q], xp[q], a0);
+  }
+}
+
+template <int L, bool SPLIT>
+__device__ __forceinline__ void chunk_dot_v(const uint32_t (&w)[Fmt<L>::cw], const uint32_t* lut,
+                                            uint32_t slot, const uint32_t (&xp)[Fmt<L>::np],
+                                            int pb, float& a0, float& a1) {
+  uint32_t cw[Fmt<L>::np];
+  chunk_lookup<L>(w, lut, slot, cw);
+  chunk_dot_pairs<L, SPLIT>(cw, xp, pb, a0, a1);
 }
 
 }  // namespace tq

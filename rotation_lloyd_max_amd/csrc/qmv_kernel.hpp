@@ -126,6 +126,34 @@ __device__ __forceinline__ float qmv_group_sum(const GroupRegs<L, CPL>& g, const
   return segment_sum_flat(acc, p.lpr_log);
 }
 
+// The same sum as qmv_group_sum from table entries looked up beforehand.
+template <int L, int CPL, bool G16>
+__device__ __forceinline__ float qmv_group_dot(const GroupRegs<L, CPL>& g, const QmvParams& p,
+                                               const Lane& ln,
+                                               const uint32_t (&cw)[CPL][Fmt<L>::np],
+                                               const uint32_t (&xr)[CPL][Fmt<L>::np]) {
+  using F = Fmt<L>;
+  constexpr bool TWO = (L == 3) || G16;
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int cr = ln.c0 + j * ln.lpr;
+    const int c = ln.ks * p.Qh + cr;
+    int pb = F::np;
+    if constexpr (L == 3) {
+      const int e0 = c * F::ce;
+      const int bound = ((e0 / p.group) + 1) * p.group - e0;
+      pb = bound >= F::ce ? F::np : bound / 2;
+    }
+    float a0 = 0.f, a1 = 0.f;
+    chunk_dot_pairs<L, G16>(cw[j], xr[j], pb, a0, a1);
+    float v = a0 * static_cast<float>(g.s[j].x);
+    if constexpr (TWO) v += a1 * static_cast<float>(g.s[j].y);
+    acc += cr < ln.slice_q ? v : 0.f;
+  }
+  return segment_sum_flat(acc, p.lpr_log);
+}
+
 template <int L, int CPL, bool G16, bool X32, int D>
 __global__ __launch_bounds__(kQmvThreads) void k_qmv(QmvParams p) {
   using F = Fmt<L>;
@@ -172,6 +200,8 @@ __global__ __launch_bounds__(kQmvThreads) void k_qmv(QmvParams p) {
 
   const int grp0 = blockIdx.x, stride = gridDim.x;
   GroupRegs<L, CPL> buf[D];
+  // D == 1: the launch gives every workgroup exactly one row group (grp0 < ngroups)
+  if constexpr (D == 1) qmv_load_group<L, CPL, G16>(buf[0], p, ln, grp0, cexp, sexp, ngroups_k);
 #pragma unroll
   for (int d = 0; d < D - 1; ++d) {
     const int g = grp0 + d * stride;
@@ -191,31 +221,47 @@ __global__ __launch_bounds__(kQmvThreads) void k_qmv(QmvParams p) {
   const float sc = xin.template finish_a<HALF>(xf, red, p.K, p.lk, p.P, rotated, p.inv_sqrt_k,
                                                &out_scale);
   build_lut_v<L, kQmvThreads>(lut, hs);  // complete after the next barrier
-  xin.template finish_b<HALF>(xf, xh, p.K, p.m, p.P, rotated, sc);
-  if constexpr (!HALF) pairs_to_lds<L, kQmvThreads>(xf, xh, p.K, p.Q, sc);
-  uint32_t xr[CPL][F::np];
-  lane_pairs<L, CPL>(xh, ln.ks * p.Qh, ln.c0, ln.lpr, ln.slice_q, xr);
-
   const float nan = __builtin_nanf("");
   const int rloc = ln.rset * ln.rpw + ln.sub;
   int grp = grp0, it = 0;
-  // The loop body is unrolled over U groups (a multiple of D, so the ring positions
-  // repeat): inside straight-line code the compiler waits for exactly the one group it
-  // computes; only the rare back edge (workgroups with more than U groups) waits longer.
-  constexpr int U = D >= 4 ? 8 : 4;
-  while (true) {
+  if constexpr (D == 1) {
+    // One row group per workgroup: its table lookups run between the two halves of the
+    // rotation (the codes arrived during the first), so only the products wait for x'.
+    __syncthreads();
+    uint32_t cw[CPL][F::np];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      // refill the set computed last with the group D - 1 strides ahead (past the end:
-      // this group again, lines just read, so the loads stay unconditional)
-      const int gl = grp + (D - 1) * stride;
-      qmv_load_group<L, CPL, G16>(buf[(u + D - 1) % D], p, ln, gl < p.ngroups ? gl : grp,
-                                  cexp, sexp, ngroups_k);
-      const float v = qmv_group_sum<L, CPL, G16>(buf[u % D], p, ln, lslot, lut, xr);
-      if (last_lane) rowpart[(it * ln.rows_per_group + rloc) * KS + ln.ks] = v;
-      ++it;
-      grp += stride;
-      if (grp >= p.ngroups) goto done;
+    for (int j = 0; j < CPL; ++j) chunk_lookup<L>(buf[0].w[j], lut, lslot, cw[j]);
+    xin.template finish_b<HALF>(xf, xh, p.K, p.m, p.P, rotated, sc);
+    if constexpr (!HALF) pairs_to_lds<L, kQmvThreads>(xf, xh, p.K, p.Q, sc);
+    uint32_t xr[CPL][F::np];
+    lane_pairs<L, CPL>(xh, ln.ks * p.Qh, ln.c0, ln.lpr, ln.slice_q, xr);
+    const float v = qmv_group_dot<L, CPL, G16>(buf[0], p, ln, cw, xr);
+    if (last_lane) rowpart[rloc * KS + ln.ks] = v;
+    it = 1;
+  } else {
+    xin.template finish_b<HALF>(xf, xh, p.K, p.m, p.P, rotated, sc);
+    if constexpr (!HALF) pairs_to_lds<L, kQmvThreads>(xf, xh, p.K, p.Q, sc);
+    uint32_t xr[CPL][F::np];
+    lane_pairs<L, CPL>(xh, ln.ks * p.Qh, ln.c0, ln.lpr, ln.slice_q, xr);
+
+    // The loop body is unrolled over U groups (a multiple of D, so the ring positions
+    // repeat): inside straight-line code the compiler waits for exactly the one group it
+    // computes; only the rare back edge (workgroups with more than U groups) waits longer.
+    constexpr int U = D >= 4 ? 8 : 4;
+    while (true) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        // refill the set computed last with the group D - 1 strides ahead (past the end:
+        // this group again, lines just read, so the loads stay unconditional)
+        const int gl = grp + (D - 1) * stride;
+        qmv_load_group<L, CPL, G16>(buf[(u + D - 1) % D], p, ln, gl < p.ngroups ? gl : grp,
+                                    cexp, sexp, ngroups_k);
+        const float v = qmv_group_sum<L, CPL, G16>(buf[u % D], p, ln, lslot, lut, xr);
+        if (last_lane) rowpart[(it * ln.rows_per_group + rloc) * KS + ln.ks] = v;
+        ++it;
+        grp += stride;
+        if (grp >= p.ngroups) goto done;
+      }
     }
   }
 done:
@@ -256,7 +302,8 @@ static const void* pick_depth(int depth) {
     if (depth >= 8) return reinterpret_cast<const void*>(k_qmv<L, CPL, G16, X32, 8>);
   }
   return depth >= 4 ? reinterpret_cast<const void*>(k_qmv<L, CPL, G16, X32, 4>)
-                    : reinterpret_cast<const void*>(k_qmv<L, CPL, G16, X32, 2>);
+         : depth >= 2 ? reinterpret_cast<const void*>(k_qmv<L, CPL, G16, X32, 2>)
+                      : reinterpret_cast<const void*>(k_qmv<L, CPL, G16, X32, 1>);
 }
 
 template <int L, int CPL>
@@ -301,7 +348,8 @@ hipError_t launch_qmv_l(QmvParams& p, int n_slots, hipStream_t s) {
     }
   }
   p.max_iters = iters;
-  const int depth = iters <= 2 ? 2 : iters <= 4 ? 4 : 8;
+  // one group per workgroup: no ring (depth 1, lookups overlap the rotation)
+  const int depth = iters <= 1 ? 1 : iters <= 2 ? 2 : iters <= 4 ? 4 : 8;
   const bool g16 = (L != 3) && p.group == 16;
   const bool x32 = p.xdt == 0;
   const void* kern = cpl <= 1 ? pick_kernel<L, 1>(g16, x32, depth)
