@@ -5,7 +5,7 @@
 //   k_bucket   counting sort of the pairs by expert into the workspace (offsets, order);
 //              pairs with an expert id outside [0, E) get a row of NaN
 //   k_rot16    every input rotated once into fp16 rows (rot16.hpp), plus one zero row
-//   k_mg       one workgroup per (expert, block of 64 output rows): each wave decodes the
+//   k_mg       one workgroup per (expert, block of 128 output rows): each wave decodes the
 //              codes of 16 rows straight into matrix-core operands (mfma_decode.hpp) and
 //              multiplies them by the rotated inputs of up to 16 of the expert's pairs at a
 //              time with v_mfma_f32_16x16x32_f16, so every code word is read from memory
@@ -18,7 +18,10 @@ namespace tq {
 
 constexpr int kBucketThreads = 1024;
 constexpr int kMaxExperts = 8192;
-constexpr int kMgWaves = 4;
+// 8 waves (128 rows) per workgroup and at most 128 VGPRs per lane (4 waves per SIMD), so
+// that two trit workgroups (70 KB of LDS each) share a CU, each with a whole 128-row K-chunk
+// of loads in flight.
+constexpr int kMgWaves = 8;
 constexpr int kMgThreads = 64 * kMgWaves;
 
 static size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
@@ -123,7 +126,7 @@ struct MgChunk {
   static constexpr int AST = KC + 8;             // LDS halves per row of inputs
   static constexpr int ROWS = 16 * kMgWaves;     // weight rows per workgroup
   static constexpr int CW = ROWS * WPC / kMgThreads;        // code words per thread
-  static constexpr int AU = 16 * (KC / 8) / kMgThreads;     // 16-byte input units per thread
+  static constexpr int AU = (16 * (KC / 8) + kMgThreads - 1) / kMgThreads;  // 16-byte input units per thread (units past 16 rows are never pairs)
 };
 
 constexpr int kMaxScalesPerChunk = 640 / 16;  // groups of a chunk at most (trits, g16)
@@ -217,7 +220,7 @@ __device__ __forceinline__ void mg_stash(const MgStage<L>& st, const MgTile& t, 
 }
 
 template <int L>
-__global__ __launch_bounds__(kMgThreads) void k_mg(MgParams p) {
+__global__ __launch_bounds__(kMgThreads, 4) void k_mg(MgParams p) {
   using S = Span<L>;
   using C = MgChunk<L>;
   // the table is the only static LDS array: it starts at address 0
