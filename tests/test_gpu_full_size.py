@@ -1,0 +1,111 @@
+"""GPU parity at the full sizes of the MoE workloads, on sampled outputs, through the C ABI
+and in the launch configuration bench.py times: full expert stacks encoded on the GPU, the
+same routing generators, the whole batch in one call. The oracle recomputes sampled output
+rows one by one from the GPU's own codes (encode parity is tested on its own)."""
+
+import numpy as np
+import pytest
+import torch
+
+import rotation_lloyd_max_amd as tq
+import workloads as wl
+from parity import as_f64, check_outputs, qmv_reference, torch_to_np
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda")
+
+
+def encode_stack(cfg, pr, chunk=16):
+    """The expert stack of projection pr, its bf16 weights drawn on the GPU chunk by chunk."""
+    E, N, K = cfg.E, pr.N, pr.K
+    codes = torch.empty((E, N, tq.words_per_row(K, pr.levels)), dtype=torch.int32, device=DEV)
+    scales = torch.empty((E, N, K // pr.group), dtype=torch.float16, device=DEV)
+    sg = tq.signs(pr.seed, K, DEV)
+    for e0 in range(0, E, chunk):
+        e1 = min(E, e0 + chunk)
+        g = wl.torch_generator(DEV, cfg.cid, wl.PROJ_TENSOR[pr.name], e0)
+        W = wl.torch_student_rows(g, (e1 - e0) * N, K, DEV, torch.bfloat16).view(e1 - e0, N, K)
+        tq.encode(W, pr.levels, pr.group, pr.seed,
+                  out=tq.QWeight(codes[e0:e1], scales[e0:e1], sg, pr.levels, pr.group, K, N, e1 - e0, pr.seed))
+        del W
+    torch.cuda.synchronize()
+    return tq.QWeight(codes, scales, sg, pr.levels, pr.group, K, N, E, pr.seed)
+
+
+def sampled_check(qw, e, rows, x_rows, y_rows, tag):
+    """Oracle rows `rows` of expert e against inputs x_rows ([n][K] fp64) vs y_rows ([n][rows])."""
+    codes = torch_to_np(qw.codes[e, rows]).reshape(len(rows), -1)
+    scales = torch_to_np(qw.scales[e, rows]).reshape(len(rows), -1)
+    want, bound = qmv_reference(codes, scales, qw.levels, qw.group, qw.K, qw.seed, x_rows)
+    return check_outputs(y_rows, want, bound, tag)
+
+
+@pytest.mark.parametrize("proj", ["gate", "down"])
+def test_moe_decode_gather_qmv_full_size(proj):
+    # 384 experts, hidden 7168, intermediate 2048; gate 2-bit g64, down 4-bit g64; one token
+    # routed to 8 experts drawn by the decode routing generator
+    c = wl.C3
+    pr = next(p for p in c.projs if p.name == proj)
+    qw = encode_stack(c, pr)
+    ids_np = wl.decode_ids(c.cid, 0, c.E, 8)
+    x = torch.randn(pr.K, generator=wl.torch_generator(DEV, c.cid, wl.T_X), device=DEV).to(torch.bfloat16)
+    y = tq.gather_qmv(qw, torch.from_numpy(ids_np).to(DEV), x)
+    torch.cuda.synchronize()
+    yg, xf = as_f64(y), as_f64(x)
+    g = wl.rng(c.cid, 90)
+    for k, e in enumerate(ids_np):
+        rows = np.sort(g.choice(pr.N, 48, replace=False))
+        sampled_check(qw, int(e), rows, xf, yg[k, rows], f"C3 {proj} slot {k} expert {e}")
+
+
+@pytest.mark.parametrize("proj", ["gate", "down"])
+def test_ternary_prefill_multi_gather_full_size(proj):
+    # 128 experts, hidden 2048, intermediate 768, trits g16; 64 tokens routed top-8
+    c = wl.C4
+    pr = next(p for p in c.projs if p.name == proj)
+    qw = encode_stack(c, pr)
+    ids_np = wl.topk_routing(c.cid, 64, c.E, 8)
+    P = len(ids_np)
+    X = torch.randn((P, pr.K), generator=wl.torch_generator(DEV, c.cid, wl.T_X), device=DEV).to(torch.bfloat16)
+    ws = torch.empty((tq.workspace_bytes(tq.OP_MULTI_GATHER_QMV, qw, P) + 7) // 8, dtype=torch.int64, device=DEV)
+    y = tq.multi_gather_qmv(qw, torch.from_numpy(ids_np).to(DEV), X, ws=ws)
+    torch.cuda.synchronize()
+    yg, Xf = as_f64(y), as_f64(X)
+    g = wl.rng(c.cid, 91)
+    for p_ in np.sort(g.choice(P, 24, replace=False)):
+        rows = np.sort(g.choice(pr.N, 32, replace=False))
+        e = int(ids_np[p_])
+        sampled_check(qw, e, rows, Xf[p_], yg[p_, rows], f"C4 {proj} pair {p_} expert {e}")
+
+
+@pytest.mark.parametrize("proj", ["gate", "down"])
+def test_batched_gather_qmm_full_size(proj):
+    # 4096 tokens x top-8 of 128 experts (Zipf-skewed), hidden 4096, intermediate 1536,
+    # 4-bit g128; rows sorted by expert; gate reads the token rows, down one input per row
+    c = wl.C5
+    pr = next(p for p in c.projs if p.name == proj)
+    qw = encode_stack(c, pr)
+    T, k = 4096, 8
+    row_token, row_expert, offsets = wl.zipf_sorted_routing(c.cid, T, c.E, k)
+    M = len(row_token)
+    gen = wl.torch_generator(DEV, c.cid, wl.T_X)
+    if proj == "gate":
+        X = torch.randn((T, pr.K), generator=gen, device=DEV).to(torch.bfloat16)
+        rt = row_token
+    else:
+        X = torch.randn((M, pr.K), generator=gen, device=DEV).to(torch.bfloat16)
+        rt = np.arange(M, dtype=np.int32)
+    ws = torch.empty((tq.workspace_bytes(tq.OP_GATHER_QMM, qw, M, X.shape[0]) + 7) // 8,
+                     dtype=torch.int64, device=DEV)
+    y = tq.gather_qmm(qw, X, torch.from_numpy(rt).to(DEV), torch.from_numpy(offsets).to(DEV), ws=ws)
+    torch.cuda.synchronize()
+    g = wl.rng(c.cid, 92)
+    ms = np.sort(g.choice(M, 40, replace=False))
+    ys = as_f64(y[torch.from_numpy(ms).to(DEV)])
+    Xs = as_f64(X[torch.from_numpy(rt[ms]).to(DEV)])
+    for i, m in enumerate(ms):
+        e = int(row_expert[m])
+        assert offsets[e] <= m < offsets[e + 1]
+        cols = np.sort(g.choice(pr.N, 48, replace=False))
+        sampled_check(qw, e, cols, Xs[i], ys[i, cols], f"C5 {proj} row {m} expert {e}")
