@@ -486,7 +486,7 @@ hipError_t launch_gather_qmm(const WeightArgs& w, const void* x, int xdt, int64_
   int32_t* count = reinterpret_cast<int32_t*>(base + lay.count);
   int4* tiles = reinterpret_cast<int4*>(base + lay.tiles);
 
-  hipError_t err = launch_rot16(x, xdt, nullptr, T, /*zero_rows=*/1, w, x_rotated, xh, xs, s);
+  hipError_t err = launch_rot16(x, xdt, nullptr, T, /*zero_rows=*/1, w, x_rotated, xh, xs, nullptr, s);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_schedule, dim3(1), dim3(kSchedThreads), 0, s, offsets, w.E, M, count, tiles);
   err = hipGetLastError();

@@ -46,10 +46,12 @@ hipError_t launch_qmv(const WeightArgs& w, const int32_t* ids, int n, const void
                       bool x_rotated, void* y, int ydt, hipStream_t s);
 
 // Rotate nrows input rows (input row rows[r], or r when rows is null) into fp16 rows in
-// the layout of rot16.hpp, then write zero_rows rows of zeros after them.
+// the layout of rot16.hpp, then write zero_rows rows of zeros after them; with a bucket job
+// (bucket.hpp), one more workgroup of the same launch sorts the pairs by expert.
+struct BucketJob;
 hipError_t launch_rot16(const void* x, int xdt, const int32_t* rows, int64_t nrows,
                         int64_t zero_rows, const WeightArgs& w, bool x_rotated, _Float16* out,
-                        float* scale, hipStream_t s);
+                        float* scale, const BucketJob* bucket, hipStream_t s);
 size_t multi_gather_workspace(const WeightArgs& w, int64_t P);
 hipError_t launch_multi_gather(const WeightArgs& w, const int32_t* ids, int64_t P,
                                const void* x, int xdt, bool x_rotated, void* y, int ydt,

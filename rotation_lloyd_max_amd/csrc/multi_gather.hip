@@ -1,10 +1,11 @@
 // multi_gather_qmv: y[p] = W_{ids[p]} R x[p] for P (input, expert) pairs.
 //
 // turboquant-mlx "How it works", "Running a quantized layer", kernel table, second row:
-// prefill with a different input per expert. Three launches:
-//   k_bucket   counting sort of the pairs by expert into the workspace (offsets, order);
-//              pairs with an expert id outside [0, E) get a row of NaN
-//   k_rot16    every input rotated once into fp16 rows (rot16.hpp), plus one zero row
+// prefill with a different input per expert. Two launches:
+//   k_rot16    every input rotated once into fp16 rows (rot16.hpp), plus one zero row; one
+//              more workgroup of the same launch sorts the pairs by expert into the
+//              workspace (bucket.hpp: offsets, order); pairs with an expert id outside
+//              [0, E) get a row of NaN
 //   k_mg       one workgroup per (expert, block of 128 output rows): each wave decodes the
 //              codes of 16 rows straight into matrix-core operands (mfma_decode.hpp) and
 //              multiplies them by the rotated inputs of up to 16 of the expert's pairs at a
@@ -16,7 +17,6 @@
 
 namespace tq {
 
-constexpr int kBucketThreads = 1024;
 constexpr int kMaxExperts = 8192;
 // 8 waves (128 rows) per workgroup and at most 128 VGPRs per lane (4 waves per SIMD), so
 // that two trit workgroups (70 KB of LDS each) share a CU, each with a whole 128-row K-chunk
@@ -42,60 +42,6 @@ static MgLayout mg_layout(const WeightArgs& w, int64_t P) {
 }
 
 size_t multi_gather_workspace(const WeightArgs& w, int64_t P) { return mg_layout(w, P).total; }
-
-__global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* ids, int64_t P, int E,
-                                                           int32_t* offsets, int32_t* order,
-                                                           void* y, int ydt, int N) {
-  __shared__ int32_t cnt[kMaxExperts];
-  __shared__ int32_t wsum[kBucketThreads / 64];
-  for (int e = threadIdx.x; e < E; e += kBucketThreads) cnt[e] = 0;
-  __syncthreads();
-  for (int64_t p = threadIdx.x; p < P; p += kBucketThreads) {
-    const int e = ids[p];
-    if (e >= 0 && e < E) {
-      atomicAdd(&cnt[e], 1);
-    } else {
-      for (int n = 0; n < N; ++n) store_any(y, ydt, p * N + n, __builtin_nanf(""));
-    }
-  }
-  __syncthreads();
-  // exclusive scan of cnt[0..E) in chunks of kBucketThreads, carried by thread 0's running sum
-  int carry = 0;
-  for (int base = 0; base < E; base += kBucketThreads) {
-    const int e = base + threadIdx.x;
-    int v = e < E ? cnt[e] : 0;
-    // inclusive wave scan
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int off = 1; off < 64; off <<= 1) {
-      const int t = __shfl_up(v, off, 64);
-      if (lane >= off) v += t;
-    }
-    if (lane == 63) wsum[wave] = v;
-    __syncthreads();
-    int before = carry;
-    for (int k = 0; k < wave; ++k) before += wsum[k];
-    const int incl = before + v;
-    int excl = incl - (e < E ? cnt[e] : 0);
-    __syncthreads();
-    if (e < E) {
-      offsets[e] = excl;
-      cnt[e] = excl;  // becomes the scatter cursor
-    }
-    int total = carry;
-    for (int k = 0; k < static_cast<int>(kBucketThreads >> 6); ++k) total += wsum[k];
-    carry = total;
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) offsets[E] = carry;
-  __syncthreads();
-  for (int64_t p = threadIdx.x; p < P; p += kBucketThreads) {
-    const int e = ids[p];
-    if (e >= 0 && e < E) {
-      const int pos = atomicAdd(&cnt[e], 1);
-      order[pos] = static_cast<int32_t>(p);
-    }
-  }
-}
 
 struct MgParams {
   const uint32_t* codes;
@@ -314,12 +260,10 @@ hipError_t launch_multi_gather(const WeightArgs& w, const int32_t* ids, int64_t 
   int32_t* order = reinterpret_cast<int32_t*>(base + lay.order);
   float* xs = reinterpret_cast<float*>(base + lay.scale);
   _Float16* xh = reinterpret_cast<_Float16*>(base + lay.rows);
-  hipLaunchKernelGGL(k_bucket, dim3(1), dim3(kBucketThreads), 0, s, ids, P, w.E, offsets, order, y,
-                     ydt, w.N);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-
-  err = launch_rot16(x, xdt, nullptr, P, /*zero_rows=*/1, w, x_rotated, xh, xs, s);
+  if (w.E > kMaxExperts) return hipErrorInvalidValue;
+  // one launch rotates every pair's input and (one extra workgroup) buckets the pairs
+  BucketJob job{ids, P, w.E, offsets, order, y, ydt, w.N};
+  hipError_t err = launch_rot16(x, xdt, nullptr, P, /*zero_rows=*/1, w, x_rotated, xh, xs, &job, s);
   if (err != hipSuccess) return err;
 
   MgParams p{};

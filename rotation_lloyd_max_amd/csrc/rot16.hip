@@ -6,8 +6,8 @@ namespace tq {
 
 hipError_t launch_rot16(const void* x, int xdt, const int32_t* rows, int64_t nrows,
                         int64_t zero_rows, const WeightArgs& w, bool x_rotated, _Float16* out,
-                        float* scale, hipStream_t s) {
-  const int64_t total = nrows + zero_rows;
+                        float* scale, const BucketJob* bucket, hipStream_t s) {
+  const int64_t total = nrows + zero_rows + (bucket ? 1 : 0);
   if (total == 0) return hipSuccess;
   Rot16Params p{};
   p.x = x; p.rows = rows; p.signs = w.signs; p.out = out; p.scale = scale;
@@ -17,7 +17,8 @@ hipError_t launch_rot16(const void* x, int xdt, const int32_t* rows, int64_t nro
   while ((1 << lk) < w.K) ++lk;
   p.lk = lk;
   p.inv_sqrt_k = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(w.K)));
-  const size_t lds = rot16_lds_bytes(w.K);
+  if (bucket) p.bucket = *bucket;
+  const size_t lds = rot16_lds_bytes(w.K, bucket ? bucket->E : 0);
   const dim3 grid(static_cast<unsigned>(total < 65536 ? total : 65536),
                   static_cast<unsigned>((total + 65535) / 65536));
   if (xdt == 0) hipLaunchKernelGGL(k_rot16<true>, grid, dim3(kRotThreads), lds, s, p);

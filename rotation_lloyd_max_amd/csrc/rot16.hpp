@@ -7,6 +7,7 @@
 // (or 1 / sc_r for an input that is already rotated) is applied to the products.
 #pragma once
 
+#include "bucket.hpp"
 #include "prologue.hpp"
 
 namespace tq {
@@ -25,6 +26,7 @@ struct Rot16Params {
   int64_t zero_rows;
   int K, m, P, lk, xdt, rotated;
   float inv_sqrt_k;
+  BucketJob bucket;  // with bucket.ids set, the workgroup after the last row sorts pairs
 };
 
 template <bool X32>
@@ -35,7 +37,13 @@ __global__ __launch_bounds__(kRotThreads) void k_rot16(Rot16Params p) {
   float* xf = reinterpret_cast<float*>(xh + Q * (kChunkHalves / 2));
   float* red = xf + padded_len(p.K);
   const int64_t r = blockIdx.x + static_cast<int64_t>(blockIdx.y) * gridDim.x;
-  if (r >= p.nrows + p.zero_rows) return;  // uniform per workgroup
+  if (r >= p.nrows + p.zero_rows) {  // uniform per workgroup
+    if (r == p.nrows + p.zero_rows && p.bucket.ids) {
+      int32_t* cnt = reinterpret_cast<int32_t*>(smem_r);
+      bucket_pairs<kRotThreads>(p.bucket, cnt, cnt + p.bucket.E);
+    }
+    return;
+  }
   if (r >= p.nrows) {
     uint4* dst = reinterpret_cast<uint4*>(p.out + r * rot16_row_halves(p.K));
     for (int i = threadIdx.x; i < Q * 4; i += kRotThreads) dst[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -58,10 +66,12 @@ __global__ __launch_bounds__(kRotThreads) void k_rot16(Rot16Params p) {
   if (threadIdx.x == 0) p.scale[r] = out_scale;
 }
 
-inline size_t rot16_lds_bytes(int K) {
+inline size_t rot16_lds_bytes(int K, int bucket_experts) {
   const int Q = (K + 31) / 32;
-  return static_cast<size_t>(Q) * kChunkHalves * 2 + padded_len(K) * 4 + (kRotThreads / 64) * 4 +
-         16;
+  const size_t rot = static_cast<size_t>(Q) * kChunkHalves * 2 + padded_len(K) * 4 +
+                     (kRotThreads / 64) * 4 + 16;
+  const size_t bkt = static_cast<size_t>(bucket_experts + kRotThreads / 64) * 4;
+  return rot > bkt ? rot : bkt;
 }
 
 }  // namespace tq
