@@ -236,6 +236,13 @@ __global__ __launch_bounds__(kQmvThreads) void k_qmv(QmvParams p) {
     uint32_t xr[CPL][F::np];
     lane_pairs<L, CPL>(xh, ln.ks * p.Qh, ln.c0, ln.lpr, ln.slice_q, xr);
     const float v = qmv_group_dot<L, CPL, G16>(buf[0], p, ln, cw, xr);
+    if (KS == 1) {
+      // a whole row per lane segment and no loads left: its last lane stores the result
+      const int n = grp0 * ln.rows_per_group + rloc;
+      if (last_lane && n < p.N)
+        store_any(p.y, p.ydt, static_cast<int64_t>(slot) * p.N + n, bad ? nan : v * out_scale);
+      return;
+    }
     if (last_lane) rowpart[rloc * KS + ln.ks] = v;
     it = 1;
   } else {
