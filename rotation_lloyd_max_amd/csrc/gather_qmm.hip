@@ -75,27 +75,33 @@ size_t gather_qmm_workspace(const WeightArgs& w, int64_t M, int64_t T) {
 constexpr int kSchedThreads = 1024;
 
 // The tile table: expert e's rows offsets[e] .. offsets[e+1] - 1 are cut into tiles of
-// 128; tiles are listed expert by expert. Experts with no rows (or inconsistent offsets)
-// get no tile; the table never holds more than max_tiles entries. Each thread takes a
-// block of consecutive experts; a block-wide scan of the per-thread tile counts gives
-// every expert its first table index.
+// 128. Full tiles come first (expert by expert), then the experts' last, partial tiles from
+// the largest to the smallest, so that the short tiles fill the end of the launch (longest
+// first). Experts with no rows (or inconsistent offsets) get no tile; the table never holds
+// more than max_tiles entries. Each thread takes a block of consecutive experts: a
+// block-wide scan places the full tiles, a histogram over the partial sizes the rest.
 __global__ __launch_bounds__(kSchedThreads) void k_schedule(const int32_t* offsets, int E,
                                                            int64_t M, int32_t* count,
                                                            int4* tiles) {
   constexpr int PER = (kMaxExpertsQmm + kSchedThreads - 1) / kSchedThreads;
   __shared__ int32_t wsum[kSchedThreads / 64];
+  __shared__ int32_t pos[kQmmBM];  // next table index for partial tiles of each size
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int e0 = threadIdx.x * PER;
-  int n[PER];
+  if (threadIdx.x < kQmmBM) pos[threadIdx.x] = 0;
+  __syncthreads();
+  int nfull[PER], part[PER];
   int local = 0;
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const int e = e0 + k;
-    int rows = e < E ? offsets[e + 1] - offsets[e] : 0;
-    n[k] = rows > 0 ? (rows + kQmmBM - 1) / kQmmBM : 0;
-    local += n[k];
+    const int rows = e < E ? offsets[e + 1] - offsets[e] : 0;
+    nfull[k] = rows > 0 ? rows / kQmmBM : 0;
+    part[k] = rows > 0 ? rows % kQmmBM : 0;
+    local += nfull[k];
+    if (part[k] > 0) atomicAdd(&pos[part[k]], 1);
   }
-  // inclusive scan within the wave, then across the waves
+  // inclusive scan of the full-tile counts within the wave, then across the waves
   int v = local;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -104,26 +110,37 @@ __global__ __launch_bounds__(kSchedThreads) void k_schedule(const int32_t* offse
   }
   if (lane == 63) wsum[wave] = v;
   __syncthreads();
-  int before = 0, total = 0;
+  int before = 0, full = 0;
 #pragma unroll
   for (int w = 0; w < kSchedThreads / 64; ++w) {
     const int x = wsum[w];
     before += w < wave ? x : 0;
-    total += x;
+    full += x;
   }
+  if (threadIdx.x == 0) {
+    // partial sizes from 127 rows down to 1: histogram counts -> first table indices
+    int at = full;
+    for (int r = kQmmBM - 1; r >= 1; --r) {
+      const int c = pos[r];
+      pos[r] = at;
+      at += c;
+    }
+    const int64_t cap = max_tiles_dev(M, E);
+    *count = static_cast<int>(at < cap ? at : cap);
+  }
+  __syncthreads();
   const int64_t cap = max_tiles_dev(M, E);
-  int idx = before + v - local;  // first table index of this thread's experts
-  if (threadIdx.x == 0) *count = static_cast<int>(total < cap ? total : cap);
+  int idx = before + v - local;  // first table index of this thread's full tiles
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const int e = e0 + k;
-    if (n[k] > 0) {
-      const int o0 = offsets[e], o1 = offsets[e + 1];
-      for (int t = 0; t < n[k]; ++t, ++idx) {
-        if (idx >= cap) break;
-        const int m0 = o0 + t * kQmmBM;
-        tiles[idx] = make_int4(e, m0, o1 - m0 < kQmmBM ? o1 - m0 : kQmmBM, 0);
-      }
+    if (nfull[k] + part[k] == 0) continue;
+    const int o0 = offsets[e];
+    for (int t = 0; t < nfull[k]; ++t, ++idx)
+      if (idx < cap) tiles[idx] = make_int4(e, o0 + t * kQmmBM, kQmmBM, 0);
+    if (part[k] > 0) {
+      const int at = atomicAdd(&pos[part[k]], 1);
+      if (at < cap) tiles[at] = make_int4(e, o0 + nfull[k] * kQmmBM, part[k], 0);
     }
   }
 }
@@ -424,18 +441,16 @@ __global__ __launch_bounds__(kQmmThreads) void k_gqmm(QmmParams p) {
   __shared__ uint16_t hs[16];
   __shared__ uint16_t ls[SL ? kQmmBN * (kQmmMaxLdsGroups + 1) : 1];
 
-  // Tile order: consecutive virtual ids run on one XCD (workgroups are dealt to the 8 XCDs
-  // in turn), so the column tiles of one row tile, and the row tiles of one expert, share
-  // that XCD's L2.
+  // Workgroups are dealt to the 8 XCDs in turn (XCD b % 8). Row tile t goes to XCD t % 8,
+  // all its column tiles in a row there, so they share the tile's inputs in that XCD's L2;
+  // each XCD takes its row tiles in table order (longest first).
   const int total_mt = *p.count;
   const int nt = (p.N + kQmmBN - 1) / kQmmBN;
-  const int G = total_mt * nt;
-  const int per = (G + 7) >> 3;
   const int b = blockIdx.x;
-  if ((b >> 3) >= per) return;
-  const int v = (b & 7) * per + (b >> 3);
-  if (v >= G) return;  // uniform per workgroup
-  const int t = v / nt, ntile = v - t * nt;
+  const int i = b >> 3;
+  const int tl = i / nt, ntile = i - tl * nt;
+  const int t = tl * 8 + (b & 7);
+  if (t >= total_mt) return;  // uniform per workgroup
   const int4 te = p.tiles[t];
   const int e = te.x, m0 = te.y;
   if (e < 0 || e >= p.E || m0 < 0 || m0 >= p.M) return;  // never touch memory past y
@@ -500,9 +515,9 @@ hipError_t launch_gather_qmm(const WeightArgs& w, const void* x, int xdt, int64_
   p.ngk = w.K / w.group;
   p.lg_group = __builtin_ctz(w.group);
   p.cb = *codebook_for(w.levels);
-  // enough workgroups for any schedule, rounded up to a multiple of 8 for the XCD-major order
+  // enough workgroups for any schedule: 8 XCDs x ceil(tiles / 8) row tiles x column tiles
   const int64_t nt = (w.N + kQmmBN - 1) / kQmmBN;
-  const int64_t gx = (max_tiles(M, w.E) * nt + 7) / 8 * 8;
+  const int64_t gx = 8 * ((max_tiles(M, w.E) + 7) / 8) * nt;
   if (gx > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(gx));
   const bool g16 = w.group == 16;
