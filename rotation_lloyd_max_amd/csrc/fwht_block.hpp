@@ -192,36 +192,41 @@ __device__ __forceinline__ void hadamard_part(T* col, int pstride, const T (&x)[
 // written; the function synchronizes at the end. With OUT the outputs go to the sink.
 template <typename T, int M, int TPC, int NT, bool OUT>
 __device__ __forceinline__ void hadamard_factor_split(T* buf, int P, HalfSink sink) {
-  const int t = threadIdx.x;
-  const bool active = t < P * TPC;
-  const int q = t / P, b = t - q * P;
-  T x[M];
-  if (P % 16 == 0) {
-    // element (a, b) is at pidx(a * P + b) = pidx(b) + a * (P + P / 16)
-    const int pstride = P + (P >> 4);
-    T* col = buf + pidx(b);
-    if (active) {
+  // TPC == 1 loops over the columns when there are more columns than threads; with
+  // TPC > 1 (P * TPC <= NT) there is one pass
+  const int span = TPC == 1 ? P : NT;
+  for (int t0 = 0; t0 < span; t0 += NT) {
+    const int t = t0 + static_cast<int>(threadIdx.x);
+    const bool active = t < P * TPC;
+    const int q = t / P, b = t - q * P;
+    T x[M];
+    if (P % 16 == 0) {
+      // element (a, b) is at pidx(a * P + b) = pidx(b) + a * (P + P / 16)
+      const int pstride = P + (P >> 4);
+      T* col = buf + pidx(b);
+      if (active) {
 #pragma unroll
-      for (int a = 0; a < M; ++a) x[a] = col[a * pstride];
-    }
-    if constexpr (TPC > 1) __syncthreads();  // the other parts read the same inputs
-    if (active) {
-      [&]<int... Q>(std::integer_sequence<int, Q...>) {
-        ((q == Q ? (hadamard_part<T, M, TPC, Q, OUT>(col, pstride, x, b, P, sink), 0) : 0), ...);
-      }(std::make_integer_sequence<int, TPC>{});
-    }
-  } else if (active) {
-    // rows shorter than 16 (only with TPC == 1): general indexing
+        for (int a = 0; a < M; ++a) x[a] = col[a * pstride];
+      }
+      if constexpr (TPC > 1) __syncthreads();  // the other parts read the same inputs
+      if (active) {
+        [&]<int... Q>(std::integer_sequence<int, Q...>) {
+          ((q == Q ? (hadamard_part<T, M, TPC, Q, OUT>(col, pstride, x, b, P, sink), 0) : 0), ...);
+        }(std::make_integer_sequence<int, TPC>{});
+      }
+    } else if (active) {
+      // rows shorter than 16 (only with TPC == 1): general indexing
 #pragma unroll
-    for (int a = 0; a < M; ++a) x[a] = buf[pidx(a * P + b)];
-    T y[M];
-    [&]<int... A>(std::integer_sequence<int, A...>) {
-      ((y[A] = hadamard_row<T, M, A>(x, std::make_integer_sequence<int, M>{})), ...);
-    }(std::make_integer_sequence<int, M>{});
+      for (int a = 0; a < M; ++a) x[a] = buf[pidx(a * P + b)];
+      T y[M];
+      [&]<int... A>(std::integer_sequence<int, A...>) {
+        ((y[A] = hadamard_row<T, M, A>(x, std::make_integer_sequence<int, M>{})), ...);
+      }(std::make_integer_sequence<int, M>{});
 #pragma unroll
-    for (int a = 0; a < M; ++a) {
-      if constexpr (OUT) sink.put_at(HalfSink::idx(a * P + b), y[a]);
-      else buf[pidx(a * P + b)] = y[a];
+      for (int a = 0; a < M; ++a) {
+        if constexpr (OUT) sink.put_at(HalfSink::idx(a * P + b), y[a]);
+        else buf[pidx(a * P + b)] = y[a];
+      }
     }
   }
   __syncthreads();
@@ -233,7 +238,7 @@ __device__ __forceinline__ void hadamard_factor_m(T* buf, int P, HalfSink sink) 
     hadamard_factor_split<T, M, 1, NT, OUT>(buf, P, sink);
     return;
   }
-  const int tpc = NT / P;  // 1 .. NT / 64, a power of two
+  const int tpc = NT / P;  // 0 (more columns than threads) .. NT / 64, a power of two
   if constexpr (M == 28) {
     if (tpc >= 2) hadamard_factor_split<T, M, 2, NT, OUT>(buf, P, sink);
     else hadamard_factor_split<T, M, 1, NT, OUT>(buf, P, sink);

@@ -117,16 +117,24 @@ __global__ __launch_bounds__(kSchedThreads) void k_schedule(const int32_t* offse
     before += w < wave ? x : 0;
     full += x;
   }
-  if (threadIdx.x == 0) {
-    // partial sizes from 127 rows down to 1: histogram counts -> first table indices
-    int at = full;
-    for (int r = kQmmBM - 1; r >= 1; --r) {
-      const int c = pos[r];
-      pos[r] = at;
-      at += c;
+  if (wave == 0) {
+    // partial sizes from 127 rows down to 1: histogram counts -> first table indices, by a
+    // wave scan (lane l takes the sizes 127 - 2l and 126 - 2l; size 0 holds no tile)
+    const int r0 = kQmmBM - 1 - 2 * lane, r1 = r0 - 1;
+    const int c0 = pos[r0], c1 = r1 >= 1 ? pos[r1] : 0;
+    int sc = c0 + c1;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(sc, off, 64);
+      if (lane >= off) sc += t;
     }
-    const int64_t cap = max_tiles_dev(M, E);
-    *count = static_cast<int>(at < cap ? at : cap);
+    const int at = full + sc - c0 - c1;
+    pos[r0] = at;
+    if (r1 >= 1) pos[r1] = at + c0;
+    if (lane == 63) {
+      const int64_t cap = max_tiles_dev(M, E);
+      *count = static_cast<int>(full + sc < cap ? full + sc : cap);
+    }
   }
   __syncthreads();
   const int64_t cap = max_tiles_dev(M, E);

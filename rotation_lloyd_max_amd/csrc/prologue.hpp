@@ -20,9 +20,9 @@ constexpr int kMaxK = 8192;
 // X32: the input is fp32; otherwise a 16-bit type, bf16 or fp16 by the runtime dtype.
 // All loads are unconditional (indices are clamped) so that no branch separates them from
 // the loads the caller issues next, and the compiler can wait for exactly these.
-template <bool X32, int NT>
+template <bool X32, int NT, int MAXK = kMaxK>
 struct InputLoad {
-  static constexpr int kSeg16 = (kMaxK / 16 + NT - 1) / NT;  // 16-element segments per thread
+  static constexpr int kSeg16 = (MAXK / 16 + NT - 1) / NT;  // 16-element segments per thread
   static constexpr int kW = X32 ? 16 : 8;
   uint32_t raw[kSeg16][kW];
   uint32_t sw[kSeg16];  // the sign word holding each segment's 16 sign bits

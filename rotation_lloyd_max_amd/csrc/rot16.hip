@@ -21,8 +21,15 @@ hipError_t launch_rot16(const void* x, int xdt, const int32_t* rows, int64_t nro
   const size_t lds = rot16_lds_bytes(w.K, bucket ? bucket->E : 0);
   const dim3 grid(static_cast<unsigned>(total < 65536 ? total : 65536),
                   static_cast<unsigned>((total + 65535) / 65536));
-  if (xdt == 0) hipLaunchKernelGGL(k_rot16<true>, grid, dim3(kRotThreads), lds, s, p);
-  else hipLaunchKernelGGL(k_rot16<false>, grid, dim3(kRotThreads), lds, s, p);
+  // short rows take one wave each, unless the launch also sorts pairs (that workgroup
+  // wants the full width)
+  if (w.K <= kRotShortK && !bucket) {
+    if (xdt == 0) hipLaunchKernelGGL((k_rot16<true, 64, kRotShortK>), grid, dim3(64), lds, s, p);
+    else hipLaunchKernelGGL((k_rot16<false, 64, kRotShortK>), grid, dim3(64), lds, s, p);
+  } else {
+    if (xdt == 0) hipLaunchKernelGGL((k_rot16<true, kRotThreads, kMaxK>), grid, dim3(kRotThreads), lds, s, p);
+    else hipLaunchKernelGGL((k_rot16<false, kRotThreads, kMaxK>), grid, dim3(kRotThreads), lds, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -29,8 +29,10 @@ struct Rot16Params {
   BucketJob bucket;  // with bucket.ids set, the workgroup after the last row sorts pairs
 };
 
-template <bool X32>
-__global__ __launch_bounds__(kRotThreads) void k_rot16(Rot16Params p) {
+// NT threads per row; MAXK bounds K (registers per thread). Short rows take one wave each
+// (NT = 64: the passes' barriers are a single wave's, and many rows are in flight per CU).
+template <bool X32, int NT, int MAXK>
+__global__ __launch_bounds__(NT) void k_rot16(Rot16Params p) {
   extern __shared__ uint32_t smem_r[];
   const int Q = (p.K + 31) / 32;
   uint32_t* xh = smem_r;                                     // Q * 20 words
@@ -40,18 +42,18 @@ __global__ __launch_bounds__(kRotThreads) void k_rot16(Rot16Params p) {
   if (r >= p.nrows + p.zero_rows) {  // uniform per workgroup
     if (r == p.nrows + p.zero_rows && p.bucket.ids) {
       int32_t* cnt = reinterpret_cast<int32_t*>(smem_r);
-      bucket_pairs<kRotThreads>(p.bucket, cnt, cnt + p.bucket.E);
+      bucket_pairs<NT>(p.bucket, cnt, cnt + p.bucket.E);
     }
     return;
   }
   if (r >= p.nrows) {
     uint4* dst = reinterpret_cast<uint4*>(p.out + r * rot16_row_halves(p.K));
-    for (int i = threadIdx.x; i < Q * 4; i += kRotThreads) dst[i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = threadIdx.x; i < Q * 4; i += NT) dst[i] = make_uint4(0u, 0u, 0u, 0u);
     if (threadIdx.x == 0) p.scale[r] = 0.f;
     return;
   }
   const int64_t src = p.rows ? p.rows[r] : r;
-  InputLoad<X32, kRotThreads> xin;
+  InputLoad<X32, NT, MAXK> xin;
   xin.issue(p.x, p.xdt, src, p.K, p.signs);
   float out_scale;
   const bool rotated = p.rotated != 0;
@@ -61,10 +63,13 @@ __global__ __launch_bounds__(kRotThreads) void k_rot16(Rot16Params p) {
   // copy the row out with 16-byte stores, dropping the 8 padding halves of every chunk
   uint4* dst = reinterpret_cast<uint4*>(p.out + r * rot16_row_halves(p.K));
   const uint4* srcv = reinterpret_cast<const uint4*>(xh);
-  for (int i = threadIdx.x; i < Q * 4; i += kRotThreads)
+  for (int i = threadIdx.x; i < Q * 4; i += NT)
     dst[i] = srcv[(i >> 2) * (kChunkHalves / 8) + (i & 3)];
   if (threadIdx.x == 0) p.scale[r] = out_scale;
 }
+
+// K up to this many elements take one wave per row
+constexpr int kRotShortK = 2048;
 
 inline size_t rot16_lds_bytes(int K, int bucket_experts) {
   const int Q = (K + 31) / 32;

@@ -185,7 +185,8 @@ def test_gather_qmv_bad_id_gives_nan_rows():
 
 
 @pytest.mark.parametrize("levels,group,K,N", [(3, 16, 2048, 96), (3, 16, 768, 160),
-                                              (16, 64, 1536, 64), (4, 32, 7168, 48)])
+                                              (16, 64, 1536, 64), (4, 32, 7168, 48),
+                                              (8, 128, 6144, 40), (4, 64, 5120, 40)])
 def test_multi_gather(levels, group, K, N):
     E = 12
     qw, _ = make_experts(916, E, N, K, levels, group, seed=1)
@@ -227,7 +228,8 @@ def routing_case(T, E, k, cfg):
 
 @pytest.mark.parametrize("levels,group,K,N", [(16, 128, 4096, 192), (16, 128, 1536, 320),
                                               (8, 64, 768, 100), (3, 16, 2048, 64),
-                                              (4, 32, 640, 130)])
+                                              (4, 32, 640, 130), (16, 64, 6144, 72),
+                                              (8, 32, 1280, 90)])
 def test_gather_qmm(levels, group, K, N):
     E, T, k = 10, 96, 3
     qw, _ = make_experts(918, E, N, K, levels, group, seed=2)
