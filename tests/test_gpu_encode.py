@@ -31,7 +31,7 @@ def test_signs(K):
         np.testing.assert_array_equal(got, (s < 0).astype(np.int64))
 
 
-@pytest.mark.parametrize("K", [64, 512, 768, 1536, 2048, 4096, 7168, 640, 96, 8192])
+@pytest.mark.parametrize("K", [64, 512, 768, 1536, 2048, 4096, 7168, 640, 96, 8192, 6144, 5120])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_fwht(K, dtype):
     g = wl.rng(900, K)

@@ -77,7 +77,7 @@ FORMATS = [(L, g) for L in (3, 4, 8, 16) for g in (16, 32, 64, 128)]
 
 
 @pytest.mark.parametrize("levels,group", FORMATS)
-@pytest.mark.parametrize("K,N", [(1536, 200), (640, 77), (7168, 64), (2048, 300)])
+@pytest.mark.parametrize("K,N", [(1536, 200), (640, 77), (7168, 64), (2048, 300), (6144, 40)])
 def test_qmv_formats(levels, group, K, N):
     g = wl.rng(910, levels * 1000 + group, K)
     W = to_dev(wl.student_rows(g, N, K), torch.bfloat16)
