@@ -26,20 +26,22 @@ __device__ __forceinline__ float dot2_h(uint32_t a, uint32_t b, float c) {
                                 false);
 }
 
-// Words of chunk c of a packed row (c must be a valid chunk; rows are 16-byte aligned for
-// 4-bit codes and 8-byte aligned for 2-bit codes because K is a multiple of 32).
+// Words of chunk c of the packed row starting `rowbyte` bytes after the expert's codes (c
+// must be a valid chunk; rows are 16-byte aligned for 4-bit codes and 8-byte aligned for
+// 2-bit codes because K is a multiple of 32).
 template <int L>
-__device__ __forceinline__ void load_chunk_words(const uint32_t* crow, int c, uint32_t (&w)[Fmt<L>::cw]) {
-  const uint32_t* p = crow + c * Fmt<L>::cw;
+__device__ __forceinline__ void load_chunk_words(const uint32_t* cexp, uint32_t rowbyte, int c,
+                                                 uint32_t (&w)[Fmt<L>::cw]) {
+  const uint32_t off = rowbyte + static_cast<uint32_t>(c) * (Fmt<L>::cw * 4);
   if constexpr (L == 16) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    const uint4 v = ld_at<uint4>(cexp, off);
     w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
   } else if constexpr (L == 4) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    const uint2 v = ld_at<uint2>(cexp, off);
     w[0] = v.x; w[1] = v.y;
   } else {
 #pragma unroll
-    for (int i = 0; i < Fmt<L>::cw; ++i) w[i] = p[i];
+    for (int i = 0; i < Fmt<L>::cw; ++i) w[i] = ld_at<uint32_t>(cexp, off + 4 * i);
   }
 }
 
@@ -48,21 +50,37 @@ __device__ __forceinline__ void load_chunk_words(const uint32_t* crow, int c, ui
 // row's last group). Each half is loaded straight into its half of the register (no
 // shift or mask after the load), so nothing waits for the load before the value is used.
 template <int L, bool G16>
-__device__ __forceinline__ half2_t load_chunk_scales(const uint16_t* srow, int c, int group, int ngroups) {
-  const _Float16* sh = reinterpret_cast<const _Float16*>(srow);
+__device__ __forceinline__ half2_t load_chunk_scales(const uint16_t* sexp, uint32_t rowbyte, int c,
+                                                     int group, int ngroups) {
   half2_t r;
   if constexpr (L == 3) {
     const int g0 = (c * 20) / group;
     const int g1 = g0 + 1 < ngroups ? g0 + 1 : g0;
-    r.x = sh[g0];
-    r.y = sh[g1];
+    r.x = ld_at<_Float16>(sexp, rowbyte + 2 * g0);
+    r.y = ld_at<_Float16>(sexp, rowbyte + 2 * g1);
   } else if constexpr (G16) {
-    r = *reinterpret_cast<const half2_t*>(sh + 2 * c);
+    r = ld_at<half2_t>(sexp, rowbyte + 4 * c);
   } else {
-    r.x = sh[(c * 32) / group];
+    r.x = ld_at<_Float16>(sexp, rowbyte + 2 * ((c * 32) / group));
     // .y unused (one group per chunk)
   }
   return r;
+}
+
+// Sum over a whole wave (lg = 6) without selects: the moves fold into the adds.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_plus(float v) {
+  const int moved = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false);
+  return v + __int_as_float(moved);
+}
+__device__ __forceinline__ float wave_sum_to_last(float v) {
+  v = dpp_plus<0xB1>(v);
+  v = dpp_plus<0x4E>(v);
+  v = dpp_plus<0x124>(v);
+  v = dpp_plus<0x128>(v);
+  v = dpp_plus<0x142, 0xA>(v);
+  v = dpp_plus<0x143, 0xC>(v);
+  return v;
 }
 
 // Sum of v over aligned segments of 2^lg lanes (lg = 0..6) with DPP lane moves (no LDS

@@ -224,4 +224,11 @@ __device__ __forceinline__ void store_any(void* p, int dt, int64_t i, float v) {
   else static_cast<uint16_t*>(p)[i] = float_to_half_rne(v);
 }
 
+// A load at a 32-bit byte offset from a uniform base: a single global load with a scalar
+// base address and a 32-bit vector offset (no 64-bit address arithmetic per lane).
+template <typename T>
+__device__ __forceinline__ T ld_at(const void* base, uint32_t byte_off) {
+  return *reinterpret_cast<const T*>(static_cast<const char*>(base) + byte_off);
+}
+
 }  // namespace tq

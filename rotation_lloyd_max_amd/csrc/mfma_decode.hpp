@@ -112,13 +112,6 @@ __device__ __forceinline__ void trit_digits81(uint32_t v, uint32_t (&q)[5]) {
   q[4] = q4;
 }
 
-// A load at a 32-bit byte offset from a uniform base: a single global load with a scalar
-// base address and a 32-bit vector offset.
-template <typename T>
-__device__ __forceinline__ T ld_at(const void* base, uint32_t byte_off) {
-  return *reinterpret_cast<const T*>(static_cast<const char*>(base) + byte_off);
-}
-
 __device__ __forceinline__ uint32_t pk_mul_h(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, a) * __builtin_bit_cast(half2_t, b));
 }

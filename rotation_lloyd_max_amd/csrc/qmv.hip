@@ -12,6 +12,9 @@ extern template hipError_t launch_qmv_l<3>(QmvParams& p, int n_slots, hipStream_
 hipError_t launch_qmv(const WeightArgs& w, const int32_t* ids, int n, const void* x, int xdt,
                       bool x_rotated, void* y, int ydt, hipStream_t s) {
   if (n == 0 || w.N == 0) return hipSuccess;
+  // the kernel addresses one expert's codes with 32-bit byte offsets and 24-bit row indices
+  if (static_cast<uint64_t>(w.N) * w.wpr * 4 > 0xffffffffull || w.N >= (1 << 24))
+    return hipErrorInvalidValue;
   QmvParams p{};
   p.codes = w.codes; p.scales = w.scales; p.signs = w.signs; p.ids = ids;
   p.x = x; p.y = y;

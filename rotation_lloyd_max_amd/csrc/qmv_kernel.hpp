@@ -74,27 +74,22 @@ struct Lane {
   int slice_q;  // chunks in this wave's slice
 };
 
-// a * b for a, b < 2^24 (row indices and row lengths, bounded on the host): two full-rate
-// 24-bit multiplies instead of 64-bit ones
-__device__ __forceinline__ uint64_t mul24_wide(uint32_t a, uint32_t b) {
-  return static_cast<uint64_t>(a & 0xffffffu) * static_cast<uint64_t>(b & 0xffffffu);
-}
-
 template <int L, int CPL, bool G16>
 __device__ __forceinline__ void qmv_load_group(GroupRegs<L, CPL>& g, const QmvParams& p,
                                                const Lane& ln, int grp, const uint32_t* cexp,
                                                const uint16_t* sexp, int ngroups_k) {
   int n = grp * ln.rows_per_group + ln.rset * ln.rpw + ln.sub;
   n = n < p.N ? n : p.N - 1;
-  const uint32_t* crow = cexp + mul24_wide(n, p.wpr);
-  const uint16_t* srow = sexp + mul24_wide(n, ngroups_k);
+  // byte offsets inside the expert (its codes are below 4 GB, checked on the host)
+  const uint32_t cbyte = __umul24(static_cast<uint32_t>(n), static_cast<uint32_t>(p.wpr)) * 4u;
+  const uint32_t sbyte = __umul24(static_cast<uint32_t>(n), static_cast<uint32_t>(ngroups_k)) * 2u;
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     int c = ln.c0 + j * ln.lpr;
     c = c < ln.slice_q ? c : ln.slice_q - 1;
     c += ln.ks * p.Qh;
-    load_chunk_words<L>(crow, c, g.w[j]);
-    g.s[j] = load_chunk_scales<L, G16>(srow, c, p.group, ngroups_k);
+    load_chunk_words<L>(cexp, cbyte, c, g.w[j]);
+    g.s[j] = load_chunk_scales<L, G16>(sexp, sbyte, c, p.group, ngroups_k);
   }
 }
 
@@ -123,7 +118,7 @@ __device__ __forceinline__ float qmv_group_sum(const GroupRegs<L, CPL>& g, const
     if constexpr (TWO) v += a1 * static_cast<float>(g.s[j].y);
     acc += cr < ln.slice_q ? v : 0.f;
   }
-  return segment_sum_flat(acc, p.lpr_log);
+  return p.lpr_log == 6 ? wave_sum_to_last(acc) : segment_sum_flat(acc, p.lpr_log);
 }
 
 // The same sum as qmv_group_sum from table entries looked up beforehand.
@@ -151,7 +146,7 @@ __device__ __forceinline__ float qmv_group_dot(const GroupRegs<L, CPL>& g, const
     if constexpr (TWO) v += a1 * static_cast<float>(g.s[j].y);
     acc += cr < ln.slice_q ? v : 0.f;
   }
-  return segment_sum_flat(acc, p.lpr_log);
+  return p.lpr_log == 6 ? wave_sum_to_last(acc) : segment_sum_flat(acc, p.lpr_log);
 }
 
 template <int L, int CPL, bool G16, bool X32, int D>
