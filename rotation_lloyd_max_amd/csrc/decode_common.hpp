@@ -34,14 +34,16 @@ __device__ __forceinline__ void load_chunk_words(const uint32_t* cexp, uint32_t 
                                                  uint32_t (&w)[Fmt<L>::cw]) {
   const uint32_t off = rowbyte + static_cast<uint32_t>(c) * (Fmt<L>::cw * 4);
   if constexpr (L == 16) {
-    const uint4 v = ld_at<uint4>(cexp, off);
+    const u32x4_t v = ld_stream<u32x4_t>(cexp, off);
     w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  } else if constexpr (L == 8) {
+    const u32x3_t v = ld_stream<u32x3_t>(cexp, off);  // one 12-byte load
+    w[0] = v.x; w[1] = v.y; w[2] = v.z;
   } else if constexpr (L == 4) {
-    const uint2 v = ld_at<uint2>(cexp, off);
+    const u32x2_t v = ld_stream<u32x2_t>(cexp, off);
     w[0] = v.x; w[1] = v.y;
   } else {
-#pragma unroll
-    for (int i = 0; i < Fmt<L>::cw; ++i) w[i] = ld_at<uint32_t>(cexp, off + 4 * i);
+    w[0] = ld_stream<uint32_t>(cexp, off);
   }
 }
 
@@ -56,12 +58,12 @@ __device__ __forceinline__ half2_t load_chunk_scales(const uint16_t* sexp, uint3
   if constexpr (L == 3) {
     const int g0 = (c * 20) / group;
     const int g1 = g0 + 1 < ngroups ? g0 + 1 : g0;
-    r.x = ld_at<_Float16>(sexp, rowbyte + 2 * g0);
-    r.y = ld_at<_Float16>(sexp, rowbyte + 2 * g1);
+    r.x = ld_stream<_Float16>(sexp, rowbyte + 2 * g0);
+    r.y = ld_stream<_Float16>(sexp, rowbyte + 2 * g1);
   } else if constexpr (G16) {
-    r = ld_at<half2_t>(sexp, rowbyte + 4 * c);
+    r = ld_stream<half2_t>(sexp, rowbyte + 4 * c);
   } else {
-    r.x = ld_at<_Float16>(sexp, rowbyte + 2 * ((c * 32) / group));
+    r.x = ld_stream<_Float16>(sexp, rowbyte + 2 * ((c * 32) / group));
     // .y unused (one group per chunk)
   }
   return r;
