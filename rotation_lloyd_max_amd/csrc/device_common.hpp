@@ -21,6 +21,9 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 // three words at a 4-byte aligned address (a 3-bit chunk): one 12-byte load
 typedef uint32_t u32x3_t __attribute__((ext_vector_type(3), aligned(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------------------
 // Rotation signs: SplitMix64 output i of the generator seeded with `seed` is

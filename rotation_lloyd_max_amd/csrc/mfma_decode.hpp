@@ -24,8 +24,6 @@
 
 namespace tq {
 
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 template <int L>
 struct Span;

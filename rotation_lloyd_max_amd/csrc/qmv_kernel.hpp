@@ -28,6 +28,7 @@
 #include "internal.hpp"
 #include "prologue.hpp"
 #include "qmv_decode.hpp"
+#include "rot_mfma.hpp"
 
 namespace tq {
 
@@ -51,9 +52,17 @@ struct QmvParams {
   int lk;         // ceil(log2(K))
   int ngroups;    // row groups per slot
   int max_iters;  // row groups per workgroup at most (sizes the slice-sum buffer)
+  int mrot;       // rotate on the matrix cores (K = 4096, 16-bit input, bit formats)
   float inv_sqrt_k;
   CodebookArgs cb;
 };
+
+// fp32 words of the kernel's row buffer: the padded row, or (rotation on the matrix cores)
+// the two bf16 terms of the transposed intermediate if they are larger.
+__host__ __device__ inline int qmv_xf_words(int K, int mrot) {
+  const int w = padded_len(K);
+  return mrot && w < 2 * kZtBytes / 4 ? 2 * kZtBytes / 4 : w;
+}
 
 // The codes and scales of one group of rows for one lane.
 template <int L, int CPL>
@@ -158,7 +167,7 @@ __global__ __launch_bounds__(kQmvThreads) void k_qmv(QmvParams p) {
   extern __shared__ uint32_t smem_u[];
   uint32_t* xh = smem_u;                                   // fp16 pairs of x', by chunk
   float* xf = reinterpret_cast<float*>(xh + p.Q * pair_stride<L>());  // padded fp32 row
-  float* red = xf + padded_len(p.K);                       // one float per wave
+  float* red = xf + qmv_xf_words(p.K, p.mrot);             // one float per wave
   uint16_t* hs = reinterpret_cast<uint16_t*>(red + kQmvWaves);  // 16 fp16 centroids
   float* rowpart = red + kQmvWaves + 8;                    // slice sums of the rows
 
@@ -181,11 +190,19 @@ __global__ __launch_bounds__(kQmvThreads) void k_qmv(QmvParams p) {
   const int slot = blockIdx.y;
   const bool last_lane = seg_sum_lane(ln.c0, p.lpr_log);
 
-  // Loads, in this order: input row and sign words, expert id (a dense layer reads none),
-  // then the first D - 1 groups' codes and scales. The rotation below waits only for the
-  // first ones while the codes stream in.
+  // bit formats: the last rotation stage writes the fp16 chunk layout directly; trit
+  // words (20 elements) are converted by a separate pass
+  constexpr bool HALF = L != 3;
+  bool mrot = false;
+  if constexpr (!X32 && HALF) mrot = p.mrot != 0;
+
+  // Loads, in this order: input row and sign words (three loads per lane either way),
+  // expert id (a dense layer reads none), then the first D - 1 groups' codes and scales.
+  // The rotation below waits only for the first ones while the codes stream in.
   InputLoad<X32, kQmvThreads> xin;
-  xin.issue(p.x, p.xdt, 0, p.K, p.signs);
+  Rot4096Mfma<kQmvThreads> mr;
+  if (mrot) mr.issue(p.x, p.xdt, p.signs);
+  else xin.issue(p.x, p.xdt, 0, p.K, p.signs);
   int e = 0;
   if (p.ids) e = p.ids[slot];
   const bool bad = e < 0 || e >= p.E;
@@ -203,33 +220,35 @@ __global__ __launch_bounds__(kQmvThreads) void k_qmv(QmvParams p) {
     qmv_load_group<L, CPL, G16>(buf[d], p, ln, g < p.ngroups ? g : grp0, cexp, sexp, ngroups_k);
   }
 
-  // the centroids reach LDS through the barrier that ends finish_a()
+  // the centroids reach LDS through the first barrier of the rotation
   if (threadIdx.x == 0) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) hs[k] = p.cb.h[k];  // uniform (scalar) loads
   }
-  // bit formats: the last rotation stage writes the fp16 chunk layout directly; trit
-  // words (20 elements) are converted by a separate pass
-  constexpr bool HALF = L != 3;
-  float out_scale;
+  // The rotation, with the table built after its first barrier (complete after its last).
+  float out_scale, sc;
   const bool rotated = p.rotated != 0;
-  const float sc = xin.template finish_a<HALF>(xf, red, p.K, p.lk, p.P, rotated, p.inv_sqrt_k,
-                                               &out_scale);
-  build_lut_v<L, kQmvThreads>(lut, hs);  // complete after the next barrier
+  if (mrot) {
+    sc = mr.rotate(reinterpret_cast<char*>(xf), red, p.lk, p.inv_sqrt_k,
+                   reinterpret_cast<_Float16*>(xh), &out_scale,
+                   [&] { build_lut_v<L, kQmvThreads>(lut, hs); });
+  } else {
+    sc = xin.template finish_a<HALF>(xf, red, p.K, p.lk, p.P, rotated, p.inv_sqrt_k,
+                                     &out_scale);
+    build_lut_v<L, kQmvThreads>(lut, hs);
+    xin.template finish_b<HALF>(xf, xh, p.K, p.m, p.P, rotated, sc);
+    if constexpr (!HALF) pairs_to_lds<L, kQmvThreads>(xf, xh, p.K, p.Q, sc);
+  }
   const float nan = __builtin_nanf("");
   const int rloc = ln.rset * ln.rpw + ln.sub;
   int grp = grp0, it = 0;
+  uint32_t xr[CPL][F::np];
+  lane_pairs<L, CPL>(xh, ln.ks * p.Qh, ln.c0, ln.lpr, ln.slice_q, xr);
   if constexpr (D == 1) {
-    // One row group per workgroup: its table lookups run between the two halves of the
-    // rotation (the codes arrived during the first), so only the products wait for x'.
-    __syncthreads();
+    // One row group per workgroup, its loads issued before the rotation.
     uint32_t cw[CPL][F::np];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) chunk_lookup<L>(buf[0].w[j], lut, lslot, cw[j]);
-    xin.template finish_b<HALF>(xf, xh, p.K, p.m, p.P, rotated, sc);
-    if constexpr (!HALF) pairs_to_lds<L, kQmvThreads>(xf, xh, p.K, p.Q, sc);
-    uint32_t xr[CPL][F::np];
-    lane_pairs<L, CPL>(xh, ln.ks * p.Qh, ln.c0, ln.lpr, ln.slice_q, xr);
     const float v = qmv_group_dot<L, CPL, G16>(buf[0], p, ln, cw, xr);
     if (KS == 1) {
       // a whole row per lane segment and no loads left: its last lane stores the result
@@ -241,11 +260,6 @@ __global__ __launch_bounds__(kQmvThreads) void k_qmv(QmvParams p) {
     if (last_lane) rowpart[rloc * KS + ln.ks] = v;
     it = 1;
   } else {
-    xin.template finish_b<HALF>(xf, xh, p.K, p.m, p.P, rotated, sc);
-    if constexpr (!HALF) pairs_to_lds<L, kQmvThreads>(xf, xh, p.K, p.Q, sc);
-    uint32_t xr[CPL][F::np];
-    lane_pairs<L, CPL>(xh, ln.ks * p.Qh, ln.c0, ln.lpr, ln.slice_q, xr);
-
     // The loop body is unrolled over U groups (a multiple of D, so the ring positions
     // repeat): inside straight-line code the compiler waits for exactly the one group it
     // computes; only the rare back edge (workgroups with more than U groups) waits longer.
@@ -331,6 +345,7 @@ hipError_t launch_qmv_l(QmvParams& p, int n_slots, hipStream_t s) {
   if (lpr_log > 6) lpr_log = 6;
   p.lpr_log = lpr_log;
   p.lk = pow2_ceil_log(p.K);
+  p.mrot = (L != 3 && p.K == 4096 && p.m == 1 && p.xdt != 0 && !p.rotated) ? 1 : 0;
   const int cpl = (p.Qh + (1 << lpr_log) - 1) >> lpr_log;  // 1 or 2
   const int rows_per_group = (kQmvWaves >> ks_log) * (64 >> lpr_log);
   p.ngroups = (p.N + rows_per_group - 1) / rows_per_group;
@@ -359,7 +374,7 @@ hipError_t launch_qmv_l(QmvParams& p, int n_slots, hipStream_t s) {
 
   const size_t rowpart = static_cast<size_t>(iters) * rows_per_group * (1 << ks_log) * 4;
   // dynamic LDS (the table is static)
-  const size_t lds = static_cast<size_t>(p.Q) * pair_stride<L>() * 4 + padded_len(p.K) * 4 +
+  const size_t lds = static_cast<size_t>(p.Q) * pair_stride<L>() * 4 + qmv_xf_words(p.K, p.mrot) * 4 +
                      (kQmvWaves + 8) * 4 + rowpart;
   if (lds + lut_bytes<L>() > 65536) {
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,

@@ -148,6 +148,27 @@ def test_qmv_large_input_and_zero_input():
     assert torch.all(y == 0)
 
 
+@pytest.mark.parametrize("levels", [4, 8, 16])
+@pytest.mark.parametrize("xdt", [torch.bfloat16, torch.float16])
+def test_qmv_k4096_16bit_inputs(levels, xdt):
+    # K = 4096 with a 16-bit input takes the matrix-core rotation: every bit format, both
+    # 16-bit types, inputs far from 1 in both directions (bf16 only: fp16 cannot hold them)
+    # and the zero input
+    K, N, group = 4096, 96, 64
+    g = wl.rng(915, levels, int(xdt == torch.float16))
+    W = to_dev(wl.student_rows(g, N, K), torch.bfloat16)
+    qw, ref = encode_both(W, levels, group, seed=5)
+    scales = (1.0, 2.0 ** -100, 2.0 ** 100) if xdt == torch.bfloat16 else (1.0, 2.0 ** -10, 2.0 ** 10)
+    for sc in scales:
+        x = to_dev(wl.gaussian(g, 1, K, outliers=8)[0] * sc, xdt)
+        y = tq.qmv(qw, x)
+        torch.cuda.synchronize()
+        check_qmv_against_oracle(qw, ref, x, y, f"L{levels} {xdt} x*{sc}")
+    y = tq.qmv(qw, torch.zeros(K, dtype=xdt, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.all(y == 0)
+
+
 def make_experts(cfg, E, N, K, levels, group, seed, dtype=torch.bfloat16):
     W = torch.stack([to_dev(wl.student_rows(wl.rng(cfg, 20, e), N, K), dtype) for e in range(E)])
     return encode_both(W, levels, group, seed)
