@@ -72,6 +72,16 @@ __device__ __forceinline__ void build_lut_v(uint32_t* lut, const uint16_t* h) {
   }
 }
 
+// The same fill by threads t = 0 .. nt - 1 of any subset of the workgroup.
+template <int L>
+__device__ __forceinline__ void build_lut_part(uint32_t* lut, const uint16_t* h, int t, int nt) {
+  constexpr int quads = Lut<L>::entries * 64 / 4;
+  for (int qi = t; qi < quads; qi += nt) {
+    const uint32_t v0 = lut_word<L>(4 * qi, h), v1 = lut_word<L>(4 * qi + 1, h);
+    reinterpret_cast<uint4*>(lut)[qi] = make_uint4(v0, v1, v0, v1);
+  }
+}
+
 __device__ __forceinline__ uint32_t lds_u32(const uint32_t* lut, uint32_t byte_addr) {
   return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(lut) + byte_addr);
 }

@@ -201,7 +201,7 @@ __global__ __launch_bounds__(kQmvThreads) void k_qmv(QmvParams p) {
   // The rotation below waits only for the first ones while the codes stream in.
   InputLoad<X32, kQmvThreads> xin;
   Rot4096Mfma<kQmvThreads> mr;
-  if (mrot) mr.issue(p.x, p.xdt, p.signs);
+  if (mrot) mr.issue(p.x, p.signs);
   else xin.issue(p.x, p.xdt, 0, p.K, p.signs);
   int e = 0;
   if (p.ids) e = p.ids[slot];
@@ -229,9 +229,15 @@ __global__ __launch_bounds__(kQmvThreads) void k_qmv(QmvParams p) {
   float out_scale, sc;
   const bool rotated = p.rotated != 0;
   if (mrot) {
-    sc = mr.rotate(reinterpret_cast<char*>(xf), red, p.lk, p.inv_sqrt_k,
-                   reinterpret_cast<_Float16*>(xh), &out_scale,
-                   [&] { build_lut_v<L, kQmvThreads>(lut, hs); });
+    // the table is built after the first barrier (the centroids reach LDS through it)
+    auto side = [&](int, int) {};
+    auto between = [&] { build_lut_v<L, kQmvThreads>(lut, hs); };
+    char* zt = reinterpret_cast<char*>(xf);
+    _Float16* xhh = reinterpret_cast<_Float16*>(xh);
+    sc = p.xdt == 1 ? mr.template rotate<true>(zt, red, p.lk, p.inv_sqrt_k, xhh, &out_scale,
+                                               side, between)
+                    : mr.template rotate<false>(zt, red, p.lk, p.inv_sqrt_k, xhh, &out_scale,
+                                                side, between);
   } else {
     sc = xin.template finish_a<HALF>(xf, red, p.K, p.lk, p.P, rotated, p.inv_sqrt_k,
                                      &out_scale);

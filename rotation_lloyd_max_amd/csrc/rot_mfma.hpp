@@ -30,6 +30,7 @@ namespace tq {
 
 // Byte a = the signs of row a of H_8: bit j set when popcount(a & j) is odd.
 constexpr uint64_t kH8Rows = 0x963C5AF066CCAA00ull;
+constexpr uint32_t kNeg2 = 0x80008000u;  // both halves negated
 
 // Sign-bit mask for the eight 16-bit values of a fragment (pairs p = 0..3) from eight sign
 // bits: bit 2p goes to bit 15 of word p, bit 2p + 1 to bit 31.
@@ -37,15 +38,17 @@ __device__ __forceinline__ uint32_t pair_sign_mask(uint32_t bits, int p) {
   return ((bits << (15 - 2 * p)) & 0x8000u) | ((bits << (30 - 2 * p)) & 0x80000000u);
 }
 
-// The eight entries H_64[r][8 g + j] (j < 8) as 16-bit +-1 pairs (one2 = the 16-bit 1.0
-// twice): row r & 7 of H_8, negated when popcount(r & 8 g) is odd.
-__device__ __forceinline__ u32x4_t h64_fragment(int r, int g8, uint32_t one2) {
-  const uint32_t bits = static_cast<uint32_t>(kH8Rows >> (8 * (r & 7))) & 0xffu;
-  const uint32_t neg = (__builtin_popcount(r & g8 & 0x38) & 1) ? 0x80008000u : 0u;
+// Row a & 7 of H_8 as four 16-bit +-1 pairs (one2 = the 16-bit 1.0 twice).
+__device__ __forceinline__ u32x4_t h8_row(int a, uint32_t one2) {
+  const uint32_t bits = static_cast<uint32_t>(kH8Rows >> (8 * (a & 7))) & 0xffu;
   u32x4_t f;
 #pragma unroll
-  for (int p = 0; p < 4; ++p) f[p] = (one2 | pair_sign_mask(bits, p)) ^ neg;
+  for (int p = 0; p < 4; ++p) f[p] = one2 | pair_sign_mask(bits, p);
   return f;
+}
+
+__device__ __forceinline__ u32x4_t xor4(const u32x4_t& v, uint32_t m) {
+  return u32x4_t{v[0] ^ m, v[1] ^ m, v[2] ^ m, v[3] ^ m};
 }
 
 __device__ __forceinline__ f32x4_t mfma_bf16(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
@@ -57,13 +60,14 @@ __device__ __forceinline__ f32x4_t mfma_h16(const u32x4_t& a, const u32x4_t& b, 
                                                 __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
-// |value| of the eight 16-bit inputs of a fragment, maximum (bf16 when bf, else fp16).
-__device__ __forceinline__ float frag_absmax(const u32x4_t& v, bool bf) {
+// max |value| of the eight 16-bit inputs of a fragment (bf16 when BF, else fp16)
+template <bool BF>
+__device__ __forceinline__ float frag_absmax(const u32x4_t& v) {
   float m = 0.f;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     float a, b;
-    if (bf) {
+    if constexpr (BF) {
       a = __uint_as_float(v[p] << 16);
       b = __uint_as_float(v[p] & 0xffff0000u);
     } else {
@@ -93,12 +97,10 @@ struct Rot4096Mfma {
   static_assert(NT == 1024, "one 16 x 16 output tile per wave of a 1024-thread workgroup");
   u32x4_t xa[2];  // X[16 t + l % 16][32 s + 8 (l / 16) + j], s = 0, 1 (16-bit, raw)
   u32x2_t sw;     // the sign words of those 64 elements of row 16 t + l % 16
-  int bf;         // bf16 input (else fp16)
 
   // Loads of the input row (16-bit, K = 4096) and its sign words: two 16-byte loads and one
   // 8-byte load per lane, every wave (waves 4..15 repeat the addresses of wave w % 4).
-  __device__ __forceinline__ void issue(const void* x, int xdt, const uint32_t* signs) {
-    bf = xdt == 1;
+  __device__ __forceinline__ void issue(const void* x, const uint32_t* signs) {
     const int lane = threadIdx.x & 63, t = (threadIdx.x >> 6) & 3;
     const int a = 16 * t + (lane & 15);
     const uint32_t e0 = 64u * a + 8u * (lane >> 4);
@@ -107,20 +109,38 @@ struct Rot4096Mfma {
     sw = ld_at<u32x2_t>(signs, 8u * a);
   }
 
-  // The whole rotation. zt: 2 kZtBytes of LDS (unused by anything else meanwhile); red: 4
-  // floats. Waves 0..3 compute Z and max |x_i|; after one barrier every wave computes its
-  // tile of X' and writes it, scaled by sc and rounded to fp16, to the chunk layout of the
-  // sink. `between` runs after the first barrier (the caller builds its tables there).
-  // Ends with a barrier. Returns sc; *out_scale gets 1 / (sc sqrt(K)).
-  template <typename F>
+  // The whole rotation (BF: bf16 input, else fp16). zt: 2 kZtBytes of LDS (unused by
+  // anything else meanwhile); red: 4 floats. Waves 0..3 compute Z and max |x_i| while
+  // waves 4..15 run side(t, nt) (thread t of nt = 768: work that needs neither x nor Z);
+  // after one barrier every wave runs between() and then computes its tile of X' and writes
+  // it, scaled by sc and rounded to fp16, to the chunk layout of the sink. Ends with a
+  // barrier. Returns sc; *out_scale gets 1 / (sc sqrt(K)).
+  //
+  // Signs of the H_64 fragments: for a lane with n = l % 16, q = l / 16 and a tile index u
+  // (the column block of Z, or the row block of X'), the fragment of row 16 u + n at columns
+  // 32 s + 8 q + j is row n & 7 of H_8 times (-1)^popcount((32 s + 8 q) & (16 u + n) & 56),
+  // and that exponent is (q & 1)(n >> 3) + (q >> 1)(u & 1) + s (u >> 1): a lane mask, a lane
+  // mask for odd u, and a sign that is uniform per instruction.
+  template <bool BF, typename Side, typename Between>
   __device__ __forceinline__ float rotate(char* zt, float* red, int lk, float inv_sqrt_k,
-                                          _Float16* xh, float* out_scale, F between) {
+                                          _Float16* xh, float* out_scale, Side side,
+                                          Between between) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, q = lane >> 4;
-    const uint32_t one2 = bf ? 0x3F803F80u : 0x3C003C00u;
+    const uint32_t m_lane = ((q & 1) & (n >> 3)) ? kNeg2 : 0u;
+    const uint32_t m_odd = (q >> 1) ? kNeg2 : 0u;
+    // second product: A = H_64[16 di + n][32 s + 8 q + j] (bf16)
+    const int di = wave >> 2, tj2 = wave & 3;
+    u32x4_t a2[2];
+    {
+      const u32x4_t h = xor4(h8_row(n, 0x3F803F80u), m_lane ^ ((di & 1) ? m_odd : 0u));
+      a2[0] = h;
+      a2[1] = xor4(h, (di >> 1) ? kNeg2 : 0u);
+    }
     if (wave < 4) {
       const int t = wave;
-      float mx = fmaxf(frag_absmax(xa[0], bf), frag_absmax(xa[1], bf));
+      const u32x4_t b0 = xor4(h8_row(n, BF ? 0x3F803F80u : 0x3C003C00u), m_lane);
+      const u32x4_t b1 = xor4(b0, m_odd);
       u32x4_t xs[2];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -128,26 +148,33 @@ struct Rot4096Mfma {
 #pragma unroll
         for (int p = 0; p < 4; ++p) xs[s][p] = xa[s][p] ^ pair_sign_mask(bits, p);
       }
+      float mx = fmaxf(frag_absmax<BF>(xa[0]), frag_absmax<BF>(xa[1]));
+      // Z[16 t + m][16 tj + c] = sum_b X[16 t + m][b] H_64[b][16 tj + c]: B is the fragment
+      // of row 16 tj + n of the symmetric H_64; four independent accumulators
+      f32x4_t acc[4];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int tj = 0; tj < 4; ++tj) {
+          const u32x4_t b = xor4((tj & 1) ? b1 : b0, (s && (tj >> 1)) ? kNeg2 : 0u);
+          const f32x4_t c = s ? acc[tj] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+          acc[tj] = BF ? mfma_bf16(xs[s], b, c) : mfma_h16(xs[s], b, c);
+        }
 #pragma unroll
       for (int tj = 0; tj < 4; ++tj) {
-        // B = H_64[32 s + 8 q + j][16 tj + n]; H is symmetric, so this is the fragment of
-        // row 16 tj + n at columns 32 s + 8 q + j
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const u32x4_t h = h64_fragment(16 * tj + n, 32 * s + 8 * q, one2);
-          acc = bf ? mfma_bf16(xs[s], h, acc) : mfma_h16(xs[s], h, acc);
-        }
-        // acc[r] = Z[16 t + 4 q + r][16 tj + n] -> Zt row 16 tj + n, columns 16 t + 4 q + r
-        const uint32_t h01 = pack_bf16x2(acc[0], acc[1]), h23 = pack_bf16x2(acc[2], acc[3]);
-        const uint32_t l01 = pack_bf16x2(acc[0] - bf16_lo_f(h01), acc[1] - bf16_hi_f(h01));
-        const uint32_t l23 = pack_bf16x2(acc[2] - bf16_lo_f(h23), acc[3] - bf16_hi_f(h23));
+        // acc[tj][r] = Z[16 t + 4 q + r][16 tj + n] -> Zt row 16 tj + n, column 16 t + 4 q + r
+        const f32x4_t z = acc[tj];
+        const uint32_t h01 = pack_bf16x2(z[0], z[1]), h23 = pack_bf16x2(z[2], z[3]);
+        const uint32_t l01 = pack_bf16x2(z[0] - bf16_lo_f(h01), z[1] - bf16_hi_f(h01));
+        const uint32_t l23 = pack_bf16x2(z[2] - bf16_lo_f(h23), z[3] - bf16_hi_f(h23));
         const uint32_t off = (16 * tj + n) * kZtRowBytes + (16 * t + 4 * q) * 2;
         *reinterpret_cast<u32x2_t*>(zt + off) = u32x2_t{h01, h23};
         *reinterpret_cast<u32x2_t*>(zt + kZtBytes + off) = u32x2_t{l01, l23};
       }
       mx = wave_max_nonneg(mx);
       if (lane == 63) red[t] = mx;
+    } else {
+      side(static_cast<int>(threadIdx.x) - 256, NT - 256);
     }
     __syncthreads();
     between();
@@ -161,22 +188,20 @@ struct Rot4096Mfma {
     const float sc = ldexpf(1.f, ex);
 
     // X'[16 di + m][16 tj + c] = sum_a H_64[16 di + m][a] Z[a][16 tj + c]
-    const int di = wave >> 2, tj = wave & 3;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const u32x4_t h = h64_fragment(16 * di + n, 32 * s + 8 * q, 0x3F803F80u);
-      const uint32_t off = (16 * tj + n) * kZtRowBytes + (32 * s + 8 * q) * 2;
+      const uint32_t off = (16 * tj2 + n) * kZtRowBytes + (32 * s + 8 * q) * 2;
       const u32x4_t zh = *reinterpret_cast<const u32x4_t*>(zt + off);
       const u32x4_t zl = *reinterpret_cast<const u32x4_t*>(zt + kZtBytes + off);
-      acc = mfma_bf16(h, zh, acc);
-      acc = mfma_bf16(h, zl, acc);
+      acc = mfma_bf16(a2[s], zh, acc);
+      acc = mfma_bf16(a2[s], zl, acc);
     }
     // acc[r] = x'_e, e = 64 (16 di + 4 q + r) + 16 tj + n
     const HalfSink sink{xh, sc};
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int e = 64 * (16 * di + 4 * q + r) + 16 * tj + n;
+      const int e = 64 * (16 * di + 4 * q + r) + 16 * tj2 + n;
       sink.put_at(HalfSink::idx(e), acc[r]);
     }
     __syncthreads();
