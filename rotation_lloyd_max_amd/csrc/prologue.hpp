@@ -18,8 +18,8 @@ namespace tq {
 constexpr int kMaxK = 8192;
 
 // X32: the input is fp32; otherwise a 16-bit type, bf16 or fp16 by the runtime dtype.
-// All loads are unconditional (indices are clamped) so that no branch separates them from
-// the loads the caller issues next, and the compiler can wait for exactly these.
+// Inside a wave the loads are unconditional (indices are clamped); a wave none of whose
+// lanes has a segment skips them.
 template <bool X32, int NT, int MAXK = kMaxK>
 struct InputLoad {
   static constexpr int kSeg16 = (MAXK / 16 + NT - 1) / NT;  // 16-element segments per thread
@@ -38,6 +38,8 @@ struct InputLoad {
 #pragma unroll
     for (int j = 0; j < kSeg16; ++j) {
       int sgi = threadIdx.x + NT * j;
+      // a wave with no segment here issues no load (finish_a() skips such segments)
+      if ((static_cast<int>(threadIdx.x) & ~63) + NT * j >= nseg) continue;
       sgi = sgi < nseg ? sgi : nseg - 1;
       const int64_t e0 = row * K + 16 * static_cast<int64_t>(sgi);
       const uint4* q = X32 ? reinterpret_cast<const uint4*>(static_cast<const float*>(x) + e0)

@@ -99,9 +99,11 @@ struct Rot4096Mfma {
   u32x2_t sw;     // the sign words of those 64 elements of row 16 t + l % 16
 
   // Loads of the input row (16-bit, K = 4096) and its sign words: two 16-byte loads and one
-  // 8-byte load per lane, every wave (waves 4..15 repeat the addresses of wave w % 4).
+  // 8-byte load per lane of waves 0..3, the only ones that use them (the other waves issue
+  // nothing here: loads they would not use only slow the issue of the code loads).
   __device__ __forceinline__ void issue(const void* x, const uint32_t* signs) {
-    const int lane = threadIdx.x & 63, t = (threadIdx.x >> 6) & 3;
+    if (threadIdx.x >= 256) return;
+    const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
     const int a = 16 * t + (lane & 15);
     const uint32_t e0 = 64u * a + 8u * (lane >> 4);
     xa[0] = ld_at<u32x4_t>(x, 2u * e0);
