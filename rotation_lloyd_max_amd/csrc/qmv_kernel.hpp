@@ -158,6 +158,55 @@ __device__ __forceinline__ float qmv_group_dot(const GroupRegs<L, CPL>& g, const
   return p.lpr_log == 6 ? wave_sum_to_last(acc) : segment_sum_flat(acc, p.lpr_log);
 }
 
+// The input row of a qmv workgroup: its loads (issued first) and its rotation into the fp16
+// chunk layout xh, by the butterflies of prologue.hpp or, for K = 4096 and a 16-bit input,
+// on the matrix cores (rot_mfma.hpp). The centroid table is built on the way: it is
+// complete when rotate() returns.
+template <int L, bool X32>
+struct QmvInput {
+  static constexpr bool HALF = L != 3;  // bit formats: the rotation writes xh directly
+  InputLoad<X32, kQmvThreads> xin;
+  Rot4096Mfma<kQmvThreads> mr;
+  bool mrot;
+
+  // three loads per lane at most
+  __device__ __forceinline__ void issue(const QmvParams& p) {
+    mrot = false;
+    if constexpr (!X32 && HALF) mrot = p.mrot != 0;
+    if (mrot) mr.issue(p.x, p.signs);
+    else xin.issue(p.x, p.xdt, 0, p.K, p.signs);
+  }
+
+  // Returns sc (x' in xh is sc times the rotated input, rounded to fp16); *out_scale gets
+  // 1 / (sc sqrt(K)) (1 / sc for a rotated input). Ends synchronized.
+  __device__ __forceinline__ float rotate(const QmvParams& p, uint32_t* lut, uint32_t* xh,
+                                         float* xf, float* red, uint16_t* hs, float* out_scale) {
+    // the centroids reach LDS through the first barrier of the rotation
+    if (threadIdx.x == 0) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) hs[k] = p.cb.h[k];  // uniform (scalar) loads
+    }
+    if (mrot) {
+      // the table is built after the first barrier (the centroids reach LDS through it)
+      auto side = [&](int, int) {};
+      auto between = [&] { build_lut_v<L, kQmvThreads>(lut, hs); };
+      char* zt = reinterpret_cast<char*>(xf);
+      _Float16* xhh = reinterpret_cast<_Float16*>(xh);
+      return p.xdt == 1 ? mr.template rotate<true>(zt, red, p.lk, p.inv_sqrt_k, xhh, out_scale,
+                                                   side, between)
+                        : mr.template rotate<false>(zt, red, p.lk, p.inv_sqrt_k, xhh, out_scale,
+                                                    side, between);
+    }
+    const bool rotated = p.rotated != 0;
+    const float sc = xin.template finish_a<HALF>(xf, red, p.K, p.lk, p.P, rotated,
+                                                 p.inv_sqrt_k, out_scale);
+    build_lut_v<L, kQmvThreads>(lut, hs);
+    xin.template finish_b<HALF>(xf, xh, p.K, p.m, p.P, rotated, sc);
+    if constexpr (!HALF) pairs_to_lds<L, kQmvThreads>(xf, xh, p.K, p.Q, sc);
+    return sc;
+  }
+};
+
 template <int L, int CPL, bool G16, bool X32, int D>
 __global__ __launch_bounds__(kQmvThreads) void k_qmv(QmvParams p) {
   using F = Fmt<L>;
@@ -190,19 +239,11 @@ __global__ __launch_bounds__(kQmvThreads) void k_qmv(QmvParams p) {
   const int slot = blockIdx.y;
   const bool last_lane = seg_sum_lane(ln.c0, p.lpr_log);
 
-  // bit formats: the last rotation stage writes the fp16 chunk layout directly; trit
-  // words (20 elements) are converted by a separate pass
-  constexpr bool HALF = L != 3;
-  bool mrot = false;
-  if constexpr (!X32 && HALF) mrot = p.mrot != 0;
-
-  // Loads, in this order: input row and sign words (three loads per lane either way),
-  // expert id (a dense layer reads none), then the first D - 1 groups' codes and scales.
-  // The rotation below waits only for the first ones while the codes stream in.
-  InputLoad<X32, kQmvThreads> xin;
-  Rot4096Mfma<kQmvThreads> mr;
-  if (mrot) mr.issue(p.x, p.signs);
-  else xin.issue(p.x, p.xdt, 0, p.K, p.signs);
+  // Loads, in this order: input row and sign words, expert id (a dense layer reads none),
+  // then the first D - 1 groups' codes and scales. The rotation below waits only for the
+  // first ones while the codes stream in.
+  QmvInput<L, X32> in;
+  in.issue(p);
   int e = 0;
   if (p.ids) e = p.ids[slot];
   const bool bad = e < 0 || e >= p.E;
@@ -220,31 +261,8 @@ __global__ __launch_bounds__(kQmvThreads) void k_qmv(QmvParams p) {
     qmv_load_group<L, CPL, G16>(buf[d], p, ln, g < p.ngroups ? g : grp0, cexp, sexp, ngroups_k);
   }
 
-  // the centroids reach LDS through the first barrier of the rotation
-  if (threadIdx.x == 0) {
-#pragma unroll
-    for (int k = 0; k < 16; ++k) hs[k] = p.cb.h[k];  // uniform (scalar) loads
-  }
-  // The rotation, with the table built after its first barrier (complete after its last).
-  float out_scale, sc;
-  const bool rotated = p.rotated != 0;
-  if (mrot) {
-    // the table is built after the first barrier (the centroids reach LDS through it)
-    auto side = [&](int, int) {};
-    auto between = [&] { build_lut_v<L, kQmvThreads>(lut, hs); };
-    char* zt = reinterpret_cast<char*>(xf);
-    _Float16* xhh = reinterpret_cast<_Float16*>(xh);
-    sc = p.xdt == 1 ? mr.template rotate<true>(zt, red, p.lk, p.inv_sqrt_k, xhh, &out_scale,
-                                               side, between)
-                    : mr.template rotate<false>(zt, red, p.lk, p.inv_sqrt_k, xhh, &out_scale,
-                                                side, between);
-  } else {
-    sc = xin.template finish_a<HALF>(xf, red, p.K, p.lk, p.P, rotated, p.inv_sqrt_k,
-                                     &out_scale);
-    build_lut_v<L, kQmvThreads>(lut, hs);
-    xin.template finish_b<HALF>(xf, xh, p.K, p.m, p.P, rotated, sc);
-    if constexpr (!HALF) pairs_to_lds<L, kQmvThreads>(xf, xh, p.K, p.Q, sc);
-  }
+  float out_scale;
+  in.rotate(p, lut, xh, xf, red, hs, &out_scale);
   const float nan = __builtin_nanf("");
   const int rloc = ln.rset * ln.rpw + ln.sub;
   int grp = grp0, it = 0;
@@ -342,6 +360,8 @@ template <int L>
 hipError_t launch_qmv_l(QmvParams& p, int n_slots, hipStream_t s) {
   using F = Fmt<L>;
   p.Q = (p.wpr + F::cw - 1) / F::cw;
+  p.lk = pow2_ceil_log(p.K);
+  p.mrot = (L != 3 && p.K == 4096 && p.m == 1 && p.xdt != 0 && !p.rotated) ? 1 : 0;
   // K-slices: at most two chunks of each row per lane
   int ks_log = 0;
   while (((p.Q + (1 << ks_log) - 1) >> ks_log) > 128) ++ks_log;
@@ -350,8 +370,6 @@ hipError_t launch_qmv_l(QmvParams& p, int n_slots, hipStream_t s) {
   int lpr_log = pow2_ceil_log(p.Qh);
   if (lpr_log > 6) lpr_log = 6;
   p.lpr_log = lpr_log;
-  p.lk = pow2_ceil_log(p.K);
-  p.mrot = (L != 3 && p.K == 4096 && p.m == 1 && p.xdt != 0 && !p.rotated) ? 1 : 0;
   const int cpl = (p.Qh + (1 << lpr_log) - 1) >> lpr_log;  // 1 or 2
   const int rows_per_group = (kQmvWaves >> ks_log) * (64 >> lpr_log);
   p.ngroups = (p.N + rows_per_group - 1) / rows_per_group;

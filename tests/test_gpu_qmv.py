@@ -169,6 +169,41 @@ def test_qmv_k4096_16bit_inputs(levels, xdt):
     assert torch.all(y == 0)
 
 
+@pytest.mark.parametrize("levels", [4, 8, 16])
+@pytest.mark.parametrize("K,N,xdt", [(2048, 333, torch.float32), (4096, 250, torch.bfloat16),
+                                     (4096, 77, torch.float16), (8192, 96, torch.bfloat16),
+                                     (2048, 1000, torch.float16)])
+def test_qmv_power_of_two_k_group_128(levels, K, N, xdt):
+    # groups of 128 with K in {2048, 4096, 8192}: every bit format and input type, row counts
+    # that are not a multiple of the rows a workgroup takes
+    g = wl.rng(916, levels, K + N)
+    W = to_dev(wl.student_rows(g, N, K), torch.bfloat16)
+    qw, ref = encode_both(W, levels, 128, seed=6)
+    x = to_dev(wl.gaussian(g, 1, K, outliers=4)[0], xdt)
+    y = tq.qmv(qw, x)
+    torch.cuda.synchronize()
+    check_qmv_against_oracle(qw, ref, x, y, f"L{levels} K{K} N{N} {xdt}")
+
+
+def test_gather_qmv_k4096_bad_ids():
+    # several experts at K = 4096 (rotation on the matrix cores), slots with ids out of range
+    # (NaN rows)
+    E, N, K, levels = 5, 40, 4096, 8
+    qw, ref = make_experts(917, E, N, K, levels, 128, seed=3)
+    ids_np = np.array([4, 0, E, 2, -1, 1], dtype=np.int32)
+    x = to_dev(wl.gaussian(wl.rng(917, 1), 1, K)[0], torch.bfloat16)
+    y = tq.gather_qmv(qw, torch.from_numpy(ids_np).cuda(), x)
+    torch.cuda.synchronize()
+    codes, scales = gpu_arrays(qw)
+    yg, xf = as_f64(y), as_f64(x)
+    for k, e in enumerate(ids_np):
+        if 0 <= e < E:
+            want, bound = qmv_reference(codes[e], scales[e], levels, 128, K, 3, xf)
+            check_outputs(yg[k], want, bound, f"slot {k} expert {e}")
+        else:
+            assert np.all(np.isnan(yg[k])), k
+
+
 def make_experts(cfg, E, N, K, levels, group, seed, dtype=torch.bfloat16):
     W = torch.stack([to_dev(wl.student_rows(wl.rng(cfg, 20, e), N, K), dtype) for e in range(E)])
     return encode_both(W, levels, group, seed)
