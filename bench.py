@@ -85,8 +85,8 @@ def cpu_baseline_qmv(W_bits, x_bits, levels, group, seed, budget_s=12.0, rows=51
 
 
 QMV_SOURCES = ["qmv.hip", "qmv_16.hip", "qmv_8.hip", "qmv_4.hip", "qmv_3.hip", "qmv_kernel.hpp",
-               "qmv_decode.hpp", "prologue.hpp", "decode_common.hpp", "fwht_block.hpp",
-               "device_common.hpp", "internal.hpp"]
+               "qmv_decode.hpp", "rot_mfma.hpp", "prologue.hpp", "decode_common.hpp",
+               "fwht_block.hpp", "device_common.hpp", "internal.hpp"]
 
 
 def recorded_traffic(profile, sources):
