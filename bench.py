@@ -19,8 +19,8 @@ not in the timed region.
   cpu_baseline  the fp64 oracle (numpy, one BLAS thread) on a bounded sample of the same
           layer, in the same unit
 
-Other workloads (--config 3, 4, 5) time gather_qmv, multi_gather_qmv and gather_qmm for
-reference; the default line is the dense decode layer.
+Other workloads (--config 3, 4, 5, 6) time gather_qmv, multi_gather_qmv, gather_qmm and
+dequant for reference; the default line is the dense decode layer.
 """
 
 import argparse
@@ -41,7 +41,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5, 6],
+                    help="2 dense qmv (default), 3 gather_qmv, 4 multi_gather_qmv, "
+                         "5 gather_qmm, 6 dequant of an expert stack")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calls", type=int, default=1000, help="qmv calls per step")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -367,6 +369,73 @@ def bench_moe(args):
     }
 
 
+def bench_dequant(args):
+    """dequant of the batched-MoE gate stack (128 experts x 1536 x 4096, 4-bit g128) to bf16:
+    codes and scales read once, the decoded weights written once, per step."""
+    import numpy as np
+    import torch
+    import rotation_lloyd_max_amd as tq
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    c = wl.C5
+    pr = c.projs[0]
+    qw = encode_stack(c.E, pr.N, pr.K, pr.levels, pr.group, pr.seed, c.cid,
+                      wl.PROJ_TENSOR[pr.name], dev)
+    out = torch.empty((c.E, pr.N, pr.K), dtype=torch.bfloat16, device=dev)
+    tq.dequant(qw, out=out)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        tq.dequant(qw, out=out)
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for _ in range(args.steps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = a.elapsed_time(b) / args.steps
+    read = qw.codes.numel() * 4 + qw.scales.numel() * 2
+    written = out.numel() * 2
+    value = (read + written) / (ms / 1e3) / 1e9
+    res = {
+        "metric": "dequant HBM GB/s (expert stack to bf16: codes and scales read, weights "
+                  "written)",
+        "value": round(value, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32 product -> bf16",
+        "data": "synthetic",
+        "config": {"workload": "dequant of the batched-MoE gate stack: 128 experts x 1536 x "
+                               "4096, 4-bit Lloyd-Max g128 -> bf16", "bytes_per_step": read + written},
+        "wall_s": round(wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(value, 3), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+        from oracle import encode as oenc
+        codes = qw.codes[0].cpu().numpy().view(np.uint32)
+        scales = qw.scales[0].view(torch.int16).cpu().numpy().view(np.uint16)
+        with threadpool_limits(1):
+            t = time.perf_counter()
+            n = 0
+            while n == 0 or time.perf_counter() - t < 10.0:
+                oenc.dequant(codes, scales, pr.levels, pr.group, pr.K)
+                n += 1
+            dt = (time.perf_counter() - t) / n
+        b1 = codes.size * 4 + scales.size * 2 + pr.N * pr.K * 2
+        res["cpu_baseline"] = {"value": round(b1 / dt / 1e9, 6), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"oracle (numpy fp64, 1 BLAS thread) dequant of expert 0 "
+                                         f"({pr.N} x {pr.K}), {n} calls in {dt * n:.1f} s"}
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -385,6 +454,8 @@ def main():
         out = copy_calibration(args.copy_calibration)
     elif args.config == 2:
         out = bench_dense(args)
+    elif args.config == 6:
+        out = bench_dequant(args)
     else:
         out = bench_moe(args)
     print(json.dumps(out), flush=True)

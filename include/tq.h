@@ -160,6 +160,17 @@ int tq_gather_qmm(const tq_qweight *w, const void *x, tq_dtype x_dtype, int64_t 
                   const int32_t *row_token, const int32_t *expert_offsets, int64_t M, void *y,
                   tq_dtype y_dtype, uint32_t flags, void *ws, size_t ws_bytes, void *stream);
 
+/* Decoded weights of n experts in the rotated basis, for the shapes of work the fused
+ * kernels above do not cover ("Running a quantized layer", kernel table, fourth row:
+ * dequantize the experts, then a regular matrix multiply):
+ *   out[k][i][j] = scale[e][i][j / group] * c[idx[e][i][j]],  e = ids[k] (k if ids is NULL),
+ * the fp32 centroid times the fp16 scale, rounded once to out_dtype, so that out[k] times
+ * the rotated input (tq_fwht) is W_e R x up to rounding. ids: device int32 [n], or NULL with
+ * n <= E. out: device [n][N][K], aligned to 16 bytes. An id outside [0, E) yields a block of
+ * NaN. n must be at most 65535. Workspace: none. */
+int tq_dequant(const tq_qweight *w, const int32_t *ids, int64_t n, void *out,
+               tq_dtype out_dtype, void *stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char *tq_last_error(void);
 

@@ -67,6 +67,7 @@ SIGNATURES = [
      [_QW, _P, _I64, _P, ctypes.c_int, _P, ctypes.c_int, _U32, _P, _SZ, _P]),
     ("tq_gather_qmm", ctypes.c_int,
      [_QW, _P, ctypes.c_int, _I64, _P, _P, _I64, _P, ctypes.c_int, _U32, _P, _SZ, _P]),
+    ("tq_dequant", ctypes.c_int, [_QW, _P, _I64, _P, ctypes.c_int, _P]),
     ("tq_last_error", ctypes.c_char_p, []),
 ]
 
@@ -200,6 +201,21 @@ def qmv(qw, x, out_dtype=torch.float32, rotated=False, out=None):
     _check(lib().tq_qmv(ctypes.byref(d), _ptr(x), _dt(x), _ptr(y), _dt(y),
                         X_ROTATED if rotated else 0, None, 0, _stream()))
     return y
+
+
+def dequant(qw, ids=None, out_dtype=torch.bfloat16, out=None):
+    """Decoded weights [n][N][K] of experts ids (all E when None), in the rotated basis."""
+    if ids is not None:
+        ids = ids.to(torch.int32).contiguous()
+        n = ids.numel()
+    else:
+        n = qw.E
+    dev = qw.codes.device
+    w = out if out is not None else torch.empty((n, qw.N, qw.K), dtype=out_dtype, device=dev)
+    d = qw.desc()
+    _check(lib().tq_dequant(ctypes.byref(d), _ptr(ids) if ids is not None else None, n,
+                            _ptr(w), _dt(w), _stream()))
+    return w
 
 
 def gather_qmv(qw, ids, x, out_dtype=torch.float32, rotated=False, out=None):

@@ -13,7 +13,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtq.so")
 
 SOURCES = ["tq_api.cpp", "rotate.hip", "encode.hip", "qmv.hip", "qmv_16.hip", "qmv_8.hip",
-           "qmv_4.hip", "qmv_3.hip", "rot16.hip", "multi_gather.hip", "gather_qmm.hip"]
+           "qmv_4.hip", "qmv_3.hip", "rot16.hip", "multi_gather.hip", "gather_qmm.hip",
+           "dequant.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",

@@ -42,6 +42,10 @@ hipError_t launch_encode(const void* W, int wdt, int64_t rows, int K, int m, int
                          uint16_t* scales, hipStream_t s);
 
 // qmv (ids == nullptr, n = 1) and gather_qmv.
+// out[k] = decoded weights of expert ids[k] (k when ids is null) in the rotated basis.
+hipError_t launch_dequant(const WeightArgs& w, const int32_t* ids, int n, void* out, int odt,
+                          hipStream_t s);
+
 hipError_t launch_qmv(const WeightArgs& w, const int32_t* ids, int n, const void* x, int xdt,
                       bool x_rotated, void* y, int ydt, hipStream_t s);
 

@@ -318,6 +318,23 @@ int tq_multi_gather_qmv(const tq_qweight* w, const int32_t* ids, int64_t P, cons
                     "tq_multi_gather_qmv");
 }
 
+int tq_dequant(const tq_qweight* w, const int32_t* ids, int64_t n, void* out,
+               tq_dtype out_dtype, void* stream) {
+  WeightArgs a{};
+  int rc = check_weight(w, &a);
+  if (rc != TQ_OK) return rc;
+  if (!valid_dtype(out_dtype)) return fail(TQ_ERR_ARG, "bad dtype");
+  if (n < 0 || n > 65535) return fail(TQ_ERR_ARG, "n must be in [0, 65535]");
+  if (!ids && n > a.E) return fail(TQ_ERR_ARG, "without ids n must be at most E");
+  if (n == 0 || a.N == 0) return TQ_OK;
+  if (ids && !aligned(ids, 4)) return fail(TQ_ERR_ALIGN, "ids misaligned");
+  if (!out) return fail(TQ_ERR_ARG, "out is NULL");
+  if (!aligned(out, 16)) return fail(TQ_ERR_ALIGN, "out must be 16-byte aligned");
+  return hip_status(launch_dequant(a, ids, static_cast<int>(n), out, out_dtype,
+                                   static_cast<hipStream_t>(stream)),
+                    "tq_dequant");
+}
+
 int tq_gather_qmm(const tq_qweight* w, const void* x, tq_dtype x_dtype, int64_t T,
                   const int32_t* row_token, const int32_t* expert_offsets, int64_t M, void* y,
                   tq_dtype y_dtype, uint32_t flags, void* ws, size_t ws_bytes, void* stream) {

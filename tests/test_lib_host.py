@@ -35,7 +35,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     handle = ctypes.CDLL(tq.LIB_PATH)
     for n in names:
         assert hasattr(handle, n), n
@@ -106,6 +106,12 @@ def test_validation_statuses():
                            None) == ERR_WORKSPACE
     assert L.tq_gather_qmm(ctypes.byref(d), 16, 1, 50, 16, 16, 100, 16, 0, 0, 128, need,
                            None) == ERR_ALIGN
+    # dequant: more blocks than experts without ids, misaligned output, bad dtype, bad n
+    assert L.tq_dequant(ctypes.byref(d), None, 5, 256, 1, None) == ERR_ARG
+    assert L.tq_dequant(ctypes.byref(d), None, 2, 258, 1, None) == ERR_ALIGN
+    assert L.tq_dequant(ctypes.byref(d), 16, 2, 256, 7, None) == ERR_ARG
+    assert L.tq_dequant(ctypes.byref(d), 16, 70000, 256, 1, None) == ERR_ARG
+    assert L.tq_dequant(ctypes.byref(d), 18, 2, 256, 1, None) == ERR_ALIGN
     # encode / fwht / signs
     assert L.tq_encode(16, 0, 4, 500, 16, 64, 0, 16, 16, None) == ERR_UNSUPPORTED
     assert L.tq_encode(0, 0, 4, 512, 16, 64, 0, 16, 16, None) == ERR_ARG
@@ -128,3 +134,4 @@ def test_empty_calls_are_no_ops():
     assert L.tq_gather_qmv(ctypes.byref(d), None, 0, 0, 1, 0, 0, 0, None, 0, None) == 0
     assert L.tq_multi_gather_qmv(ctypes.byref(d), None, 0, 0, 1, 0, 0, 0, None, 0, None) == 0
     assert L.tq_gather_qmm(ctypes.byref(d), 0, 1, 0, None, None, 0, 0, 0, 0, None, 0, None) == 0
+    assert L.tq_dequant(ctypes.byref(d), None, 0, None, 1, None) == 0
