@@ -6,9 +6,10 @@
 // out[k][i][j] = scale(ids[k], i, j / group) * c[idx(ids[k], i, j)]: the fp32 centroid times
 // the fp16 scale in fp32, rounded once to the output type. One thread per chunk of a row
 // (32 elements, or one 20-trit word): the chunk's words and scales are read with
-// nontemporal loads (read once) and its outputs written with 8- or 16-byte stores, so a
-// wave writes whole contiguous runs of the output row. The work is bound by the output
-// bytes (2 or 4 per weight against 0.2..0.6 read).
+// nontemporal loads (read once); a wave's outputs, one contiguous block of the row, leave
+// through an LDS exchange so that each store instruction writes 1 KB of consecutive bytes
+// (plain stores: with the nontemporal hint the kernel measured a third slower). The work
+// is bound by the output bytes (2 or 4 per weight against 0.2..0.6 read).
 #include "decode_common.hpp"
 #include "internal.hpp"
 
@@ -25,12 +26,6 @@ struct DequantParams {
   int K, N, E, wpr, group, ngk, Q;
   CodebookArgs cb;
 };
-
-// Plain stores: with the nontemporal hint the kernel measured a third slower.
-template <typename T>
-__device__ __forceinline__ void store_vec(T* p, T v) {
-  *p = v;
-}
 
 template <int L>
 __device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[Fmt<L>::cw], int j) {
@@ -90,33 +85,77 @@ __global__ __launch_bounds__(kDeqThreads) void k_dequant(DequantParams p) {
   // elements of the chunk inside the row: all of them, except in a row's last trit word
   // (K is a multiple of 32, so the count is a multiple of 4)
   const int cnt = p.K - e0 < CE ? p.K - e0 : CE;
-  if constexpr (ODT == 0) {
-    // fp32: 16-byte stores at 16-byte aligned offsets (K and e0 are multiples of 4)
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(static_cast<float*>(p.out) + o);
+  // the output of the chunk as 16-byte units (bit formats: 4 for 16-bit types, 8 for fp32)
+  constexpr int BYTES = CE * (ODT == 0 ? 4 : 2);
+  if constexpr (BYTES % 16 == 0) {
+    constexpr int U = BYTES / 16;
+    u32x4_t u[U];
 #pragma unroll
-    for (int q = 0; q < CE / 4; ++q)
-      if (4 * q < cnt)
-        store_vec(dst + q, u32x4_t{__float_as_uint(v[4 * q]), __float_as_uint(v[4 * q + 1]),
-                                   __float_as_uint(v[4 * q + 2]), __float_as_uint(v[4 * q + 3])});
-  } else {
-    uint32_t h[CE / 2];
+    for (int q = 0; q < U; ++q) {
+      if constexpr (ODT == 0) {
+        u[q] = u32x4_t{__float_as_uint(v[4 * q]), __float_as_uint(v[4 * q + 1]),
+                       __float_as_uint(v[4 * q + 2]), __float_as_uint(v[4 * q + 3])};
+      } else {
+        uint32_t h[4];
 #pragma unroll
-    for (int q = 0; q < CE / 2; ++q) {
-      const uint16_t a = ODT == 1 ? float_to_bf16_rne(v[2 * q]) : float_to_half_rne(v[2 * q]);
-      const uint16_t b = ODT == 1 ? float_to_bf16_rne(v[2 * q + 1]) : float_to_half_rne(v[2 * q + 1]);
-      h[q] = static_cast<uint32_t>(a) | (static_cast<uint32_t>(b) << 16);
+        for (int r = 0; r < 4; ++r) {
+          const float a = v[8 * q + 2 * r], b = v[8 * q + 2 * r + 1];
+          const uint16_t ha = ODT == 1 ? float_to_bf16_rne(a) : float_to_half_rne(a);
+          const uint16_t hb = ODT == 1 ? float_to_bf16_rne(b) : float_to_half_rne(b);
+          h[r] = static_cast<uint32_t>(ha) | (static_cast<uint32_t>(hb) << 16);
+        }
+        u[q] = u32x4_t{h[0], h[1], h[2], h[3]};
+      }
     }
-    uint16_t* base = static_cast<uint16_t*>(p.out) + o;
-    if constexpr (CE % 8 == 0) {
-      u32x4_t* dst = reinterpret_cast<u32x4_t*>(base);  // 64 bytes, 16-byte aligned
+    // When the wave's 64 chunks are consecutive chunks of one row, their outputs are one
+    // contiguous block of 64 U units: exchange them through LDS so that every store
+    // instruction of the wave writes 1 KB of consecutive bytes (measured a third faster
+    // than each lane storing its own 64 or 128 bytes). Units are padded by one per 64 so
+    // that both sides of the exchange are free of bank conflicts.
+    const int lane = threadIdx.x & 63;
+    const int64_t c0 = chunk - lane;
+    // (a block ending with a partial last trit word of its row takes the per-lane path)
+    const bool block = c0 + 63 < p.chunks && c0 / p.Q == (c0 + 63) / p.Q &&
+                       (L != 3 || (c0 + 63) % p.Q != p.Q - 1 || p.K % CE == 0);
+    if (block) {
+      __shared__ u32x4_t xch[kDeqThreads / 64][64 * U + U];
+      u32x4_t* wx = xch[threadIdx.x >> 6];
 #pragma unroll
-      for (int q = 0; q < CE / 8; ++q)
-        store_vec(dst + q, u32x4_t{h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]});
+      for (int q = 0; q < U; ++q) {
+        const int pos = U * lane + q;
+        wx[pos + (pos >> 6)] = u[q];
+      }
+      __builtin_amdgcn_wave_barrier();
+      const int64_t ob = (static_cast<int64_t>(k) * p.N + c0 / p.Q) * p.K + (c0 % p.Q) * CE;
+      u32x4_t* dst = reinterpret_cast<u32x4_t*>(static_cast<char*>(p.out) + ob * (ODT == 0 ? 4 : 2));
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        const int pos = 64 * q + lane;
+        dst[pos] = wx[pos + (pos >> 6)];
+      }
     } else {
-      u32x2_t* dst = reinterpret_cast<u32x2_t*>(base);  // up to 40 bytes, 8-byte aligned
+      u32x4_t* dst = reinterpret_cast<u32x4_t*>(static_cast<char*>(p.out) + o * (ODT == 0 ? 4 : 2));
+      constexpr int EPU = ODT == 0 ? 4 : 8;  // elements per 16-byte unit
 #pragma unroll
-      for (int q = 0; q < CE / 4; ++q)
-        if (4 * q < cnt) store_vec(dst + q, u32x2_t{h[2 * q], h[2 * q + 1]});
+      for (int q = 0; q < U; ++q)
+        if (EPU * q < cnt) dst[q] = u[q];
+    }
+  } else {
+    // trit chunks of 16-bit outputs: 40 bytes, 8-byte aligned
+    u32x2_t* dst = reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.out) + o);
+#pragma unroll
+    for (int q = 0; q < CE / 4; ++q) {
+      if (4 * q < cnt) {
+        uint32_t h2[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const float a = v[4 * q + 2 * r], b = v[4 * q + 2 * r + 1];
+          const uint16_t ha = ODT == 1 ? float_to_bf16_rne(a) : float_to_half_rne(a);
+          const uint16_t hb = ODT == 1 ? float_to_bf16_rne(b) : float_to_half_rne(b);
+          h2[r] = static_cast<uint32_t>(ha) | (static_cast<uint32_t>(hb) << 16);
+        }
+        dst[q] = u32x2_t{h2[0], h2[1]};
+      }
     }
   }
 }
