@@ -109,3 +109,24 @@ def test_batched_gather_qmm_full_size(proj):
         assert offsets[e] <= m < offsets[e + 1]
         cols = np.sort(g.choice(pr.N, 48, replace=False))
         sampled_check(qw, e, cols, Xs[i], ys[i, cols], f"C5 {proj} row {m} expert {e}")
+
+
+def test_dequant_full_size_gate_stack():
+    # the whole batched-MoE gate stack (128 experts x 1536 x 4096, 4-bit g128) decoded to
+    # bf16 in one call, as bench.py times it; sampled rows of sampled experts checked
+    # against the oracle's fp64 dequantization of the GPU's own codes
+    from oracle import encode as oenc
+    c = wl.C5
+    pr = c.projs[0]
+    qw = encode_stack(c, pr)
+    out = tq.dequant(qw, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    g = wl.rng(c.cid, 93)
+    for e in np.sort(g.choice(c.E, 6, replace=False)):
+        rows = np.sort(g.choice(pr.N, 16, replace=False))
+        codes = torch_to_np(qw.codes[int(e), rows]).reshape(len(rows), -1)
+        scales = torch_to_np(qw.scales[int(e), rows]).reshape(len(rows), -1)
+        want = oenc.dequant(codes, scales, pr.levels, pr.group, pr.K)
+        got = as_f64(out[int(e), torch.from_numpy(rows).to(DEV)])
+        tol = np.abs(want) * 2.0 ** -7
+        assert np.all(np.abs(got - want) <= tol), f"expert {e}"
