@@ -146,3 +146,26 @@ def test_constant_row_rotates_to_spike():
     V = hd.rotate(W, 0)
     assert np.isclose(np.sqrt(np.mean(V * V)), 1.0)
     assert np.max(np.abs(V)) < 0.25 * np.sqrt(K)
+
+
+def test_dequant_worked_examples():
+    # Hand-built rows: known indices packed by the (separately pinned) packers, fp16 scales
+    # with exact values, and the expected weights written out as centroid times the scale of
+    # element j's group j // g. A wrong group mapping, index order or scale decode fails.
+    c8 = cb.centroids(8)
+    idx = np.array(list(range(8)) + list(range(7, -1, -1)) + list(range(8)) + list(range(7, -1, -1)))
+    words = enc.pack(idx[None, :], 8)
+    scales = np.array([[0x3800, 0x4200]], dtype=np.uint16)  # 0.5, 3.0
+    got = enc.dequant(words, scales, 8, 16, 32)[0]
+    want = np.array([c8[i] * (0.5 if j < 16 else 3.0) for j, i in enumerate(idx)])
+    np.testing.assert_array_equal(got, want)
+    # trits: K = 64 in four 16-element groups, digit j % 3 of element j
+    c3 = cb.centroids(3)
+    tidx = np.arange(64) % 3
+    tw = enc.pack(tidx[None, :], 3)
+    ts = np.array([[0x3E00, 0x3400, 0x4000, 0x3C00]], dtype=np.uint16)  # 1.5, 0.25, 2.0, 1.0
+    got = enc.dequant(tw, ts, 3, 16, 64)[0]
+    sv = [1.5, 0.25, 2.0, 1.0]
+    want = np.array([c3[t] * sv[j // 16] for j, t in enumerate(tidx)])
+    np.testing.assert_array_equal(got, want)
+    assert c3[1] == 0.0 and c3[0] == -c3[2]
