@@ -287,7 +287,11 @@ __device__ __forceinline__ void qmm_tile(const QmmParams& p, int e, int m0, int 
   auto load_codes = [&](QmmStage<L, G16>& st, int step) {
     step = step < last ? step : last;
     const int e0 = step * Q::BK + g * S::elems;
-    const int fw = span_first_word<L>(e0);
+    // With K an odd multiple of 32, the second lane group's span of the last step starts at
+    // K: its vector loads read the row's last span instead of the words past the row (its
+    // inputs are zero, so the values do not matter, but the last row of the last expert
+    // ends the buffer).
+    const int fw = span_first_word<L>(L == 3 || e0 < p.K ? e0 : p.K - S::elems);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       if constexpr (L == 16) {

@@ -285,8 +285,11 @@ def routing_case(T, E, k, cfg):
 @pytest.mark.parametrize("levels,group,K,N", [(16, 128, 4096, 192), (16, 128, 1536, 320),
                                               (8, 64, 768, 100), (3, 16, 2048, 64),
                                               (4, 32, 640, 130), (16, 64, 6144, 72),
-                                              (8, 32, 1280, 90)])
+                                              (8, 32, 1280, 90), (16, 32, 96, 40),
+                                              (4, 16, 160, 70), (16, 16, 224, 33),
+                                              (8, 32, 96, 50), (4, 32, 224, 100)])
 def test_gather_qmm(levels, group, K, N):
+    # (the last five: K an odd multiple of 32, so the last K step is half empty)
     E, T, k = 10, 96, 3
     qw, _ = make_experts(918, E, N, K, levels, group, seed=2)
     row_token, row_expert, offsets = routing_case(T, E, k, 918 + K)
