@@ -33,8 +33,13 @@ constexpr int kQmmThreads = 64 * kQmmWaves;
 constexpr int kQmmBM = 128;                      // rows per tile: 4 sub-tiles of 32
 constexpr int kQmmWN = 64;                       // output columns per wave: 2 tiles of 32
 constexpr int kQmmBN = kQmmWN * kQmmWaves;       // output columns per workgroup
-// Scales of a tile's rows are staged in LDS when a row has at most this many groups.
-constexpr int kQmmMaxLdsGroups = 32;
+// Scales of a tile's rows are staged in LDS (except for the bit formats with groups of
+// 16), a window of this many consecutive groups of every row at a time: what the LDS holds
+// beside the format's table and the double-buffered input tile.
+template <int L>
+constexpr int qmm_lds_groups() {
+  return L == 3 ? 88 : 32;
+}
 
 template <int L>
 struct QmmStep {
@@ -244,7 +249,8 @@ __device__ __forceinline__ void qmm_tile(const QmmParams& p, int e, int m0, int 
   const uint32_t* cexp = p.codes + static_cast<int64_t>(e) * p.N * p.wpr;
   const uint16_t* sexp = p.scales + static_cast<int64_t>(e) * p.N * p.ngk;
   uint32_t coff[2], soff[2];
-  const int sst = p.ngk + 1;  // LDS halves per row of staged scales (odd: no bank conflicts)
+  constexpr int WG = qmm_lds_groups<L>();
+  constexpr int sst = WG + 1;  // LDS halves per row of staged scales (odd: no bank conflicts)
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     int n = n0 + wave * kQmmWN + 32 * j + c32;
@@ -252,16 +258,22 @@ __device__ __forceinline__ void qmm_tile(const QmmParams& p, int e, int m0, int 
     coff[j] = static_cast<uint32_t>(n) * p.wpr * 4u;
     soff[j] = SL ? static_cast<uint32_t>((n - n0) * sst) : static_cast<uint32_t>(n) * p.ngk * 2u;
   }
-  if constexpr (SL) {
-    // the tile's rows' scales are one contiguous block: copy it once with coalesced loads
+  // groups wbase .. wbase + WG - 1 of the tile's rows are in LDS; the window moves forward
+  // when a step needs a group past it (only trits: the bit formats stage their scales only
+  // when a row has at most WG groups)
+  constexpr bool MOVES = L == 3;
+  int wbase = 0;
+  auto stage_scales = [&](int gb) {
     const int rows = p.N - n0 < kQmmBN ? p.N - n0 : kQmmBN;
-    const int total = rows * p.ngk;
-    const uint16_t* src = sexp + static_cast<int64_t>(n0) * p.ngk;
+    const int ng = p.ngk - gb < WG ? p.ngk - gb : WG;
+    const int total = rows * ng;
+    const uint16_t* src = sexp + static_cast<int64_t>(n0) * p.ngk + gb;
     for (int i = threadIdx.x; i < total; i += kQmmThreads) {
-      const int r = i / p.ngk;
-      ls[r * sst + (i - r * p.ngk)] = src[i];
+      const int r = i / ng, c = i - r * ng;
+      ls[r * sst + c] = src[r * p.ngk + c];
     }
-  }
+  };
+  if constexpr (SL) stage_scales(0);
   // this thread's 16-byte units of the input tile (a unit past the tile, which only the
   // trit format has, loads the tile's first unit and is not stored)
   const _Float16* asrc[Q::AU];
@@ -372,8 +384,8 @@ __device__ __forceinline__ void qmm_tile(const QmmParams& p, int e, int m0, int 
   auto body = [&](auto parity, int step) {
     constexpr int P = decltype(parity)::value;
     QmmStage<L, G16>& cur = st[P];
-    uint32_t s2[2][MF];
     const int e0 = (step < last ? step : last) * Q::BK + g * S::elems;
+    uint32_t s2[2][MF];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
 #pragma unroll
@@ -384,7 +396,7 @@ __device__ __forceinline__ void qmm_tile(const QmmParams& p, int e, int m0, int 
           const int ek = L == 3 ? e0 + 8 * k : e0 + 16 * k;
           int gi = ek >> p.lg_group;
           gi = gi < p.ngk ? gi : p.ngk - 1;
-          sv = ls[soff[j] + gi];
+          sv = ls[soff[j] + gi - (MOVES ? wbase : 0)];
         } else {
           sv = cur.s[j][k];
         }
@@ -429,8 +441,25 @@ __device__ __forceinline__ void qmm_tile(const QmmParams& p, int e, int m0, int 
     fetch_a(st[P ^ 1], step + 3);
     __syncthreads();
   };
+  // Before a step whose groups run past the window, the window restarts at the step's first
+  // group (the barrier that ends every step has retired the reads of the old window; a
+  // window of WG groups covers any step, as WG * group >= BK + group).
+  auto advance_window = [&](int step) {
+    if constexpr (SL && MOVES) {
+      const int sc = step < last ? step : last;
+      int hi = (sc * Q::BK + Q::BK - 1) >> p.lg_group;
+      hi = hi < p.ngk ? hi : p.ngk - 1;
+      if (hi >= wbase + WG) {  // uniform per workgroup
+        wbase = (sc * Q::BK) >> p.lg_group;
+        stage_scales(wbase);
+        __syncthreads();
+      }
+    }
+  };
   for (int step = 0; step < nsteps; step += 2) {
+    advance_window(step);
     body(std::integral_constant<int, 0>{}, step);
+    advance_window(step + 1);
     body(std::integral_constant<int, 1>{}, step + 1);
   }
 
@@ -451,7 +480,7 @@ __global__ __launch_bounds__(kQmmThreads) void k_gqmm(QmmParams p) {
   __shared__ int32_t tok[kQmmBM];
   __shared__ __attribute__((aligned(16))) float txs[kQmmBM];
   __shared__ uint16_t hs[16];
-  __shared__ uint16_t ls[SL ? kQmmBN * (kQmmMaxLdsGroups + 1) : 1];
+  __shared__ uint16_t ls[SL ? kQmmBN * (qmm_lds_groups<L>() + 1) : 1];
 
   // Workgroups are dealt to the 8 XCDs in turn (XCD b % 8). Row tile t goes to XCD t % 8,
   // all its column tiles in a row there, so they share the tile's inputs in that XCD's L2;
@@ -533,8 +562,10 @@ hipError_t launch_gather_qmm(const WeightArgs& w, const void* x, int xdt, int64_
   if (gx > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(gx));
   const bool g16 = w.group == 16;
-  // scales staged in LDS per tile when a row has few enough groups (never with groups of 16)
-  const bool sl = !g16 && p.ngk <= kQmmMaxLdsGroups;
+  // Scales staged in LDS: always for trits (kept in registers, their five scales per span
+  // and stage make the kernel spill, at half the speed); for the bit formats when a row's
+  // groups fit one window (never with groups of 16, whose scales are per half fragment).
+  const bool sl = !g16 && p.ngk <= qmm_lds_groups<16>();
   const dim3 blk(kQmmThreads);
   switch (w.levels) {
     case 16:
@@ -553,8 +584,7 @@ hipError_t launch_gather_qmm(const WeightArgs& w, const void* x, int xdt, int64_
       else hipLaunchKernelGGL((k_gqmm<4, false, false>), grid, blk, 0, s, p);
       break;
     default:
-      if (sl) hipLaunchKernelGGL((k_gqmm<3, false, true>), grid, blk, 0, s, p);
-      else hipLaunchKernelGGL((k_gqmm<3, false, false>), grid, blk, 0, s, p);
+      hipLaunchKernelGGL((k_gqmm<3, false, true>), grid, blk, 0, s, p);
       break;
   }
   return hipGetLastError();

@@ -287,9 +287,11 @@ def routing_case(T, E, k, cfg):
                                               (4, 32, 640, 130), (16, 64, 6144, 72),
                                               (8, 32, 1280, 90), (16, 32, 96, 40),
                                               (4, 16, 160, 70), (16, 16, 224, 33),
-                                              (8, 32, 96, 50), (4, 32, 224, 100)])
+                                              (8, 32, 96, 50), (4, 32, 224, 100),
+                                              (3, 16, 7168, 40), (3, 128, 768, 48)])
 def test_gather_qmm(levels, group, K, N):
-    # (the last five: K an odd multiple of 32, so the last K step is half empty)
+    # (K 96, 160, 224: an odd multiple of 32, so the last K step is half empty; trits with
+    # 128 and 448 groups per row: the LDS window of staged scales moves along the row)
     E, T, k = 10, 96, 3
     qw, _ = make_experts(918, E, N, K, levels, group, seed=2)
     row_token, row_expert, offsets = routing_case(T, E, k, 918 + K)
