@@ -288,10 +288,13 @@ def routing_case(T, E, k, cfg):
                                               (8, 32, 1280, 90), (16, 32, 96, 40),
                                               (4, 16, 160, 70), (16, 16, 224, 33),
                                               (8, 32, 96, 50), (4, 32, 224, 100),
-                                              (3, 16, 7168, 40), (3, 128, 768, 48)])
+                                              (3, 16, 7168, 40), (3, 128, 768, 48),
+                                              (16, 16, 2048, 80), (8, 16, 5120, 40),
+                                              (4, 16, 1536, 64)])
 def test_gather_qmm(levels, group, K, N):
     # (K 96, 160, 224: an odd multiple of 32, so the last K step is half empty; trits with
-    # 128 and 448 groups per row: the LDS window of staged scales moves along the row)
+    # 128 and 448 groups per row: the LDS window of staged scales moves along the row;
+    # groups of 16 with 96 to 320 groups per row, their scales loaded per lane)
     E, T, k = 10, 96, 3
     qw, _ = make_experts(918, E, N, K, levels, group, seed=2)
     row_token, row_expert, offsets = routing_case(T, E, k, 918 + K)
