@@ -372,3 +372,54 @@ def test_gather_qmm_many_experts():
         a, b = offsets[e], offsets[e + 1]
         want, bound = qmv_reference(cs[e], ss[e], levels, group, K, 0, Xf[row_token[a:b]])
         check_outputs(yg[a:b], want, bound, f"expert {e}")
+
+
+# output rounding of each result type, relative to the value (round to nearest)
+OUT_ROUND = {torch.float32: 0.0, torch.bfloat16: 2.0 ** -8, torch.float16: 2.0 ** -11}
+
+
+@pytest.mark.parametrize("xdt", [torch.float32, torch.float16])
+@pytest.mark.parametrize("ydt", [torch.bfloat16, torch.float16])
+def test_gather_family_dtypes(xdt, ydt):
+    # every input and output type through gather_qmv, multi_gather_qmv and gather_qmm (the
+    # other tests of these three use bf16 inputs and fp32 results)
+    E, N, K, levels, group = 6, 72, 1024, 16, 64
+    qw, _ = make_experts(925, E, N, K, levels, group, seed=3)
+    codes, scales = gpu_arrays(qw)
+    g = wl.rng(925, 1)
+    # gather_qmv: one input, several experts
+    x = to_dev(wl.gaussian(g, 1, K)[0], xdt)
+    ids = torch.tensor([5, 0, 2, 5], dtype=torch.int32, device="cuda")
+    y = tq.gather_qmv(qw, ids, x, out_dtype=ydt)
+    torch.cuda.synchronize()
+    assert y.dtype == ydt
+    xf = as_f64(x)
+    for k, e in enumerate([5, 0, 2, 5]):
+        want, bound = qmv_reference(codes[e], scales[e], levels, group, K, 3, xf)
+        check_outputs(as_f64(y[k]), want, bound + OUT_ROUND[ydt] * np.abs(want), f"gather_qmv {k}")
+    # multi_gather_qmv: an input per pair
+    pids = np.array([1, 4, 4, 0, 3, 1, 1], dtype=np.int32)
+    X = to_dev(wl.gaussian(g, len(pids), K), xdt)
+    y = tq.multi_gather_qmv(qw, torch.from_numpy(pids).cuda(), X, out_dtype=ydt)
+    torch.cuda.synchronize()
+    assert y.dtype == ydt
+    Xf = as_f64(X)
+    for k, e in enumerate(pids):
+        want, bound = qmv_reference(codes[e], scales[e], levels, group, K, 3, Xf[k])
+        check_outputs(as_f64(y[k]), want, bound + OUT_ROUND[ydt] * np.abs(want), f"multi_gather {k}")
+    # gather_qmm: rows sorted by expert
+    T = 40
+    row_token, _, offsets = routing_case(T, E, 2, 925)
+    X = to_dev(wl.gaussian(g, T, K), xdt)
+    y = tq.gather_qmm(qw, X, torch.from_numpy(row_token).cuda(), torch.from_numpy(offsets).cuda(),
+                      out_dtype=ydt)
+    torch.cuda.synchronize()
+    assert y.dtype == ydt
+    Xf = as_f64(X)
+    yg = as_f64(y)
+    for e in range(E):
+        a, b = offsets[e], offsets[e + 1]
+        if b == a:
+            continue
+        want, bound = qmv_reference(codes[e], scales[e], levels, group, K, 3, Xf[row_token[a:b]])
+        check_outputs(yg[a:b], want, bound + OUT_ROUND[ydt] * np.abs(want), f"gather_qmm expert {e}")
