@@ -423,3 +423,28 @@ def test_gather_family_dtypes(xdt, ydt):
             continue
         want, bound = qmv_reference(codes[e], scales[e], levels, group, K, 3, Xf[row_token[a:b]])
         check_outputs(yg[a:b], want, bound + OUT_ROUND[ydt] * np.abs(want), f"gather_qmm expert {e}")
+
+
+def test_gather_and_multi_gather_pre_rotated_inputs():
+    # inputs already rotated on the caller's side (fp32 x' = H diag(s) x / sqrt(K)): the same
+    # products as the oracle's on the unrotated x, within the fp32 rounding of x'
+    E, N, K, levels, group = 5, 64, 2560, 8, 64
+    qw, _ = make_experts(926, E, N, K, levels, group, seed=6)
+    codes, scales = gpu_arrays(qw)
+    g = wl.rng(926, 1)
+    x = wl.gaussian(g, 1, K)[0].astype(np.float64)
+    xr = torch.from_numpy(ohd.rotate(x, 6).astype(np.float32)).cuda()
+    ids = [4, 1, 1, 0]
+    y = tq.gather_qmv(qw, torch.tensor(ids, dtype=torch.int32, device="cuda"), xr, rotated=True)
+    torch.cuda.synchronize()
+    for k, e in enumerate(ids):
+        want, bound = qmv_reference(codes[e], scales[e], levels, group, K, 6, x)
+        check_outputs(as_f64(y[k]), want, bound + 1e-6 * np.abs(want), f"gather_qmv {k}")
+    X = wl.gaussian(g, 6, K).astype(np.float64)
+    Xr = torch.from_numpy(np.stack([ohd.rotate(X[i], 6) for i in range(6)]).astype(np.float32)).cuda()
+    pids = np.array([2, 2, 3, 0, 4, 2], dtype=np.int32)
+    y = tq.multi_gather_qmv(qw, torch.from_numpy(pids).cuda(), Xr, rotated=True)
+    torch.cuda.synchronize()
+    for k, e in enumerate(pids):
+        want, bound = qmv_reference(codes[e], scales[e], levels, group, K, 6, X[k])
+        check_outputs(as_f64(y[k]), want, bound + 1e-6 * np.abs(want), f"multi_gather {k}")
