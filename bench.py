@@ -41,9 +41,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5, 6],
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5, 6, 7],
                     help="2 dense qmv (default), 3 gather_qmv, 4 multi_gather_qmv, "
-                         "5 gather_qmm, 6 dequant of an expert stack")
+                         "5 gather_qmm, 6 dequant of an expert stack, 7 encode of an "
+                         "expert stack streamed from pinned host memory")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calls", type=int, default=1000, help="qmv calls per step")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -441,6 +442,67 @@ def bench_dequant(args):
     return res
 
 
+def bench_encode_stream(args):
+    """encode_stream of 16 experts of the batched-MoE gate stack (16 x 1536 x 4096 bf16,
+    201 MB) from pinned host memory through a 64 MB device staging buffer, copies on their
+    own stream: host bytes per second, PCIe included (the input is not in HBM)."""
+    import torch
+    import rotation_lloyd_max_amd as tq
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    c = wl.C5
+    pr = c.projs[0]
+    E = 16
+    g = wl.torch_generator(dev, c.cid, wl.PROJ_TENSOR[pr.name], 0)
+    Wd = wl.torch_student_rows(g, E * pr.N, pr.K, dev, torch.bfloat16).view(E, pr.N, pr.K)
+    W = torch.empty(Wd.shape, dtype=torch.bfloat16, pin_memory=True)
+    W.copy_(Wd)
+    ref = tq.encode(Wd, pr.levels, pr.group, pr.seed)
+    del Wd
+    torch.cuda.synchronize()
+    out = tq.QWeight(torch.empty_like(ref.codes), torch.empty_like(ref.scales), ref.signs,
+                     pr.levels, pr.group, pr.K, pr.N, E, pr.seed)
+    cs = torch.cuda.Stream(device=dev)
+    staging = 64 << 20
+
+    def call():
+        tq.encode_stream(W, pr.levels, pr.group, pr.seed, device=dev, staging_bytes=staging,
+                         out=out, copy_stream=cs)
+
+    call()
+    torch.cuda.synchronize()
+    same = torch.equal(out.codes, ref.codes) and torch.equal(out.scales.view(torch.int16),
+                                                           ref.scales.view(torch.int16))
+    if not same:
+        raise RuntimeError("encode_stream differs from encode")
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for _ in range(args.steps):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = a.elapsed_time(b) / args.steps
+    host = W.numel() * 2
+    value = host / (ms / 1e3) / 1e9
+    return {
+        "metric": "encode_stream GB/s of host weight bytes (pinned host -> HBM, PCIe included)",
+        "value": round(value, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 in, f64 rotation",
+        "data": "synthetic",
+        "config": {"workload": "encode_stream of 16 experts of the batched-MoE gate stack "
+                               "(16 x 1536 x 4096 bf16, 4-bit g128), 64 MB staging",
+                   "bytes_per_step": host, "byte_identical_to_encode": same},
+        "wall_s": round(wall, 4),
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -461,6 +523,8 @@ def main():
         out = bench_dense(args)
     elif args.config == 6:
         out = bench_dequant(args)
+    elif args.config == 7:
+        out = bench_encode_stream(args)
     else:
         out = bench_moe(args)
     print(json.dumps(out), flush=True)

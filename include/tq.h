@@ -118,6 +118,30 @@ int tq_signs(uint64_t seed, int64_t K, uint32_t *bits, void *stream);
 int tq_encode(const void *W, tq_dtype w_dtype, int64_t rows, int64_t K, int32_t n_levels,
               int32_t group, uint64_t seed, uint32_t *codes, uint16_t *scales, void *stream);
 
+/* tq_encode of weight rows that live in HOST memory, streamed through a caller-owned device
+ * staging buffer, so that device memory holds the encoded weight plus the staging buffer
+ * and never the whole unquantized weight (turboquant-mlx "How it works", "Two converters":
+ * the streaming converter keeps memory near one shard and writes the same bytes as the
+ * in-memory one). The rows go up in chunks: each chunk is copied on `copy_stream` into one
+ * half of `staging` and encoded on `stream` into its rows of codes and scales; the halves
+ * alternate, ordered by events, so the copy of chunk i + 1 overlaps the encode of chunk i
+ * when W_host is pinned (a pageable W_host is copied as the runtime allows). The output is
+ * byte-identical to one tq_encode of all rows.
+ *   W_host         host, [rows][K] of w_dtype; must stay valid and unchanged until the
+ *                  work enqueued on `stream` has completed
+ *   staging        device, 256-byte aligned, staging_bytes >= 2 * 256-byte-rounded K row
+ *                  bytes (a chunk is as many rows as half of it holds)
+ *   copy_stream    hipStream_t as void*, or NULL to copy on `stream` (no overlap)
+ * Like every call here it enqueues and returns; it creates four HIP events and releases
+ * them before returning (they are freed by the runtime once the work has used them).
+ * Errors: the tq_encode argument errors; TQ_ERR_ARG for a NULL W_host or staging, or a
+ * staging buffer that holds fewer than two rows; TQ_ERR_ALIGN for a misaligned staging;
+ * TQ_ERR_HIP if the runtime fails, in which case some chunks may already be enqueued. */
+int tq_encode_stream(const void *W_host, tq_dtype w_dtype, int64_t rows, int64_t K,
+                     int32_t n_levels, int32_t group, uint64_t seed, uint32_t *codes,
+                     uint16_t *scales, void *staging, size_t staging_bytes, void *stream,
+                     void *copy_stream);
+
 /* out[r] = R x[r] for `rows` rows of length K (device, row-major). Computed in fp32.
  * ("Running a quantized layer": the input is rotated with the weights' rotation.) */
 int tq_fwht(const void *x, tq_dtype x_dtype, int64_t rows, int64_t K, uint64_t seed,

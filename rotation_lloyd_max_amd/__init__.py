@@ -19,7 +19,8 @@ import torch
 
 __all__ = [
     "TqError", "QWeight", "lib", "codebook", "words_per_row", "signs", "encode", "fwht",
-    "qmv", "gather_qmv", "multi_gather_qmv", "gather_qmm", "workspace_bytes",
+    "qmv", "gather_qmv", "multi_gather_qmv", "gather_qmm", "workspace_bytes", "dequant",
+    "encode_stream",
     "F32", "BF16", "F16", "X_ROTATED",
 ]
 
@@ -68,6 +69,8 @@ SIGNATURES = [
     ("tq_gather_qmm", ctypes.c_int,
      [_QW, _P, ctypes.c_int, _I64, _P, _P, _I64, _P, ctypes.c_int, _U32, _P, _SZ, _P]),
     ("tq_dequant", ctypes.c_int, [_QW, _P, _I64, _P, ctypes.c_int, _P]),
+    ("tq_encode_stream", ctypes.c_int,
+     [_P, ctypes.c_int, _I64, _I64, _I32, _I32, _U64, _P, _P, _P, _SZ, _P, _P]),
     ("tq_last_error", ctypes.c_char_p, []),
 ]
 
@@ -166,6 +169,41 @@ def encode(W, levels, group, seed, out=None):
         codes, scales, sg = out.codes, out.scales, out.signs
     _check(lib().tq_encode(_ptr(W), _dt(W), E * N, K, levels, group, seed, _ptr(codes),
                            _ptr(scales), _stream()))
+    return QWeight(codes, scales, sg, levels, group, K, N, E, seed)
+
+
+def encode_stream(W_host, levels, group, seed, device="cuda", staging_bytes=64 << 20,
+                  out=None, copy_stream=None):
+    """encode() of a weight held in host memory ([N, K] or [E, N, K] contiguous CPU tensor,
+    pinned for overlap), streamed to the device through a staging buffer of staging_bytes;
+    the same bytes as encode() of the whole weight on the device. The copies read W_host
+    after this returns: keep it alive and unchanged until the current stream has passed
+    this call. copy_stream: a torch.cuda.Stream for the copies (default: a new one), or the
+    current stream for no overlap."""
+    if W_host.device.type != "cpu":
+        raise ValueError("encode_stream takes a host (CPU) tensor")
+    if not W_host.is_contiguous():
+        raise ValueError("encode_stream needs a contiguous W_host (the copies are asynchronous)")
+    if W_host.dim() == 2:
+        W_host = W_host.unsqueeze(0)
+    E, N, K = W_host.shape
+    device = torch.device(device)
+    wpr = words_per_row(K, levels)
+    if out is None:
+        codes = torch.empty((E, N, wpr), dtype=torch.int32, device=device)
+        scales = torch.empty((E, N, K // group), dtype=torch.float16, device=device)
+        sg = signs(seed, K, device)
+    else:
+        codes, scales, sg = out.codes, out.scales, out.signs
+    staging = _workspace(staging_bytes, device)
+    cs = copy_stream if copy_stream is not None else torch.cuda.Stream(device=device)
+    # the staging memory may have been in use by earlier work of the current stream
+    cs.wait_stream(torch.cuda.current_stream(device))
+    _check(lib().tq_encode_stream(_ptr(W_host), _dt(W_host), E * N, K, levels, group, seed,
+                                  _ptr(codes), _ptr(scales), _ptr(staging), staging_bytes,
+                                  _stream(), ctypes.c_void_p(cs.cuda_stream)))
+    # the copy stream wrote the staging buffer; keep it alive for that stream too
+    staging.record_stream(cs)
     return QWeight(codes, scales, sg, levels, group, K, N, E, seed)
 
 

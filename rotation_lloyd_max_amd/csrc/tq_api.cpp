@@ -238,6 +238,64 @@ int tq_encode(const void* W, tq_dtype w_dtype, int64_t rows, int64_t K, int32_t 
                     "tq_encode");
 }
 
+int tq_encode_stream(const void* W_host, tq_dtype w_dtype, int64_t rows, int64_t K,
+                     int32_t n_levels, int32_t group, uint64_t seed, uint32_t* codes,
+                     uint16_t* scales, void* staging, size_t staging_bytes, void* stream,
+                     void* copy_stream) {
+  int m = 1, P = 1;
+  const int rc = check_shape(K, n_levels, group, &m, &P);
+  if (rc != TQ_OK) return rc;
+  if (!valid_dtype(w_dtype)) return fail(TQ_ERR_ARG, "bad weight dtype");
+  if (rows < 0) return fail(TQ_ERR_ARG, "rows must be >= 0");
+  if (rows == 0) return TQ_OK;
+  if (!W_host || !codes || !scales || !staging)
+    return fail(TQ_ERR_ARG, "W_host, codes, scales and staging must be non-NULL");
+  if (!aligned(W_host, dtype_size(w_dtype)) || !aligned(codes, 4) || !aligned(scales, 2))
+    return fail(TQ_ERR_ALIGN, "W_host, codes or scales misaligned");
+  if (!aligned(staging, 256)) return fail(TQ_ERR_ALIGN, "staging must be 256-byte aligned");
+  // each half of the staging buffer holds `chunk` whole rows and starts 256-byte aligned
+  const size_t row_bytes = static_cast<size_t>(K) * dtype_size(w_dtype);
+  const size_t half = (staging_bytes / 2) & ~static_cast<size_t>(255);
+  const int64_t chunk = static_cast<int64_t>(half / row_bytes);
+  if (chunk < 1)
+    return fail(TQ_ERR_ARG, "staging of %zu bytes holds fewer than two rows of %zu bytes",
+                staging_bytes, row_bytes);
+  const int64_t wpr = words_per_row(K, n_levels);
+  const int64_t ngk = K / group;
+  const hipStream_t cs = static_cast<hipStream_t>(stream);
+  const hipStream_t xs = copy_stream ? static_cast<hipStream_t>(copy_stream) : cs;
+  // filled[b]: half b holds its chunk (copy done); freed[b]: its encode is done
+  hipEvent_t filled[2] = {nullptr, nullptr}, freed[2] = {nullptr, nullptr};
+  hipError_t e = hipSuccess;
+  for (int b = 0; b < 2 && e == hipSuccess; ++b) {
+    e = hipEventCreateWithFlags(&filled[b], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&freed[b], hipEventDisableTiming);
+  }
+  const char* src = static_cast<const char*>(W_host);
+  char* stage = static_cast<char*>(staging);
+  for (int64_t i = 0, r0 = 0; e == hipSuccess && r0 < rows; ++i, r0 += chunk) {
+    const int b = static_cast<int>(i & 1);
+    const int64_t n = rows - r0 < chunk ? rows - r0 : chunk;
+    char* buf = stage + b * half;
+    // the half is reused once the encode of the chunk it held two steps ago is done
+    if (i >= 2) e = hipStreamWaitEvent(xs, freed[b], 0);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(buf, src + static_cast<size_t>(r0) * row_bytes,
+                         static_cast<size_t>(n) * row_bytes, hipMemcpyHostToDevice, xs);
+    if (e == hipSuccess) e = hipEventRecord(filled[b], xs);
+    if (e == hipSuccess) e = hipStreamWaitEvent(cs, filled[b], 0);
+    if (e == hipSuccess)
+      e = launch_encode(buf, w_dtype, n, static_cast<int>(K), m, P, n_levels, group, seed,
+                        codes + r0 * wpr, scales + r0 * ngk, cs);
+    if (e == hipSuccess) e = hipEventRecord(freed[b], cs);
+  }
+  for (int b = 0; b < 2; ++b) {
+    if (filled[b]) (void)hipEventDestroy(filled[b]);
+    if (freed[b]) (void)hipEventDestroy(freed[b]);
+  }
+  return hip_status(e, "tq_encode_stream");
+}
+
 int tq_fwht(const void* x, tq_dtype x_dtype, int64_t rows, int64_t K, uint64_t seed, void* out,
             tq_dtype out_dtype, void* stream) {
   int m = 1, P = 1;

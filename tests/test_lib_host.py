@@ -35,7 +35,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     handle = ctypes.CDLL(tq.LIB_PATH)
     for n in names:
         assert hasattr(handle, n), n
@@ -118,6 +118,18 @@ def test_validation_statuses():
     assert L.tq_encode(16, 0, -1, 512, 16, 64, 0, 16, 16, None) == ERR_ARG
     assert L.tq_fwht(16, 0, 2, 100, 0, 16, 0, None) == ERR_UNSUPPORTED
     assert L.tq_signs(0, 0, 16, None) == ERR_ARG
+    # encode_stream: checked before any copy or launch (no GPU needed): unsupported K, NULL
+    # host rows or staging, misaligned staging, staging under two rows (K 512 fp32 = 2 KB a
+    # row: 4 KB is the least), and nothing to do for zero rows
+    es = L.tq_encode_stream
+    assert es(16, 0, 4, 500, 16, 64, 0, 16, 16, 256, 1 << 20, None, None) == ERR_UNSUPPORTED
+    assert es(0, 0, 4, 512, 16, 64, 0, 16, 16, 256, 1 << 20, None, None) == ERR_ARG
+    assert es(16, 0, 4, 512, 16, 64, 0, 16, 16, 0, 1 << 20, None, None) == ERR_ARG
+    assert es(16, 0, 4, 512, 16, 64, 0, 16, 16, 128, 1 << 20, None, None) == ERR_ALIGN
+    assert es(16, 0, 4, 512, 16, 64, 0, 16, 16, 256, 4095, None, None) == ERR_ARG
+    assert b"fewer than two rows" in L.tq_last_error()
+    assert es(16, 3, 4, 512, 16, 64, 0, 16, 16, 256, 1 << 20, None, None) == ERR_ARG
+    assert es(16, 0, 0, 512, 16, 64, 0, 16, 16, 256, 0, None, None) == 0
     # workspace query with a bad descriptor
     assert L.tq_workspace_bytes(3, None, 1, 0) == ctypes.c_size_t(-1).value
     assert L.tq_workspace_bytes(9, ctypes.byref(desc()), 1, 0) == ctypes.c_size_t(-1).value
