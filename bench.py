@@ -19,8 +19,9 @@ not in the timed region.
   cpu_baseline  the fp64 oracle (numpy, one BLAS thread) on a bounded sample of the same
           layer, in the same unit
 
-Other workloads (--config 3, 4, 5, 6) time gather_qmv, multi_gather_qmv, gather_qmm and
-dequant for reference; the default line is the dense decode layer.
+Other workloads (--config 3, 4, 5, 6, 7) time gather_qmv, multi_gather_qmv, gather_qmm,
+dequant and the streamed encode from pinned host memory for reference; the default line is
+the dense decode layer.
 """
 
 import argparse
