@@ -172,14 +172,25 @@ def encode(W, levels, group, seed, out=None):
     return QWeight(codes, scales, sg, levels, group, K, N, E, seed)
 
 
+_copy_streams = {}
+
+
+def _copy_stream(device):
+    """One copy stream per device (default priority), created on first use."""
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    if idx not in _copy_streams:
+        _copy_streams[idx] = torch.cuda.Stream(device=idx)
+    return _copy_streams[idx]
+
+
 def encode_stream(W_host, levels, group, seed, device="cuda", staging_bytes=64 << 20,
                   out=None, copy_stream=None):
     """encode() of a weight held in host memory ([N, K] or [E, N, K] contiguous CPU tensor,
     pinned for overlap), streamed to the device through a staging buffer of staging_bytes;
     the same bytes as encode() of the whole weight on the device. The copies read W_host
     after this returns: keep it alive and unchanged until the current stream has passed
-    this call. copy_stream: a torch.cuda.Stream for the copies (default: a new one), or the
-    current stream for no overlap."""
+    this call. copy_stream: a torch.cuda.Stream for the copies (default: one kept per
+    device), or the current stream for no overlap."""
     if W_host.device.type != "cpu":
         raise ValueError("encode_stream takes a host (CPU) tensor")
     if not W_host.is_contiguous():
@@ -196,7 +207,7 @@ def encode_stream(W_host, levels, group, seed, device="cuda", staging_bytes=64 <
     else:
         codes, scales, sg = out.codes, out.scales, out.signs
     staging = _workspace(staging_bytes, device)
-    cs = copy_stream if copy_stream is not None else torch.cuda.Stream(device=device)
+    cs = copy_stream if copy_stream is not None else _copy_stream(device)
     # the staging memory may have been in use by earlier work of the current stream
     cs.wait_stream(torch.cuda.current_stream(device))
     _check(lib().tq_encode_stream(_ptr(W_host), _dt(W_host), E * N, K, levels, group, seed,
