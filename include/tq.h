@@ -85,7 +85,12 @@ enum { TQ_X_ROTATED = 1 }; /* x is already R x: skip the input rotation */
 enum { TQ_OP_QMV = 1, TQ_OP_GATHER_QMV = 2, TQ_OP_MULTI_GATHER_QMV = 3, TQ_OP_GATHER_QMM = 4 };
 
 /* A packed quantized weight: E experts of N x K (E = 1 for a dense layer). Read only
- * during the call. */
+ * during the call.
+ * The rotation of the weight is given by one thing only, `signs`: the kernels rotate the
+ * input with R = H_K diag(s) / sqrt(K) for the s these bits hold. The rotation is recorded
+ * by its seed ("Configuration that converter and loader share": rotation, seed and group
+ * sizes), so a caller makes `signs` with tq_signs(seed, K) for the seed that tq_encode was
+ * given; the descriptor carries no seed, so it cannot name a second, disagreeing rotation. */
 typedef struct {
   const uint32_t *codes;  /* device, [E][N][words_per_row], 16-byte aligned */
   const uint16_t *scales; /* device, [E][N][K / group], fp16 bits, 2-byte aligned */
@@ -93,7 +98,6 @@ typedef struct {
   int32_t n_levels;       /* 3 -> trit packed; 4 / 8 / 16 -> 2 / 3 / 4-bit bitstream */
   int32_t group;          /* 16, 32, 64 or 128 */
   int64_t K, N, E;        /* input dim, output dim, number of experts */
-  uint64_t seed;          /* the seed the signs came from (recorded, not read by kernels) */
 } tq_qweight;
 
 /* Number of uint32 words per packed row, or 0 for an unsupported (K, n_levels). */
@@ -132,8 +136,12 @@ int tq_encode(const void *W, tq_dtype w_dtype, int64_t rows, int64_t K, int32_t 
  *   staging        device, 256-byte aligned, staging_bytes >= 2 * 256-byte-rounded K row
  *                  bytes (a chunk is as many rows as half of it holds)
  *   copy_stream    hipStream_t as void*, or NULL to copy on `stream` (no overlap)
- * Like every call here it enqueues and returns; it creates four HIP events and releases
- * them before returning (they are freed by the runtime once the work has used them).
+ * The first copies wait for all work enqueued on `stream` before the call (an event
+ * recorded on `stream` at entry), so a staging buffer that earlier encodes on `stream`
+ * still read, for example the previous call's, is not overwritten early; work on other
+ * streams that uses `staging` is the caller's to order. Like every call here it enqueues
+ * and returns; it creates five HIP events and releases them before returning (the runtime
+ * frees them once the work has used them).
  * Errors: the tq_encode argument errors; TQ_ERR_ARG for a NULL W_host or staging, or a
  * staging buffer that holds fewer than two rows; TQ_ERR_ALIGN for a misaligned staging;
  * TQ_ERR_HIP if the runtime fails, in which case some chunks may already be enqueued. */

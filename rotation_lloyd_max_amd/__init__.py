@@ -44,7 +44,6 @@ class _QWeight(ctypes.Structure):
         ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("signs", ctypes.c_void_p),
         ("n_levels", ctypes.c_int32), ("group", ctypes.c_int32),
         ("K", ctypes.c_int64), ("N", ctypes.c_int64), ("E", ctypes.c_int64),
-        ("seed", ctypes.c_uint64),
     ]
 
 
@@ -96,8 +95,8 @@ def _check(status):
         raise TqError(status, lib().tq_last_error().decode())
 
 
-def _stream():
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+def _stream(device=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
 def _ptr(t):
@@ -133,7 +132,8 @@ def signs(seed, K, device="cuda"):
 @dataclass
 class QWeight:
     """Packed weight of E experts of N x K: codes int32 [E, N, wpr] (uint32 bit patterns),
-    scales float16 [E, N, K/group], signs int32 [ceil(K/32)]."""
+    scales float16 [E, N, K/group], signs int32 [ceil(K/32)] = signs(seed, K). The seed is
+    the record of the rotation; the library reads only the sign bits made from it."""
     codes: torch.Tensor
     scales: torch.Tensor
     signs: torch.Tensor
@@ -146,12 +146,28 @@ class QWeight:
 
     def desc(self):
         return _QWeight(self.codes.data_ptr(), self.scales.data_ptr(), self.signs.data_ptr(),
-                        self.levels, self.group, self.K, self.N, self.E, self.seed)
+                        self.levels, self.group, self.K, self.N, self.E)
 
     def expert(self, e):
         """View of expert e as a dense (E = 1) weight."""
         return QWeight(self.codes[e:e + 1], self.scales[e:e + 1], self.signs, self.levels,
                        self.group, self.K, self.N, 1, self.seed)
+
+
+def _check_out(out, E, N, K, levels, group, seed, device):
+    """An out= weight must be exactly the one the call writes: the library writes E*N rows
+    of codes and scales through its pointers."""
+    wpr = words_per_row(K, levels)
+    want = {"levels": levels, "group": group, "K": K, "N": N, "E": E, "seed": seed}
+    got = {k: getattr(out, k) for k in want}
+    if got != want:
+        raise ValueError(f"out= describes {got}, the call writes {want}")
+    for name, t, shape, dt in (("codes", out.codes, (E, N, wpr), torch.int32),
+                               ("scales", out.scales, (E, N, K // group), torch.float16)):
+        if tuple(t.shape) != shape or t.dtype != dt or not t.is_contiguous():
+            raise ValueError(f"out.{name} must be a contiguous {dt} tensor of shape {shape}")
+        if t.device != torch.device(device):
+            raise ValueError(f"out.{name} is on {t.device}, the call writes on {device}")
 
 
 def encode(W, levels, group, seed, out=None):
@@ -166,9 +182,11 @@ def encode(W, levels, group, seed, out=None):
         scales = torch.empty((E, N, K // group), dtype=torch.float16, device=W.device)
         sg = signs(seed, K, W.device)
     else:
+        _check_out(out, E, N, K, levels, group, seed, W.device)
         codes, scales, sg = out.codes, out.scales, out.signs
-    _check(lib().tq_encode(_ptr(W), _dt(W), E * N, K, levels, group, seed, _ptr(codes),
-                           _ptr(scales), _stream()))
+    with torch.cuda.device(W.device):
+        _check(lib().tq_encode(_ptr(W), _dt(W), E * N, K, levels, group, seed, _ptr(codes),
+                               _ptr(scales), _stream(W.device)))
     return QWeight(codes, scales, sg, levels, group, K, N, E, seed)
 
 
@@ -199,20 +217,25 @@ def encode_stream(W_host, levels, group, seed, device="cuda", staging_bytes=64 <
         W_host = W_host.unsqueeze(0)
     E, N, K = W_host.shape
     device = torch.device(device)
+    if device.index is None:
+        device = torch.device("cuda", torch.cuda.current_device())
     wpr = words_per_row(K, levels)
     if out is None:
         codes = torch.empty((E, N, wpr), dtype=torch.int32, device=device)
         scales = torch.empty((E, N, K // group), dtype=torch.float16, device=device)
         sg = signs(seed, K, device)
     else:
+        _check_out(out, E, N, K, levels, group, seed, device)
         codes, scales, sg = out.codes, out.scales, out.signs
     staging = _workspace(staging_bytes, device)
     cs = copy_stream if copy_stream is not None else _copy_stream(device)
-    # the staging memory may have been in use by earlier work of the current stream
-    cs.wait_stream(torch.cuda.current_stream(device))
-    _check(lib().tq_encode_stream(_ptr(W_host), _dt(W_host), E * N, K, levels, group, seed,
-                                  _ptr(codes), _ptr(scales), _ptr(staging), staging_bytes,
-                                  _stream(), ctypes.c_void_p(cs.cuda_stream)))
+    # the library orders the first copies after the work already on the encode stream
+    # (which may still use the staging memory torch hands out again)
+    with torch.cuda.device(device):
+        _check(lib().tq_encode_stream(_ptr(W_host), _dt(W_host), E * N, K, levels, group,
+                                      seed, _ptr(codes), _ptr(scales), _ptr(staging),
+                                      staging_bytes, _stream(device),
+                                      ctypes.c_void_p(cs.cuda_stream)))
     # the copy stream wrote the staging buffer; keep it alive for that stream too
     staging.record_stream(cs)
     return QWeight(codes, scales, sg, levels, group, K, N, E, seed)

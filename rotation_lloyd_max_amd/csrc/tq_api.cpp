@@ -264,12 +264,18 @@ int tq_encode_stream(const void* W_host, tq_dtype w_dtype, int64_t rows, int64_t
   const int64_t ngk = K / group;
   const hipStream_t cs = static_cast<hipStream_t>(stream);
   const hipStream_t xs = copy_stream ? static_cast<hipStream_t>(copy_stream) : cs;
-  // filled[b]: half b holds its chunk (copy done); freed[b]: its encode is done
-  hipEvent_t filled[2] = {nullptr, nullptr}, freed[2] = {nullptr, nullptr};
+  // filled[b]: half b holds its chunk (copy done); freed[b]: its encode is done; entry:
+  // everything enqueued on `stream` before this call (which may still read `staging`)
+  hipEvent_t filled[2] = {nullptr, nullptr}, freed[2] = {nullptr, nullptr}, entry = nullptr;
   hipError_t e = hipSuccess;
   for (int b = 0; b < 2 && e == hipSuccess; ++b) {
     e = hipEventCreateWithFlags(&filled[b], hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&freed[b], hipEventDisableTiming);
+  }
+  if (e == hipSuccess && xs != cs) {
+    e = hipEventCreateWithFlags(&entry, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventRecord(entry, cs);
+    if (e == hipSuccess) e = hipStreamWaitEvent(xs, entry, 0);
   }
   const char* src = static_cast<const char*>(W_host);
   char* stage = static_cast<char*>(staging);
@@ -293,6 +299,7 @@ int tq_encode_stream(const void* W_host, tq_dtype w_dtype, int64_t rows, int64_t
     if (filled[b]) (void)hipEventDestroy(filled[b]);
     if (freed[b]) (void)hipEventDestroy(freed[b]);
   }
+  if (entry) (void)hipEventDestroy(entry);
   return hip_status(e, "tq_encode_stream");
 }
 

@@ -129,3 +129,25 @@ def test_encode_expert_stack_shape():
     assert qw.codes.shape == (3, 50, 39) and qw.scales.shape == (3, 50, 48)
     ref = oenc.encode(as_f64(W.reshape(150, K)), levels, group, 1)
     check_codes(torch_to_np(qw.codes).reshape(150, -1), ref, levels, K)
+
+
+@pytest.mark.parametrize("levels,group,K", [(4, 64, 7168), (3, 16, 768), (16, 64, 1536),
+                                            (8, 128, 4096)])
+def test_encode_many_rows_in_one_call(levels, group, K):
+    # 3 * 4096 + 17 rows in one tq_encode call, the way expert stacks are encoded (16
+    # experts at a time); sampled rows, among them the first and last rows of each block of
+    # 4096 and the ragged tail, checked against the oracle's encode of the same bytes
+    rows = 3 * 4096 + 17
+    gen = wl.torch_generator(torch.device(DEV), 907, levels, K)
+    W = wl.torch_student_rows(gen, rows, K, DEV, torch.bfloat16)
+    qw = tq.encode(W, levels, group, seed=2)
+    torch.cuda.synchronize()
+    g = wl.rng(907, levels, K)
+    edges = [0, 1, 4095, 4096, 4097, 8191, 8192, 12287, 12288, rows - 2, rows - 1]
+    sample = np.unique(np.concatenate([edges, g.choice(rows, 40, replace=False)]))
+    idx = torch.from_numpy(sample).to(DEV)
+    ref = oenc.encode(as_f64(W[idx]), levels, group, 2)
+    codes = torch_to_np(qw.codes[0][idx]).reshape(len(sample), -1)
+    scales = torch_to_np(qw.scales[0][idx]).reshape(len(sample), -1)
+    check_codes(codes, ref, levels, K, f"L{levels} K{K} {rows} rows")
+    check_scales(scales, ref, f"L{levels} K{K} {rows} rows")

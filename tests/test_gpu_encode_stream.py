@@ -3,11 +3,16 @@ bytes as tq_encode of the whole weight on the device: chunks of a few rows with 
 last chunk, one chunk exactly, pinned and pageable host memory, copies on their own stream
 or on the encode stream, every weight dtype and code format."""
 
+import ctypes
+
+import numpy as np
 import pytest
 import torch
 
 import rotation_lloyd_max_amd as tq
 import workloads as wl
+from oracle import encode as oenc
+from parity import as_f64, check_codes, check_scales, torch_to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -55,3 +60,52 @@ def test_encode_stream_into_existing_weight_twice():
         assert q.codes.data_ptr() == out.codes.data_ptr()
         assert torch.equal(q.codes, qd.codes), rep
         assert torch.equal(q.scales.view(torch.int16), qd.scales.view(torch.int16)), rep
+
+
+@pytest.mark.parametrize("levels,group,K,dtype", [(4, 64, 7168, torch.bfloat16),
+                                                  (3, 16, 768, torch.float32),
+                                                  (8, 128, 4096, torch.float16)])
+def test_encode_stream_matches_oracle(levels, group, K, dtype):
+    # the streamed encode checked against the oracle directly (not only against tq_encode):
+    # sampled rows from every chunk, the ragged last chunk included
+    E, N, chunk = 3, 70, 23
+    g = wl.rng(962, levels, K)
+    W = torch.from_numpy(wl.student_rows(g, E * N, K)).to(dtype).view(E, N, K).pin_memory()
+    q = tq.encode_stream(W, levels, group, seed=5, staging_bytes=staging_for(chunk, K, dtype))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, E * N, 11), [E * N - 1, chunk - 1, chunk]]))
+    Wr = as_f64(W.view(E * N, K)[torch.from_numpy(rows)])
+    ref = oenc.encode(Wr, levels, group, 5)
+    check_codes(torch_to_np(q.codes).reshape(E * N, -1)[rows], ref, levels, K, "stream")
+    check_scales(torch_to_np(q.scales).reshape(E * N, -1)[rows], ref, "stream")
+
+
+def test_back_to_back_calls_reuse_one_staging_buffer():
+    # two tq_encode_stream calls through the C ABI, one staging buffer, one copy stream, and
+    # nothing between them (no host sync, no stream wait): the second call's first copies
+    # must wait for the first call's last encodes, which still read the staging halves
+    levels, group, K, rows = 16, 64, 2048, 96
+    L = tq.lib()
+    g = wl.rng(963, 0)
+    Ws = [torch.from_numpy(wl.student_rows(g, rows, K)).to(torch.bfloat16).pin_memory()
+          for _ in range(2)]
+    nbytes = staging_for(4, K, torch.bfloat16)
+    staging = torch.empty(nbytes // 8, dtype=torch.int64, device="cuda")
+    wpr = tq.words_per_row(K, levels)
+    outs = [(torch.empty((rows, wpr), dtype=torch.int32, device="cuda"),
+             torch.empty((rows, K // group), dtype=torch.float16, device="cuda")) for _ in Ws]
+    copy = torch.cuda.Stream()
+    enc = torch.cuda.current_stream()
+    for W, (c, s) in zip(Ws, outs):
+        rc = L.tq_encode_stream(ctypes.c_void_p(W.data_ptr()), tq.BF16, rows, K, levels, group,
+                                9, ctypes.c_void_p(c.data_ptr()), ctypes.c_void_p(s.data_ptr()),
+                                ctypes.c_void_p(staging.data_ptr()), nbytes,
+                                ctypes.c_void_p(enc.cuda_stream),
+                                ctypes.c_void_p(copy.cuda_stream))
+        assert rc == 0, L.tq_last_error()
+    torch.cuda.synchronize()
+    for W, (c, s) in zip(Ws, outs):
+        ref = tq.encode(W.cuda(), levels, group, 9)
+        torch.cuda.synchronize()
+        assert torch.equal(c, ref.codes[0])
+        assert torch.equal(s.view(torch.int16), ref.scales[0].view(torch.int16))

@@ -448,3 +448,23 @@ def test_gather_and_multi_gather_pre_rotated_inputs():
     for k, e in enumerate(pids):
         want, bound = qmv_reference(codes[e], scales[e], levels, group, K, 6, X[k])
         check_outputs(as_f64(y[k]), want, bound + 1e-6 * np.abs(want), f"multi_gather {k}")
+
+
+@pytest.mark.parametrize("K", [4096, 1536])
+def test_rotation_comes_from_the_sign_bits_alone(K):
+    # the descriptor holds the sign bits and no seed: a weight encoded with seed 3 but given
+    # the sign bits of seed 8 is applied with seed 8's rotation (the oracle's qmv with seed
+    # 8 on the same codes), and with its own sign bits it matches seed 3
+    levels, group, N = 16, 64, 64
+    g = wl.rng(975, K)
+    W = to_dev(wl.student_rows(g, N, K), torch.bfloat16)
+    x = to_dev(wl.gaussian(g, 1, K)[0], torch.bfloat16)
+    qw = tq.encode(W, levels, group, 3)
+    other = tq.QWeight(qw.codes, qw.scales, tq.signs(8, K), levels, group, K, N, 1, 8)
+    y_own, y_other = tq.qmv(qw, x), tq.qmv(other, x)
+    torch.cuda.synchronize()
+    codes, scales = gpu_arrays(qw)
+    for y, seed in ((y_own, 3), (y_other, 8)):
+        want, bound = qmv_reference(codes[0], scales[0], levels, group, K, seed, as_f64(x))
+        check_outputs(as_f64(y), want, bound, f"signs of seed {seed}")
+    assert not torch.allclose(y_own, y_other)

@@ -66,10 +66,24 @@ def test_words_per_row():
 
 
 def desc(**kw):
-    d = dict(codes=16, scales=16, signs=16, n_levels=16, group=64, K=512, N=4, E=1, seed=0)
+    d = dict(codes=16, scales=16, signs=16, n_levels=16, group=64, K=512, N=4, E=1)
     d.update(kw)
     return tq._QWeight(d["codes"], d["scales"], d["signs"], d["n_levels"], d["group"], d["K"],
-                       d["N"], d["E"], d["seed"])
+                       d["N"], d["E"])
+
+
+def test_descriptor_holds_one_rotation():
+    # tq_qweight carries the sign bits and no seed: the header's struct and the binding's
+    # mirror of it list the same fields, in the same order, and "seed" is not one of them
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct \{(.*?)\} tq_qweight;", text, flags=re.S).group(1)
+    fields = re.findall(r"\b(\w+)\s*[;,]", body)
+    assert fields == [f[0] for f in tq._QWeight._fields_], fields
+    assert "seed" not in fields and "signs" in fields
+    assert ctypes.sizeof(tq._QWeight) == 3 * 8 + 2 * 4 + 3 * 8
+    # without sign bits there is no rotation: rejected before any launch
+    assert qmv_status(desc(signs=0)) == ERR_ARG
+    assert b"signs" in tq.lib().tq_last_error()
 
 
 def qmv_status(d, x=16, xdt=0, y=16, ydt=0):

@@ -169,3 +169,27 @@ def test_dequant_worked_examples():
     want = np.array([c3[t] * sv[j // 16] for j, t in enumerate(tidx)])
     np.testing.assert_array_equal(got, want)
     assert c3[1] == 0.0 and c3[0] == -c3[2]
+
+
+# Thresholds of the 3-level and 8-level codebooks written out from the closed form and the
+# Max (1960) table rather than taken from the oracle: the ternary midpoint c/2 with c the
+# root of c = phi(c/2) / (1 - Phi(c/2)), and the 3-bit midpoints of the pinned centroids.
+HAND_THRESHOLDS = {3: [-0.6120, 0.6120], 8: [-1.7479, -1.0500, -0.5005, 0.0, 0.5005, 1.0500, 1.7479]}
+
+
+@pytest.mark.parametrize("levels", [3, 8])
+def test_near_threshold_band_edges(levels):
+    # u placed 0.9e-6 and 1.1e-6 from each threshold (the band is 1e-6 wide in normalized
+    # units); the hand values above locate the thresholds to 1e-4, then the exact fp64
+    # threshold is the one the oracle uses, so the offsets are taken from it
+    t = cb.thresholds(levels)
+    assert np.allclose(t, HAND_THRESHOLDS[levels], atol=1.5e-4)
+    inside = np.concatenate([t - 0.9e-6, t + 0.9e-6, t])
+    outside = np.concatenate([t - 1.1e-6, t + 1.1e-6])
+    assert np.all(enc.near_threshold(inside, levels, 1e-6))
+    assert not np.any(enc.near_threshold(outside, levels, 1e-6))
+    # far from every threshold, including the centroids themselves and large |u|
+    far = np.concatenate([cb.centroids(levels), [-9.0, 9.0]])
+    assert not np.any(enc.near_threshold(far, levels, 1e-6))
+    # the mask keeps the input's shape
+    assert enc.near_threshold(inside.reshape(-1, 1), levels).shape == (inside.size, 1)
