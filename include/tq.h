@@ -180,6 +180,22 @@ int tq_multi_gather_qmv(const tq_qweight *w, const int32_t *ids, int64_t P, cons
                         tq_dtype x_dtype, void *y, tq_dtype y_dtype, uint32_t flags, void *ws,
                         size_t ws_bytes, void *stream);
 
+/* tq_multi_gather_qmv with no workspace argument and no allocation of any kind, for
+ * callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc). Its workspace is one fixed array of 8 MiB per GPU,
+ * held from the first such call on that GPU until the process ends; the call uses the
+ * array of the device current on the calling thread (`stream` must belong to it). Arguments,
+ * kernels and results are those of tq_multi_gather_qmv. Limit: the workspace
+ * tq_workspace_bytes(TQ_OP_MULTI_GATHER_QMV, w, P, 0) must fit in 8 MiB (about
+ * 2 (P + 1) (K + 4) bytes: about 2000 pairs at K = 2048, or 500 at K = 8192); a larger call returns
+ * TQ_ERR_WORKSPACE before anything is launched. Every call on one GPU shares the array and
+ * nothing in it must start at zero (each call writes all it reads); calls that overlap in
+ * time on one GPU (different streams, or several host threads) race on it and give wrong
+ * results; calls on one stream are ordered and safe. */
+int tq_multi_gather_qmv_static(const tq_qweight *w, const int32_t *ids, int64_t P,
+                               const void *x, tq_dtype x_dtype, void *y, tq_dtype y_dtype,
+                               uint32_t flags, void *stream);
+
 /* Batched gather-GEMM over rows sorted by expert ("Running a quantized layer", kernel
  * table, third row): for offsets[e] <= m < offsets[e+1], y[m] = W_e R x[row_token[m]].
  * x device [T][K]; row_token device int32 [M]; expert_offsets device int32 [E+1],

@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "TqError", "QWeight", "lib", "codebook", "words_per_row", "signs", "encode", "fwht",
     "qmv", "gather_qmv", "multi_gather_qmv", "gather_qmm", "workspace_bytes", "dequant",
-    "encode_stream",
+    "encode_stream", "multi_gather_qmv_static",
     "F32", "BF16", "F16", "X_ROTATED",
 ]
 
@@ -65,6 +65,8 @@ SIGNATURES = [
      [_QW, _P, _I32, _P, ctypes.c_int, _P, ctypes.c_int, _U32, _P, _SZ, _P]),
     ("tq_multi_gather_qmv", ctypes.c_int,
      [_QW, _P, _I64, _P, ctypes.c_int, _P, ctypes.c_int, _U32, _P, _SZ, _P]),
+    ("tq_multi_gather_qmv_static", ctypes.c_int,
+     [_QW, _P, _I64, _P, ctypes.c_int, _P, ctypes.c_int, _U32, _P]),
     ("tq_gather_qmm", ctypes.c_int,
      [_QW, _P, ctypes.c_int, _I64, _P, _P, _I64, _P, ctypes.c_int, _U32, _P, _SZ, _P]),
     ("tq_dequant", ctypes.c_int, [_QW, _P, _I64, _P, ctypes.c_int, _P]),
@@ -313,6 +315,21 @@ def multi_gather_qmv(qw, ids, X, out_dtype=torch.float32, rotated=False, out=Non
     _check(lib().tq_multi_gather_qmv(ctypes.byref(d), _ptr(ids), P, _ptr(X), _dt(X), _ptr(y),
                                      _dt(y), X_ROTATED if rotated else 0, _ptr(ws), nbytes,
                                      _stream()))
+    return y
+
+
+def multi_gather_qmv_static(qw, ids, X, out_dtype=torch.float32, rotated=False, out=None):
+    """multi_gather_qmv with the library's fixed per-GPU workspace (no allocation in the
+    library; at most 8 MiB of workspace, see tq.h)."""
+    X = X.contiguous()
+    ids = ids.to(torch.int32).contiguous()
+    P = ids.numel()
+    y = out if out is not None else torch.empty((P, qw.N), dtype=out_dtype, device=X.device)
+    d = qw.desc()
+    with torch.cuda.device(X.device):
+        _check(lib().tq_multi_gather_qmv_static(ctypes.byref(d), _ptr(ids), P, _ptr(X), _dt(X),
+                                                _ptr(y), _dt(y), X_ROTATED if rotated else 0,
+                                                _stream(X.device)))
     return y
 
 

@@ -57,6 +57,10 @@ hipError_t launch_rot16(const void* x, int xdt, const int32_t* rows, int64_t nro
                         int64_t zero_rows, const WeightArgs& w, bool x_rotated, _Float16* out,
                         float* scale, const BucketJob* bucket, hipStream_t s);
 size_t multi_gather_workspace(const WeightArgs& w, int64_t P);
+// The fixed per-GPU workspace of tq_multi_gather_qmv_static (device address on the current
+// device, resolved once per device).
+constexpr size_t kStaticScratchBytes = size_t(8) << 20;
+hipError_t static_scratch(void** ptr);
 hipError_t launch_multi_gather(const WeightArgs& w, const int32_t* ids, int64_t P,
                                const void* x, int xdt, bool x_rotated, void* y, int ydt,
                                void* ws, hipStream_t s);

@@ -11,6 +11,8 @@
 //              multiplies them by the rotated inputs of up to 16 of the expert's pairs at a
 //              time with v_mfma_f32_16x16x32_f16, so every code word is read from memory
 //              and decoded once per 16 pairs, whatever the number of pairs.
+#include <mutex>
+
 #include "internal.hpp"
 #include "mfma_decode.hpp"
 #include "rot16.hpp"
@@ -248,6 +250,35 @@ __global__ __launch_bounds__(kMgThreads, 4) void k_mg(MgParams p) {
       }
     }
   }
+}
+
+// The workspace of tq_multi_gather_qmv_static: one fixed array per GPU, for callers that
+// cannot allocate. Host code never passes `scratch` itself (on the host it names a stand-in,
+// not device memory): static_scratch() resolves its address on the current device once
+// and the kernels receive that address like any other workspace.
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t static_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_multi_gather(const WeightArgs& w, const int32_t* ids, int64_t P, const void* x,

@@ -383,6 +383,32 @@ int tq_multi_gather_qmv(const tq_qweight* w, const int32_t* ids, int64_t P, cons
                     "tq_multi_gather_qmv");
 }
 
+int tq_multi_gather_qmv_static(const tq_qweight* w, const int32_t* ids, int64_t P,
+                               const void* x, tq_dtype x_dtype, void* y, tq_dtype y_dtype,
+                               uint32_t flags, void* stream) {
+  WeightArgs a{};
+  int rc = check_weight(w, &a);
+  if (rc != TQ_OK) return rc;
+  if (P < 0 || P > (1 << 30)) return fail(TQ_ERR_ARG, "P out of range");
+  if (P > 0 && !ids) return fail(TQ_ERR_ARG, "ids is NULL");
+  if (P > 0 && !aligned(ids, 4)) return fail(TQ_ERR_ALIGN, "ids misaligned");
+  rc = check_io(x, x_dtype, y, y_dtype, P > 0 && a.N > 0);
+  if (rc != TQ_OK) return rc;
+  if (P == 0 || a.N == 0) return TQ_OK;
+  const size_t need = multi_gather_workspace(a, P);
+  if (need > kStaticScratchBytes)
+    return fail(TQ_ERR_WORKSPACE,
+                "tq_multi_gather_qmv_static: %lld pairs of K=%d need %zu bytes of workspace, "
+                "above the fixed %zu (use tq_multi_gather_qmv with a workspace)",
+                static_cast<long long>(P), a.K, need, kStaticScratchBytes);
+  void* ws = nullptr;
+  rc = hip_status(static_scratch(&ws), "tq_multi_gather_qmv_static");
+  if (rc != TQ_OK) return rc;
+  return hip_status(launch_multi_gather(a, ids, P, x, x_dtype, (flags & TQ_X_ROTATED) != 0, y,
+                                        y_dtype, ws, static_cast<hipStream_t>(stream)),
+                    "tq_multi_gather_qmv_static");
+}
+
 int tq_dequant(const tq_qweight* w, const int32_t* ids, int64_t n, void* out,
                tq_dtype out_dtype, void* stream) {
   WeightArgs a{};

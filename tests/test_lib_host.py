@@ -35,7 +35,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     handle = ctypes.CDLL(tq.LIB_PATH)
     for n in names:
         assert hasattr(handle, n), n
@@ -144,6 +144,14 @@ def test_validation_statuses():
     assert b"fewer than two rows" in L.tq_last_error()
     assert es(16, 3, 4, 512, 16, 64, 0, 16, 16, 256, 1 << 20, None, None) == ERR_ARG
     assert es(16, 0, 0, 512, 16, 64, 0, 16, 16, 256, 0, None, None) == 0
+    # the allocation-free multi_gather refuses a call whose workspace exceeds its fixed 8 MiB
+    # (4000 pairs of K = 2048), before touching the device
+    d2 = desc(E=4, K=2048, n_levels=3, group=16)
+    assert L.tq_multi_gather_qmv_static(ctypes.byref(d2), 16, 4000, 16, 1, 16, 0, 0,
+                                        None) == ERR_WORKSPACE
+    assert b"8388608" in L.tq_last_error()
+    assert L.tq_multi_gather_qmv_static(ctypes.byref(d2), None, 4, 16, 1, 16, 0, 0,
+                                        None) == ERR_ARG
     # workspace query with a bad descriptor
     assert L.tq_workspace_bytes(3, None, 1, 0) == ctypes.c_size_t(-1).value
     assert L.tq_workspace_bytes(9, ctypes.byref(desc()), 1, 0) == ctypes.c_size_t(-1).value
