@@ -1,5 +1,7 @@
 // Encode kernel: rotate -> group RMS -> fp16 scale -> snap -> pack, one row at a time per
-// workgroup (grid-stride over rows).
+// workgroup (grid-stride over rows). Rows of 12, 20 or 28 times a power of two, rows of
+// 8192, and sources not 16-byte aligned take this kernel; power-of-two rows up to 4096
+// take k_encode_p2 (encode_p2.hip).
 //
 // Steps (turboquant-mlx "How it works", "Quantizing a weight, with no data"; "The ternary
 // tier (1.58 bits)"):
@@ -141,6 +143,9 @@ hipError_t launch_encode(const void* W, int wdt, int64_t rows, int K, int m, int
                          int group, uint64_t seed, uint32_t* codes, uint16_t* scales,
                          hipStream_t s) {
   if (rows == 0) return hipSuccess;
+  // power-of-two rows up to 4096 long, read with 16-byte loads: the register kernel
+  if (encode_p2_supported(K, m) && (reinterpret_cast<uintptr_t>(W) & 15) == 0)
+    return launch_encode_p2(W, wdt, rows, K, levels, group, seed, codes, scales, s);
   switch (wdt) {
     case 0: return launch_encode_l<0>(W, rows, K, m, P, levels, group, seed, codes, scales, s);
     case 1: return launch_encode_l<1>(W, rows, K, m, P, levels, group, seed, codes, scales, s);

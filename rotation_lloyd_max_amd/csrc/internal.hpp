@@ -40,6 +40,10 @@ hipError_t launch_fwht(const void* x, int xdt, int64_t rows, int K, int m, int P
 hipError_t launch_encode(const void* W, int wdt, int64_t rows, int K, int m, int P,
                          int levels, int group, uint64_t seed, uint32_t* codes,
                          uint16_t* scales, hipStream_t s);
+// The register-resident encode for K = 2^p, 64 <= K <= 4096 (W 16-byte aligned).
+bool encode_p2_supported(int K, int m);
+hipError_t launch_encode_p2(const void* W, int wdt, int64_t rows, int K, int levels, int group,
+                            uint64_t seed, uint32_t* codes, uint16_t* scales, hipStream_t s);
 
 // qmv (ids == nullptr, n = 1) and gather_qmv.
 // out[k] = decoded weights of expert ids[k] (k when ids is null) in the rotated basis.

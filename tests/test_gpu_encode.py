@@ -70,17 +70,46 @@ def test_encode_configs(levels, group, K, rows, dtype):
         assert n == 0  # the small layer must be bit-exact
 
 
+DTYPES = [torch.float16, torch.bfloat16, torch.float32]
+
+
 @pytest.mark.parametrize("levels", [3, 4, 8, 16])
 @pytest.mark.parametrize("group", [16, 32, 64, 128])
-def test_encode_all_formats(levels, group):
-    K = 1536  # 12 * 128: exercises the 12-point Hadamard factor with every group size
-    g = wl.rng(902, levels, group)
-    W = to_dev(wl.student_rows(g, 40, K), torch.float16)
+@pytest.mark.parametrize("K", [1536, 2048, 256, 4096, 128])
+def test_encode_all_formats(levels, group, K):
+    # K = 12 * 128 takes the 12-point factor; the powers of two take the register kernel
+    # in each of its layouts (one exchange for K <= 512, two for K >= 1024); 41 rows leave
+    # a partial batch of rows
+    if group > K:
+        pytest.skip("group larger than the row")
+    g = wl.rng(902, levels * 1000 + group, K)
+    dtype = DTYPES[(levels + group // 16 + K // 128) % 3]
+    W = to_dev(wl.student_rows(g, 41, K), dtype)
     qw = tq.encode(W, levels, group, seed=3)
     torch.cuda.synchronize()
     ref = oenc.encode(as_f64(W), levels, group, 3)
-    check_codes(torch_to_np(qw.codes).reshape(40, -1), ref, levels, K)
-    check_scales(torch_to_np(qw.scales).reshape(40, -1), ref)
+    check_codes(torch_to_np(qw.codes).reshape(41, -1), ref, levels, K)
+    check_scales(torch_to_np(qw.scales).reshape(41, -1), ref)
+
+
+@pytest.mark.parametrize("K", [64, 128, 256, 512, 1024, 2048, 4096])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_encode_power_of_two_rows(K, dtype):
+    # every power-of-two row length of the register kernel, every input dtype, with edge
+    # rows (zero, constant, huge and tiny magnitudes) among ordinary ones
+    levels, group = 16, 64 if K >= 64 else K
+    g = wl.rng(908, K)
+    W = wl.student_rows(g, 70, K)
+    W[3] = 0.0
+    W[5, :] = 1.0
+    W[7] *= 1e2 if dtype == torch.float16 else 1e6  # fp16 holds at most 65504
+    W[9] *= 1e-3 if dtype == torch.float16 else 1e-6
+    Wd = to_dev(W, dtype)
+    qw = tq.encode(Wd, levels, group, seed=17)
+    torch.cuda.synchronize()
+    ref = oenc.encode(as_f64(Wd), levels, group, 17)
+    check_codes(torch_to_np(qw.codes).reshape(70, -1), ref, levels, K)
+    check_scales(torch_to_np(qw.scales).reshape(70, -1), ref)
 
 
 def test_encode_edge_rows():
