@@ -16,8 +16,15 @@ not in the timed region.
           passes recorded in profiles/ (scaled by a copy kernel of known size); null
           when the kernel sources no longer match the ones those counters were taken on
   encode_mweights_per_s  16,777,216 weights / the encode time of a step
+  encode  Mweights/s, GB/s and fraction of HBM peak of that encode (bytes = bf16 source +
+          packed codes + fp16 scales, 2.39 B per weight) and of the MoE decode layer's
+          gate stack (7168-wide rows: the 28-point Hadamard factor) and down stack, timed
+          with HIP events around each encode call as the stacks are built
+  gather_qmv  the MoE decode step (384 experts; gate, up, down of 8 routed experts): GB/s
+          of the routed experts' codes + scales + inputs per step, fraction of HBM peak
   cpu_baseline  the fp64 oracle (numpy, one BLAS thread) on a bounded sample of the same
-          layer, in the same unit
+          layer, in the same unit; host_cpu_count and host_affinity give the host's logical
+          CPUs and the ones this process may use (one is used)
 
 Other workloads (--config 3, 4, 5, 6, 7) time gather_qmv, multi_gather_qmv, gather_qmm,
 dequant and the streamed encode from pinned host memory for reference; the default line is
@@ -47,6 +54,8 @@ def parse():
                          "5 gather_qmm, 6 dequant of an expert stack, 7 encode of an "
                          "expert stack streamed from pinned host memory")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-moe", action="store_true",
+                    help="default line without the MoE decode (gather_qmv) sub-measurement")
     ap.add_argument("--calls", type=int, default=1000, help="qmv calls per step")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB device buffer 5 times (a plain copy kernel of "
@@ -80,6 +89,8 @@ def cpu_baseline_qmv(W_bits, x_bits, levels, group, seed, budget_s=12.0, rows=51
         "value": round(nbytes * n / t_q / 1e9, 6),
         "unit": "GB/s",
         "cores": 1,
+        "host_cpu_count": os.cpu_count(),
+        "host_affinity": len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": f"oracle (numpy fp64, 1 BLAS thread) qmv of the first {rows} of 4096 rows "
                   f"of the layer, {n} calls in {t_q:.1f} s; oracle encode of those rows "
@@ -226,13 +237,97 @@ def bench_dense(args):
             "traffic": recorded_traffic("k_qmv_dense_4096x4096_3bit_g128.md", QMV_SOURCES),
         },
     }
+    enc_rates = {"dense 4096x4096 bf16 -> 3-bit g128 (once per step)":
+                 encode_rate(N * K * steps, enc_ms, 2, L, G)}
+    del copies, base
+    torch.cuda.empty_cache()
+    if not args.no_moe:
+        moe = moe_decode_measure(steps=max(20, args.steps * 2), warmup=args.warmup)
+        for k, v in moe.pop("encode").items():
+            enc_rates[k] = v
+        out["gather_qmv"] = moe
+    out["encode"] = enc_rates
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_qmv(W_bits, x_bits, L, G, p.seed)
     return out
 
 
-def encode_stack(E, N, K, levels, group, seed, cfg, tensor, dev, chunk=16):
-    """Encode an expert stack whose bf16 weights are drawn on the GPU, chunk by chunk."""
+def moe_decode_measure(steps, warmup):
+    """The MoE decode layer (384 experts, hidden 7168, intermediate 2048; gate and up 2-bit
+    g64, down 4-bit g64): every step routes one token to 8 experts drawn uniformly and runs
+    gather_qmv for gate, up (shared 7168-wide input) and down (2048-wide input). Steps are
+    captured 20 to a graph with 20 different routings and timed with HIP events around the
+    replays. Bytes per step = the 8 routed experts' codes and scales of the three
+    projections + the bf16 inputs (128,450,560 + 32,768 B). Also returns the encode rates of
+    the stacks as they are built (HIP events around each encode call)."""
+    import numpy as np
+    import torch
+    import rotation_lloyd_max_amd as tq
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    c = wl.C3
+    timing = {}
+    layer = {}
+    for pr in c.projs:
+        t = [] if pr.name != "up" else None
+        layer[pr.name] = encode_stack(c.E, pr.N, pr.K, pr.levels, pr.group, pr.seed, c.cid,
+                                      wl.PROJ_TENSOR[pr.name], dev, timing=t)
+        if t:
+            timing[pr.name] = (pr, t[0])
+    wbytes = {pr.name: layer[pr.name].codes.numel() * 4 // c.E +
+              layer[pr.name].scales.numel() * 2 // c.E for pr in c.projs}
+    per_graph = 20
+    K1, K2 = c.projs[0].K, c.projs[2].K
+    ids = torch.from_numpy(np.stack([wl.decode_ids(c.cid, s, c.E, 8)
+                                     for s in range(per_graph)])).to(dev)
+    x1 = torch.randn(K1, generator=wl.torch_generator(dev, c.cid, wl.T_X), device=dev).to(torch.bfloat16)
+    x2 = torch.randn(K2, generator=wl.torch_generator(dev, c.cid, wl.T_XD), device=dev).to(torch.bfloat16)
+    ys = {pr.name: torch.empty((8, pr.N), dtype=torch.float32, device=dev) for pr in c.projs}
+
+    def step(s):
+        tq.gather_qmv(layer["gate"], ids[s], x1, out=ys["gate"])
+        tq.gather_qmv(layer["up"], ids[s], x1, out=ys["up"])
+        tq.gather_qmv(layer["down"], ids[s], x2, out=ys["down"])
+
+    for s in range(per_graph):
+        step(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for s in range(per_graph):
+            step(s)
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // per_graph)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    nsteps = reps * per_graph
+    ms_per_step = e0.elapsed_time(e1) / nsteps
+    bytes_step = 8 * sum(wbytes.values()) + 2 * K1 * 2 + K2 * 2
+    gbs = bytes_step / (ms_per_step / 1e3) / 1e9
+    enc = {}
+    for name, (pr, (w, ms)) in timing.items():
+        key = (f"MoE {name} stack {c.E}x{pr.N}x{pr.K} bf16 -> "
+               f"{ {4: '2-bit', 16: '4-bit'}[pr.levels]} g{pr.group}")
+        enc[key] = encode_rate(w, ms, 2, pr.levels, pr.group)
+    del layer
+    torch.cuda.empty_cache()
+    return {"metric": "gather_qmv HBM GB/s (MoE decode: gate+up+down of 8 routed experts)",
+            "value": round(gbs, 3), "unit": "GB/s", "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "ms_per_step": round(ms_per_step, 6), "steps": nsteps, "bytes_per_step": bytes_step,
+            "encode": enc}
+
+
+def encode_stack(E, N, K, levels, group, seed, cfg, tensor, dev, chunk=16, timing=None):
+    """Encode an expert stack whose bf16 weights are drawn on the GPU, chunk by chunk. With
+    `timing` (a list), the encode calls alone are timed with HIP events on the current
+    stream and (weights, milliseconds) is appended."""
     import torch
     import rotation_lloyd_max_amd as tq
     import workloads as wl
@@ -240,15 +335,33 @@ def encode_stack(E, N, K, levels, group, seed, cfg, tensor, dev, chunk=16):
     codes = torch.empty((E, N, wpr), dtype=torch.int32, device=dev)
     scales = torch.empty((E, N, K // group), dtype=torch.float16, device=dev)
     sg = tq.signs(seed, K, dev)
+    ms = 0.0
     for e0 in range(0, E, chunk):
         e1 = min(E, e0 + chunk)
         g = wl.torch_generator(dev, cfg, tensor, e0)
         Wc = wl.torch_student_rows(g, (e1 - e0) * N, K, dev, torch.bfloat16).view(e1 - e0, N, K)
         part = tq.QWeight(codes[e0:e1], scales[e0:e1], sg, levels, group, K, N, e1 - e0, seed)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
         tq.encode(Wc, levels, group, seed, out=part)
+        b.record()
+        if timing is not None:
+            b.synchronize()
+            ms += a.elapsed_time(b)
         del Wc
     torch.cuda.synchronize()
+    if timing is not None:
+        timing.append((E * N * K, ms))
     return tq.QWeight(codes, scales, sg, levels, group, K, N, E, seed)
+
+
+def encode_rate(weights, ms, src_bytes, levels, group):
+    """Encode throughput and its HBM fraction: bytes = source + packed codes + fp16 scales."""
+    bits = {3: 1.6, 4: 2, 8: 3, 16: 4}[levels]
+    per_w = src_bytes + bits / 8 + 2.0 / group
+    gbs = weights * per_w / (ms / 1e3) / 1e9
+    return {"mweights_per_s": round(weights / (ms / 1e3) / 1e6, 3), "bytes_per_weight": per_w,
+            "gb_per_s": round(gbs, 3), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def bench_moe(args):
@@ -260,6 +373,18 @@ def bench_moe(args):
 
     dev = torch.device("cuda:0")
     c = wl.CONFIGS[args.config]
+    if args.config == 3:
+        m = moe_decode_measure(args.steps, args.warmup)
+        return {
+            "metric": m["metric"], "value": m["value"], "unit": "GB/s", "n_gpus": 1,
+            "steps": m["steps"], "warmup": args.warmup, "ms_per_step": m["ms_per_step"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f16*f16->f32", "data": "synthetic",
+            "config": {"workload": c.name, "bytes_per_step": m["bytes_per_step"]},
+            "roofline": {"bound": "hbm", "achieved": m["value"], "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": m["frac_of_hbm_peak"], "traffic": None},
+            "encode": m["encode"],
+        }
     ncopy = 3 if args.config == 4 else 1
     layers = []
     for _ in range(ncopy):
@@ -269,22 +394,7 @@ def bench_moe(args):
     wbytes = {pr.name: layers[0][pr.name].codes.numel() * 4 // c.E +
               layers[0][pr.name].scales.numel() * 2 // c.E for pr in c.projs}
     steps_per_graph = 20
-    if args.config == 3:
-        K1, K2 = c.projs[0].K, c.projs[2].K
-        ids = torch.from_numpy(np.stack([wl.decode_ids(c.cid, s, c.E, 8)
-                                         for s in range(steps_per_graph)])).to(dev)
-        x1 = torch.randn(K1, generator=wl.torch_generator(dev, c.cid, wl.T_X), device=dev).to(torch.bfloat16)
-        x2 = torch.randn(K2, generator=wl.torch_generator(dev, c.cid, wl.T_XD), device=dev).to(torch.bfloat16)
-        ys = {pr.name: torch.empty((8, pr.N), dtype=torch.float32, device=dev) for pr in c.projs}
-
-        def step(s):
-            L = layers[0]
-            tq.gather_qmv(L["gate"], ids[s], x1, out=ys["gate"])
-            tq.gather_qmv(L["up"], ids[s], x1, out=ys["up"])
-            tq.gather_qmv(L["down"], ids[s], x2, out=ys["down"])
-        bytes_step = 8 * sum(wbytes.values()) + 2 * K1 * 2 + K2 * 2
-        unit, metric = "GB/s", "gather_qmv HBM GB/s (MoE decode: gate+up+down of 8 routed experts)"
-    elif args.config == 4:
+    if args.config == 4:
         P = 64 * 8
         ids_np = wl.topk_routing(c.cid, 64, c.E, 8)
         ids = torch.from_numpy(ids_np).to(dev)
