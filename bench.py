@@ -26,9 +26,9 @@ not in the timed region.
           layer, in the same unit; host_cpu_count and host_affinity give the host's logical
           CPUs and the ones this process may use (one is used)
 
-Other workloads (--config 3, 4, 5, 6, 7) time gather_qmv, multi_gather_qmv, gather_qmm,
-dequant and the streamed encode from pinned host memory for reference; the default line is
-the dense decode layer.
+Other workloads (--config 3, 4, 5, 6, 7, 8) time gather_qmv, multi_gather_qmv, gather_qmm,
+dequant, the streamed encode from pinned host memory and the MoE decode with its experts
+streamed from pinned host memory, for reference; the default line is the dense decode layer.
 """
 
 import argparse
@@ -49,10 +49,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5, 6, 7],
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5, 6, 7, 8],
                     help="2 dense qmv (default), 3 gather_qmv, 4 multi_gather_qmv, "
                          "5 gather_qmm, 6 dequant of an expert stack, 7 encode of an "
-                         "expert stack streamed from pinned host memory")
+                         "expert stack streamed from pinned host memory, 8 MoE decode with "
+                         "its experts streamed from pinned host memory")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-moe", action="store_true",
                     help="default line without the MoE decode (gather_qmv) sub-measurement")
@@ -614,6 +615,72 @@ def bench_encode_stream(args):
     }
 
 
+def bench_expert_stream(args):
+    """The MoE decode layer with its experts streamed from pinned host memory: gate, up and
+    down stacks (384 experts each, 6.2 GB) stay on the host, 64 device slots per projection
+    hold the experts in use (least recently used out), and each step fetches the 8 routed
+    experts (uniform routing) before its three gather_qmv calls. Reported: step time, the
+    host-to-device bytes of the step's copies (PCIe included), and the hit rate."""
+    import numpy as np
+    import torch
+    import rotation_lloyd_max_amd as tq
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    c = wl.C3
+    slots = 64
+    caches, copy = {}, torch.cuda.Stream(device=dev)
+    per_expert = {}
+    for pr in c.projs:
+        qw = encode_stack(c.E, pr.N, pr.K, pr.levels, pr.group, pr.seed, c.cid,
+                          wl.PROJ_TENSOR[pr.name], dev)
+        host = tq.QWeight(qw.codes.cpu().pin_memory(), qw.scales.cpu().pin_memory(), qw.signs,
+                          pr.levels, pr.group, pr.K, pr.N, c.E, pr.seed)
+        per_expert[pr.name] = qw.codes[0].numel() * 4 + qw.scales[0].numel() * 2
+        del qw
+        torch.cuda.empty_cache()
+        caches[pr.name] = tq.ExpertCache(host, slots, copy_stream=copy)
+    K1, K2 = c.projs[0].K, c.projs[2].K
+    x1 = torch.randn(K1, generator=wl.torch_generator(dev, c.cid, wl.T_X), device=dev).to(torch.bfloat16)
+    x2 = torch.randn(K2, generator=wl.torch_generator(dev, c.cid, wl.T_XD), device=dev).to(torch.bfloat16)
+    ys = {pr.name: torch.empty((8, pr.N), dtype=torch.float32, device=dev) for pr in c.projs}
+    total = args.warmup + args.steps
+    routes = [wl.decode_ids(c.cid, s, c.E, 8) for s in range(total)]
+
+    def step(s):
+        moved = 0
+        for name, x in (("gate", x1), ("up", x1), ("down", x2)):
+            sid, n = caches[name].fetch(routes[s])
+            tq.gather_qmv(caches[name].pool, sid, x, out=ys[name])
+            moved += n * per_expert[name]
+        return moved
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    moved = sum(step(args.warmup + s) for s in range(args.steps))
+    b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = a.elapsed_time(b) / args.steps
+    hits = sum(cch.stats()[0] for cch in caches.values())
+    misses = sum(cch.stats()[1] for cch in caches.values())
+    gbs = moved / args.steps / (ms / 1e3) / 1e9
+    return {
+        "metric": "streamed MoE decode: host-to-device GB/s of expert copies (PCIe included)",
+        "value": round(gbs, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16*f16->f32", "data": "synthetic",
+        "config": {"workload": c.name + "; experts in pinned host memory, 64 device slots per "
+                               "projection, uniform routing", "slots": slots,
+                   "bytes_copied_per_step": moved // args.steps},
+        "hit_rate": round(hits / max(1, hits + misses), 4), "wall_s": round(wall, 4),
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -636,6 +703,8 @@ def main():
         out = bench_dequant(args)
     elif args.config == 7:
         out = bench_encode_stream(args)
+    elif args.config == 8:
+        out = bench_expert_stream(args)
     else:
         out = bench_moe(args)
     print(json.dumps(out), flush=True)

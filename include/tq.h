@@ -219,6 +219,49 @@ int tq_gather_qmm(const tq_qweight *w, const void *x, tq_dtype x_dtype, int64_t 
 int tq_dequant(const tq_qweight *w, const int32_t *ids, int64_t n, void *out,
                tq_dtype out_dtype, void *stream);
 
+/* Expert streaming (turboquant-mlx "How it works", "Expert streaming": experts are read on
+ * demand through an LRU cache, with results bit-identical to a model held in memory). The
+ * packed experts stay in HOST memory; a caller-owned device pool of `slots` expert slots
+ * holds the ones in use, and a caller-owned host state (tq_expert_cache_bytes) keeps which
+ * expert sits in which slot. Each fetch makes the routed experts resident and writes their
+ * slot numbers to the device, so the usual layer calls run on the pool:
+ *     tq_expert_cache_fetch(state, host, pool, ids, n, slot_ids_dev, ...);
+ *     tq_gather_qmv(pool, slot_ids_dev, n, x, ...);   (or tq_multi_gather_qmv)
+ * and their outputs are bit-identical to the same calls on all E experts in device memory. */
+
+/* Bytes of host state for `slots` slots over E experts (SIZE_MAX for slots or E outside
+ * [1, 8192]). */
+size_t tq_expert_cache_bytes(int32_t slots, int64_t E);
+
+/* Empties the cache: `state` host, 8-byte aligned, state_bytes >= tq_expert_cache_bytes.
+ * Returns TQ_OK, TQ_ERR_ARG or TQ_ERR_ALIGN. */
+int tq_expert_cache_init(void *state, size_t state_bytes, int32_t slots, int64_t E);
+
+/* Makes experts ids_host[0..n) resident (n <= 512; repeats allowed; the distinct ones must
+ * fit the slots) and writes the slot of ids_host[k] to slot_ids_dev[k] (device int32 [n])
+ * and, when not NULL, to slot_ids_host[k]. Experts already resident are kept; each missing
+ * one takes the least recently used slot that this call does not need, and its codes and
+ * scales are copied from `host` into that slot of `pool`.
+ *   host   the packed weight with codes and scales in HOST memory, [E][N][..] as usual
+ *          (pinned memory lets the copies run asynchronously); its signs pointer is not
+ *          read here and may be the pool's
+ *   pool   a device weight of E = slots experts with the same n_levels, group, K and N;
+ *          its codes and scales are written here, its signs are those of the weight
+ *   copied when not NULL, the number of experts copied by this call
+ * Copies go on `copy_stream` (NULL: on `stream`) after the work already on `stream`, and
+ * `stream` waits for them, so a following call on `stream` sees the slots filled and no
+ * earlier one sees them change; the slot numbers are written on `stream`. `host` must stay
+ * valid and unchanged until the copies have run. Host-side errors (bad ids, too many
+ * distinct experts, mismatched descriptors) are found before anything is enqueued and leave
+ * the state unchanged; TQ_ERR_HIP leaves the state recording the new residency. */
+int tq_expert_cache_fetch(void *state, const tq_qweight *host, const tq_qweight *pool,
+                          const int32_t *ids_host, int32_t n, int32_t *slot_ids_dev,
+                          int32_t *slot_ids_host, int32_t *copied, void *stream,
+                          void *copy_stream);
+
+/* Total hits and misses (experts found resident / copied) since tq_expert_cache_init. */
+int tq_expert_cache_stats(const void *state, int64_t *hits, int64_t *misses);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char *tq_last_error(void);
 

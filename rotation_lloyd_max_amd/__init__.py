@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "TqError", "QWeight", "lib", "codebook", "words_per_row", "signs", "encode", "fwht",
     "qmv", "gather_qmv", "multi_gather_qmv", "gather_qmm", "workspace_bytes", "dequant",
-    "encode_stream", "multi_gather_qmv_static",
+    "encode_stream", "multi_gather_qmv_static", "ExpertCache",
     "F32", "BF16", "F16", "X_ROTATED",
 ]
 
@@ -72,6 +72,10 @@ SIGNATURES = [
     ("tq_dequant", ctypes.c_int, [_QW, _P, _I64, _P, ctypes.c_int, _P]),
     ("tq_encode_stream", ctypes.c_int,
      [_P, ctypes.c_int, _I64, _I64, _I32, _I32, _U64, _P, _P, _P, _SZ, _P, _P]),
+    ("tq_expert_cache_bytes", _SZ, [_I32, _I64]),
+    ("tq_expert_cache_init", ctypes.c_int, [_P, _SZ, _I32, _I64]),
+    ("tq_expert_cache_fetch", ctypes.c_int, [_P, _QW, _QW, _P, _I32, _P, _P, _P, _P, _P]),
+    ("tq_expert_cache_stats", ctypes.c_int, [_P, _P, _P]),
     ("tq_last_error", ctypes.c_char_p, []),
 ]
 
@@ -349,3 +353,56 @@ def gather_qmm(qw, X, row_token, offsets, out_dtype=torch.float32, rotated=False
                                _ptr(offsets), M, _ptr(y), _dt(y),
                                X_ROTATED if rotated else 0, _ptr(ws), nbytes, _stream()))
     return y
+
+
+class ExpertCache:
+    """Expert streaming: `host` is a QWeight whose codes and scales are CPU tensors (pinned
+    for asynchronous copies) and whose signs are on the device; `slots` experts at a time
+    live in a device pool, replaced least recently used first. fetch(ids) makes ids resident
+    and returns their slot numbers on the device; gather_qmv / multi_gather_qmv run the
+    layer on the pool with results bit-identical to the all-resident weight."""
+
+    def __init__(self, host, slots, device="cuda", copy_stream=None):
+        if host.codes.device.type != "cpu" or host.scales.device.type != "cpu":
+            raise ValueError("ExpertCache takes a weight whose codes and scales are in host memory")
+        self.host = host
+        self.device = torch.device(device)
+        self.copy_stream = copy_stream
+        nbytes = lib().tq_expert_cache_bytes(slots, host.E)
+        if nbytes == ctypes.c_size_t(-1).value:
+            raise ValueError("slots and E must be in [1, 8192]")
+        self.state = np.zeros((nbytes + 7) // 8, dtype=np.uint64)
+        _check(lib().tq_expert_cache_init(self.state.ctypes.data, self.state.nbytes, slots, host.E))
+        self.pool = QWeight(
+            torch.empty((slots,) + tuple(host.codes.shape[1:]), dtype=torch.int32, device=self.device),
+            torch.empty((slots,) + tuple(host.scales.shape[1:]), dtype=torch.float16, device=self.device),
+            host.signs, host.levels, host.group, host.K, host.N, slots, host.seed)
+        self.slot_ids = torch.empty(512, dtype=torch.int32, device=self.device)
+
+    def fetch(self, ids):
+        """Make experts `ids` (host ints) resident; returns (slot ids on the device, number
+        of experts copied)."""
+        ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32).reshape(-1))
+        n = ids.size
+        copied = ctypes.c_int32(0)
+        hd, pd = self.host.desc(), self.pool.desc()
+        cs = ctypes.c_void_p(self.copy_stream.cuda_stream) if self.copy_stream is not None else None
+        with torch.cuda.device(self.device):
+            _check(lib().tq_expert_cache_fetch(self.state.ctypes.data, ctypes.byref(hd),
+                                               ctypes.byref(pd), ids.ctypes.data, n,
+                                               _ptr(self.slot_ids), None, ctypes.byref(copied),
+                                               _stream(self.device), cs))
+        return self.slot_ids[:n], int(copied.value)
+
+    def stats(self):
+        h, m = ctypes.c_int64(0), ctypes.c_int64(0)
+        _check(lib().tq_expert_cache_stats(self.state.ctypes.data, ctypes.byref(h), ctypes.byref(m)))
+        return int(h.value), int(m.value)
+
+    def gather_qmv(self, ids, x, **kw):
+        sid, _ = self.fetch(ids)
+        return gather_qmv(self.pool, sid, x, **kw)
+
+    def multi_gather_qmv(self, ids, X, **kw):
+        sid, _ = self.fetch(ids)
+        return multi_gather_qmv(self.pool, sid, X, **kw)

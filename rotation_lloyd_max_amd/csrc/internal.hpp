@@ -74,4 +74,12 @@ hipError_t launch_gather_qmm(const WeightArgs& w, const void* x, int xdt, int64_
                              const int32_t* row_token, const int32_t* offsets, int64_t M,
                              bool x_rotated, void* y, int ydt, void* ws, hipStream_t s);
 
+// Up to kMaxSlotIds int32 values passed by value to a kernel (tq_expert_cache_fetch).
+constexpr int kMaxSlotIds = 512;
+struct SlotIds {
+  int32_t n;
+  int32_t v[kMaxSlotIds];
+};
+hipError_t launch_put_ids(const SlotIds& ids, int32_t* dst, hipStream_t s);
+
 }  // namespace tq

@@ -453,6 +453,181 @@ int tq_gather_qmm(const tq_qweight* w, const void* x, tq_dtype x_dtype, int64_t 
                     "tq_gather_qmm");
 }
 
+// ---- expert cache ------------------------------------------------------------------------
+// Host state (caller-owned memory): a header, then slot_expert[slots] (int32, -1 = empty),
+// slot_tick[slots] (uint64, the call that last used the slot), expert_slot[E] (int32, -1 =
+// not resident).
+namespace {
+constexpr uint64_t kCacheMagic = 0x7471657863616368ull;  // "tqexcach"
+struct CacheHeader {
+  uint64_t magic;
+  int64_t E;
+  uint64_t tick;
+  int64_t hits, misses;
+  int32_t slots, pad;
+};
+size_t align8(size_t n) { return (n + 7) & ~static_cast<size_t>(7); }
+size_t cache_bytes(int64_t slots, int64_t E) {
+  return sizeof(CacheHeader) + align8(static_cast<size_t>(slots) * 4) +
+         static_cast<size_t>(slots) * 8 + align8(static_cast<size_t>(E) * 4);
+}
+struct CacheView {
+  CacheHeader* h;
+  int32_t* slot_expert;
+  uint64_t* slot_tick;
+  int32_t* expert_slot;
+};
+CacheView cache_view(void* state) {
+  CacheView v{};
+  v.h = static_cast<CacheHeader*>(state);
+  char* p = static_cast<char*>(state) + sizeof(CacheHeader);
+  v.slot_expert = reinterpret_cast<int32_t*>(p);
+  p += align8(static_cast<size_t>(v.h->slots) * 4);
+  v.slot_tick = reinterpret_cast<uint64_t*>(p);
+  p += static_cast<size_t>(v.h->slots) * 8;
+  v.expert_slot = reinterpret_cast<int32_t*>(p);
+  return v;
+}
+}  // namespace
+
+size_t tq_expert_cache_bytes(int32_t slots, int64_t E) {
+  if (slots < 1 || slots > 8192 || E < 1 || E > 8192) return SIZE_MAX;
+  return cache_bytes(slots, E);
+}
+
+int tq_expert_cache_init(void* state, size_t state_bytes, int32_t slots, int64_t E) {
+  if (slots < 1 || slots > 8192 || E < 1 || E > 8192)
+    return fail(TQ_ERR_ARG, "slots and E must be in [1, 8192]");
+  if (!state) return fail(TQ_ERR_ARG, "state is NULL");
+  if (!aligned(state, 8)) return fail(TQ_ERR_ALIGN, "state must be 8-byte aligned");
+  if (state_bytes < cache_bytes(slots, E))
+    return fail(TQ_ERR_ARG, "state of %zu bytes needed (got %zu)", cache_bytes(slots, E),
+                state_bytes);
+  CacheHeader* h = static_cast<CacheHeader*>(state);
+  std::memset(h, 0, sizeof *h);
+  h->magic = kCacheMagic;
+  h->E = E;
+  h->slots = slots;
+  CacheView v = cache_view(state);
+  for (int32_t s = 0; s < slots; ++s) {
+    v.slot_expert[s] = -1;
+    v.slot_tick[s] = 0;
+  }
+  for (int64_t e = 0; e < E; ++e) v.expert_slot[e] = -1;
+  return TQ_OK;
+}
+
+int tq_expert_cache_fetch(void* state, const tq_qweight* host, const tq_qweight* pool,
+                          const int32_t* ids_host, int32_t n, int32_t* slot_ids_dev,
+                          int32_t* slot_ids_host, int32_t* copied, void* stream,
+                          void* copy_stream) {
+  if (!state || !aligned(state, 8) || static_cast<CacheHeader*>(state)->magic != kCacheMagic)
+    return fail(TQ_ERR_ARG, "state was not set up by tq_expert_cache_init");
+  CacheView v = cache_view(state);
+  WeightArgs hw{}, pw{};
+  int rc = check_weight(host, &hw);
+  if (rc != TQ_OK) return rc;
+  rc = check_weight(pool, &pw);
+  if (rc != TQ_OK) return rc;
+  if (hw.levels != pw.levels || hw.group != pw.group || hw.K != pw.K || hw.N != pw.N)
+    return fail(TQ_ERR_ARG, "host weight and slot pool differ in levels, group, K or N");
+  if (hw.E != v.h->E || pw.E != v.h->slots)
+    return fail(TQ_ERR_ARG, "host weight must have the cache's E experts and the pool its slots");
+  if (n < 0 || n > kMaxSlotIds) return fail(TQ_ERR_ARG, "n must be in [0, %d]", kMaxSlotIds);
+  if (n > 0 && (!ids_host || !slot_ids_dev)) return fail(TQ_ERR_ARG, "ids_host and slot_ids_dev needed");
+  if (n > 0 && !aligned(slot_ids_dev, 4)) return fail(TQ_ERR_ALIGN, "slot_ids_dev misaligned");
+  for (int32_t k = 0; k < n; ++k)
+    if (ids_host[k] < 0 || ids_host[k] >= hw.E)
+      return fail(TQ_ERR_ARG, "ids_host[%d] = %d is outside [0, %d)", k, ids_host[k], hw.E);
+  // distinct experts of this call must fit the pool
+  {
+    int32_t distinct = 0;
+    for (int32_t k = 0; k < n; ++k) {
+      bool seen = false;
+      for (int32_t j = 0; j < k && !seen; ++j) seen = ids_host[j] == ids_host[k];
+      distinct += seen ? 0 : 1;
+    }
+    if (distinct > pw.E)
+      return fail(TQ_ERR_ARG, "%d distinct experts do not fit %d slots", distinct, pw.E);
+  }
+  // residency: hits first (so that no expert this call needs is evicted), then misses take
+  // the least recently used slots that this call does not use
+  const uint64_t tick = ++v.h->tick;
+  for (int32_t k = 0; k < n; ++k) {
+    const int32_t s = v.expert_slot[ids_host[k]];
+    if (s >= 0) v.slot_tick[s] = tick;
+  }
+  int32_t load_e[kMaxSlotIds], load_s[kMaxSlotIds];
+  int32_t nload = 0;
+  SlotIds out{};
+  out.n = n;
+  for (int32_t k = 0; k < n; ++k) {
+    const int32_t e = ids_host[k];
+    int32_t s = v.expert_slot[e];
+    if (s < 0) {
+      int32_t best = -1;
+      for (int32_t c = 0; c < pw.E; ++c) {
+        if (v.slot_tick[c] == tick) continue;
+        if (best < 0 || v.slot_tick[c] < v.slot_tick[best]) best = c;
+      }
+      s = best;  // exists: distinct experts <= slots
+      if (v.slot_expert[s] >= 0) v.expert_slot[v.slot_expert[s]] = -1;
+      v.slot_expert[s] = e;
+      v.expert_slot[e] = s;
+      v.slot_tick[s] = tick;
+      load_e[nload] = e;
+      load_s[nload] = s;
+      ++nload;
+      ++v.h->misses;
+    } else {
+      ++v.h->hits;
+    }
+    out.v[k] = s;
+    if (slot_ids_host) slot_ids_host[k] = s;
+  }
+  if (copied) *copied = nload;
+  const hipStream_t cs = static_cast<hipStream_t>(stream);
+  const hipStream_t xs = copy_stream ? static_cast<hipStream_t>(copy_stream) : cs;
+  hipError_t e = hipSuccess;
+  if (nload > 0) {
+    const size_t cb = static_cast<size_t>(hw.N) * hw.wpr * 4;
+    const size_t sb = static_cast<size_t>(hw.N) * (hw.K / hw.group) * 2;
+    hipEvent_t entry = nullptr, done = nullptr;
+    // a slot being refilled may still be read by work already on `stream`
+    if (xs != cs) {
+      e = hipEventCreateWithFlags(&entry, hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventRecord(entry, cs);
+      if (e == hipSuccess) e = hipStreamWaitEvent(xs, entry, 0);
+    }
+    for (int32_t i = 0; i < nload && e == hipSuccess; ++i) {
+      const char* hc = reinterpret_cast<const char*>(hw.codes) + cb * load_e[i];
+      const char* hs = reinterpret_cast<const char*>(hw.scales) + sb * load_e[i];
+      char* dc = reinterpret_cast<char*>(const_cast<uint32_t*>(pw.codes)) + cb * load_s[i];
+      char* ds = reinterpret_cast<char*>(const_cast<uint16_t*>(pw.scales)) + sb * load_s[i];
+      e = hipMemcpyAsync(dc, hc, cb, hipMemcpyHostToDevice, xs);
+      if (e == hipSuccess) e = hipMemcpyAsync(ds, hs, sb, hipMemcpyHostToDevice, xs);
+    }
+    if (xs != cs && e == hipSuccess) {
+      e = hipEventCreateWithFlags(&done, hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventRecord(done, xs);
+      if (e == hipSuccess) e = hipStreamWaitEvent(cs, done, 0);
+    }
+    if (entry) (void)hipEventDestroy(entry);
+    if (done) (void)hipEventDestroy(done);
+  }
+  if (e == hipSuccess) e = launch_put_ids(out, slot_ids_dev, cs);
+  return hip_status(e, "tq_expert_cache_fetch");
+}
+
+int tq_expert_cache_stats(const void* state, int64_t* hits, int64_t* misses) {
+  if (!state || !aligned(state, 8) || static_cast<const CacheHeader*>(state)->magic != kCacheMagic)
+    return fail(TQ_ERR_ARG, "state was not set up by tq_expert_cache_init");
+  const CacheHeader* h = static_cast<const CacheHeader*>(state);
+  if (hits) *hits = h->hits;
+  if (misses) *misses = h->misses;
+  return TQ_OK;
+}
+
 const char* tq_last_error(void) { return g_err.c_str(); }
 
 }  // extern "C"

@@ -35,7 +35,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 14, names
+    assert len(names) == 18, names
     handle = ctypes.CDLL(tq.LIB_PATH)
     for n in names:
         assert hasattr(handle, n), n
@@ -152,6 +152,25 @@ def test_validation_statuses():
     assert b"8388608" in L.tq_last_error()
     assert L.tq_multi_gather_qmv_static(ctypes.byref(d2), None, 4, 16, 1, 16, 0, 0,
                                         None) == ERR_ARG
+    # expert cache: sizes, set-up checks, and fetches refused before anything is enqueued
+    assert L.tq_expert_cache_bytes(0, 10) == ctypes.c_size_t(-1).value
+    nb = L.tq_expert_cache_bytes(4, 10)
+    st = np.zeros(nb // 8 + 1, dtype=np.uint64)
+    assert L.tq_expert_cache_init(st.ctypes.data, nb - 1, 4, 10) == ERR_ARG
+    assert L.tq_expert_cache_init(st.ctypes.data + 4, nb, 4, 10) == ERR_ALIGN
+    assert L.tq_expert_cache_init(st.ctypes.data, nb, 4, 10) == 0
+    hostw, pool = desc(E=10), desc(E=4)
+    fetch = lambda ids, p=pool: L.tq_expert_cache_fetch(
+        st.ctypes.data, ctypes.byref(hostw), ctypes.byref(p),
+        np.asarray(ids, dtype=np.int32).ctypes.data, len(ids), 256, None, None, None, None)
+    assert fetch([0, 10]) == ERR_ARG                      # id outside [0, E)
+    assert fetch([0, 1, 2, 3, 4]) == ERR_ARG              # five distinct experts, four slots
+    assert fetch([1], desc(E=5)) == ERR_ARG               # pool is not the cache's slots
+    assert fetch([1], desc(E=4, group=32)) == ERR_ARG     # pool of another format
+    h, m = ctypes.c_int64(7), ctypes.c_int64(7)
+    assert L.tq_expert_cache_stats(st.ctypes.data, ctypes.byref(h), ctypes.byref(m)) == 0
+    assert (h.value, m.value) == (0, 0)                   # refused fetches left no trace
+    assert L.tq_expert_cache_stats(np.zeros(8, dtype=np.uint64).ctypes.data, None, None) == ERR_ARG
     # workspace query with a bad descriptor
     assert L.tq_workspace_bytes(3, None, 1, 0) == ctypes.c_size_t(-1).value
     assert L.tq_workspace_bytes(9, ctypes.byref(desc()), 1, 0) == ctypes.c_size_t(-1).value
