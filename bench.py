@@ -27,8 +27,9 @@ not in the timed region.
           CPUs and the ones this process may use (one is used)
 
 Other workloads (--config 3, 4, 5, 6, 7, 8) time gather_qmv, multi_gather_qmv, gather_qmm,
-dequant, the streamed encode from pinned host memory and the MoE decode with its experts
-streamed from pinned host memory, for reference; the default line is the dense decode layer.
+dequant, the streamed encode from pinned host memory, the MoE decode with its experts
+streamed from pinned host memory and the KV-cache fetch (--config 9), for reference; the
+default line is the dense decode layer.
 """
 
 import argparse
@@ -49,11 +50,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5, 6, 7, 8],
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5, 6, 7, 8, 9],
                     help="2 dense qmv (default), 3 gather_qmv, 4 multi_gather_qmv, "
                          "5 gather_qmm, 6 dequant of an expert stack, 7 encode of an "
                          "expert stack streamed from pinned host memory, 8 MoE decode with "
-                         "its experts streamed from pinned host memory")
+                         "its experts streamed from pinned host memory, 9 KV-cache fetch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-moe", action="store_true",
                     help="default line without the MoE decode (gather_qmv) sub-measurement")
@@ -681,6 +682,86 @@ def bench_expert_stream(args):
     }
 
 
+def bench_kv(args):
+    """KV-cache compression: a cache of 32,768 tokens x 8 KV heads x head_dim 128 with 8-bit
+    keys and 3-bit values (groups of 64), stored with tq_encode; one step fetches the whole
+    cache (both halves dequantized and rotated back to bf16), as a decode step that reads
+    every cached key and value would. Bytes per step = packed codes + fp16 scales read +
+    bf16 rows written. The store rate of the whole cache is reported beside it."""
+    import torch
+    import rotation_lloyd_max_amd as tq
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    T, H, d, g = 32768, 8, 128, 64
+    gen = wl.torch_generator(dev, 9, wl.T_X)
+    ch = torch.randperm(d, generator=torch.Generator().manual_seed(9))[:4]
+    Kx = torch.randn((T * H, d), generator=gen, device=dev)
+    Kx[:, ch.to(dev)] *= 20.0  # fixed outlier channels of attention keys
+    Kx = Kx.to(torch.bfloat16)
+    Vx = torch.randn((T * H, d), generator=gen, device=dev).to(torch.bfloat16)
+    kq = tq.encode(Kx, 256, g, 0)
+    vq = tq.encode(Vx, 8, g, 1)
+    ko = torch.empty((1, T * H, d), dtype=torch.bfloat16, device=dev)
+    vo = torch.empty_like(ko)
+    torch.cuda.synchronize()
+
+    def store():
+        tq.encode(Kx, 256, g, 0, out=kq)
+        tq.encode(Vx, 8, g, 1, out=vq)
+
+    def fetch():
+        tq.kv_fetch(kq, out=ko)
+        tq.kv_fetch(vq, out=vo)
+
+    per_graph = 5
+    gs, gf = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    store(); fetch()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(gs):
+        store()
+    with torch.cuda.graph(gf):
+        for _ in range(per_graph):
+            fetch()
+    for _ in range(args.warmup):
+        gs.replay(); gf.replay()
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // per_graph)
+    a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    t0 = time.perf_counter()
+    a.record()
+    for _ in range(reps):
+        gf.replay()
+    b.record()
+    for _ in range(reps):
+        gs.replay()
+    c.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    nsteps = reps * per_graph
+    ms = a.elapsed_time(b) / nsteps
+    store_ms = b.elapsed_time(c) / reps
+    read = (kq.codes.numel() + vq.codes.numel()) * 4 + (kq.scales.numel() + vq.scales.numel()) * 2
+    written = (ko.numel() + vo.numel()) * 2
+    gbs = (read + written) / (ms / 1e3) / 1e9
+    src = (Kx.numel() + Vx.numel()) * 2
+    store_gbs = (src + read) / (store_ms / 1e3) / 1e9
+    return {
+        "metric": "KV-cache fetch HBM GB/s (8-bit keys + 3-bit values dequantized and rotated back to bf16)",
+        "value": round(gbs, 3), "unit": "GB/s", "n_gpus": 1, "steps": nsteps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32 decode -> bf16", "data": "synthetic",
+        "config": {"workload": "KV cache 32768 tokens x 8 heads x 128, keys 8-bit g64 (4 outlier "
+                               "channels x20), values 3-bit g64; step = fetch of the whole cache",
+                   "bytes_per_step": read + written},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 3), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "store": {"ms": round(store_ms, 6), "gb_per_s": round(store_gbs, 3),
+                  "tokens_per_s": round(T / (store_ms / 1e3), 1)},
+        "wall_s": round(wall, 4),
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -705,6 +786,8 @@ def main():
         out = bench_encode_stream(args)
     elif args.config == 8:
         out = bench_expert_stream(args)
+    elif args.config == 9:
+        out = bench_kv(args)
     else:
         out = bench_moe(args)
     print(json.dumps(out), flush=True)

@@ -32,7 +32,8 @@
  *             with tq_last_error(). A launch failure returns TQ_ERR_HIP. Nothing aborts
  *             and nothing throws across this interface. TQ_OK is 0.
  *   Shapes    K = m * 2^k with m in {1, 12, 20, 28}, K a multiple of 32 in [64, 8192];
- *             group in {16, 32, 64, 128} dividing K; n_levels in {3, 4, 8, 16};
+ *             group in {16, 32, 64, 128} dividing K; n_levels in {3, 4, 8, 16} (and 256
+ *             for KV-cache rows, see tq_kv_fetch);
  *             E in [1, 8192]. Other shapes return TQ_ERR_UNSUPPORTED.
  *   Layout    codes  uint32 [E][N][words_per_row], rows packed independently;
  *                    words_per_row = ceil(K * b / 32) for b = log2(n_levels) bits, element
@@ -105,6 +106,7 @@ int64_t tq_words_per_row(int64_t K, int32_t n_levels);
 
 /* Centroids (ascending, n_levels floats) and, if `thresholds` is not NULL, the n_levels-1
  * decision thresholds (midpoints of neighbouring centroids), both binary32, host memory.
+ * n_levels 3, 4, 8, 16 or 256.
  * The codebook is the Lloyd-Max quantizer of N(0,1) ("Quantizing a weight, with no data",
  * third bullet; "The ternary tier"), computed by Lloyd iteration in double precision when
  * the library loads and rounded once. Returns TQ_OK or TQ_ERR_UNSUPPORTED. */
@@ -218,6 +220,25 @@ int tq_gather_qmm(const tq_qweight *w, const void *x, tq_dtype x_dtype, int64_t 
  * NaN. n must be at most 65535. Workspace: none. */
 int tq_dequant(const tq_qweight *w, const int32_t *ids, int64_t n, void *out,
                tq_dtype out_dtype, void *stream);
+
+/* KV-cache compression (turboquant-mlx "How it works", "The KV cache": the weights' rotation
+ * and codebook compress the cache at run time, 8-bit keys and 3-bit values; "your SSD is a
+ * GPU", KV-cache section: rotate, quantize, store; dequantize, de-rotate on the way out).
+ * A cache of T tokens x H heads is rows = T * H rows of head_dim = K:
+ *   store  tq_encode(x, dtype, rows, K, n_levels, group, seed, codes, scales, stream), with
+ *          n_levels = 256 (8-bit keys: one byte per code, four per word) or 8 (3-bit values),
+ *          or any other level count; 256 levels need K a power of two in [64, 4096] and a
+ *          16-byte aligned x (TQ_ERR_UNSUPPORTED / TQ_ERR_ALIGN otherwise);
+ *   fetch  tq_kv_fetch below.
+ * The 256-level codebook is the Lloyd-Max quantizer of N(0,1) like the others (tq_codebook
+ * accepts 256); the qmv family, tq_dequant and tq_gather_qmm do not take it. */
+
+/* Fetch: out[r] = R^T w'_r for every row r < E * N of w, w'_r[j] = c[idx_rj] * scale_{r, j /
+ * group} (the dequantized row) and R^T = diag(s) H_K / sqrt(K) the inverse rotation (the
+ * signs of w). w: n_levels 4, 8, 16 or 256 (bit formats), K a power of two in [64, 2048],
+ * any group. out: device [E * N][K] of out_dtype, 16-byte aligned. Computed in fp32 and
+ * rounded once to out_dtype. Returns TQ_ERR_UNSUPPORTED for other formats or K. */
+int tq_kv_fetch(const tq_qweight *w, void *out, tq_dtype out_dtype, void *stream);
 
 /* Expert streaming (turboquant-mlx "How it works", "Expert streaming": experts are read on
  * demand through an LRU cache, with results bit-identical to a model held in memory). The

@@ -24,6 +24,9 @@ centroid of the ternary codebook is exactly 0.0.
 
 Index order is ascending: index 0 is the most negative centroid. For the ternary codebook
 index 0/1/2 is -c/0/+c.
+
+The 256-level codebook is the one 8-bit KV-cache keys use ("How it works", "The KV cache":
+the same rotation and codebook compress the cache, 8-bit keys and 3-bit values).
 """
 
 import math
@@ -98,14 +101,133 @@ def _solve(levels, tol, max_iter):
     return c, t, D, it
 
 
+def lloyd_jacobian(c):
+    """Tridiagonal Jacobian of lloyd_step at c: (sub, diag, super) of d(new c)/d(c).
+
+    With a = t_{k-1}, b = t_k and m = E[X | a < X <= b], differentiating the cell mean
+    (phi(a) - phi(b)) / P(a < X <= b) gives dm/db = phi(b) (b - m) / P and
+    dm/da = phi(a) (m - a) / P; each threshold is the mean of its two neighbours, so
+    d/dc_{k-1} = dm/da / 2, d/dc_k = (dm/da + dm/db) / 2, d/dc_{k+1} = dm/db / 2."""
+    L = len(c)
+    t = midpoints(c)
+    edges = [-math.inf] + [float(v) for v in t] + [math.inf]
+    sub, diag, sup = np.zeros(L), np.zeros(L), np.zeros(L)
+    for k in range(L):
+        a, b = edges[k], edges[k + 1]
+        P = cell_probability(a, b)
+        m = cell_mean(a, b)
+        da = 0.0 if math.isinf(a) else pdf(a) * (m - a) / P
+        db = 0.0 if math.isinf(b) else pdf(b) * (b - m) / P
+        sub[k], diag[k], sup[k] = da / 2.0, (da + db) / 2.0, db / 2.0
+    return sub, diag, sup
+
+
+def solve_tridiagonal(sub, diag, sup, rhs):
+    """Thomas algorithm: x with sub[k] x[k-1] + diag[k] x[k] + sup[k] x[k+1] = rhs[k]."""
+    n = len(diag)
+    cp, dp = np.zeros(n), np.zeros(n)
+    cp[0], dp[0] = sup[0] / diag[0], rhs[0] / diag[0]
+    for k in range(1, n):
+        den = diag[k] - sub[k] * cp[k - 1]
+        cp[k] = sup[k] / den
+        dp[k] = (rhs[k] - sub[k] * dp[k - 1]) / den
+    x = np.zeros(n)
+    x[-1] = dp[-1]
+    for k in range(n - 2, -1, -1):
+        x[k] = dp[k] - cp[k] * x[k + 1]
+    return x
+
+
+def _mp_lloyd_residual_and_jacobian(c):
+    """lloyd_step(c) - c and its tridiagonal Jacobian, in mpmath's working precision (the
+    same formulas as lloyd_step and lloyd_jacobian)."""
+    import mpmath as mp
+    L = len(c)
+    t = [(c[k] + c[k + 1]) / 2 for k in range(L - 1)]
+    edges = [None] + t + [None]
+    pdf_ = lambda x: mp.exp(-x * x / 2) / mp.sqrt(2 * mp.pi)
+    g, sub, diag, sup = [], [], [], []
+    for k in range(L):
+        a, b = edges[k], edges[k + 1]
+        pa = mp.mpf(0) if a is None else pdf_(a)
+        pb = mp.mpf(0) if b is None else pdf_(b)
+        Qa = mp.mpf(1) if a is None else mp.erfc(a / mp.sqrt(2)) / 2
+        Qb = mp.mpf(0) if b is None else mp.erfc(b / mp.sqrt(2)) / 2
+        P = Qa - Qb
+        m = (pa - pb) / P
+        da = mp.mpf(0) if a is None else pa * (m - a) / P
+        db = mp.mpf(0) if b is None else pb * (b - m) / P
+        g.append(m - c[k])
+        sub.append(da / 2)
+        diag.append((da + db) / 2 - 1)
+        sup.append(db / 2)
+    return g, sub, diag, sup
+
+
+@lru_cache(maxsize=None)
+def _solve_newton(levels, lloyd_steps):
+    """The same fixed point for a large codebook. Plain Lloyd iteration contracts too slowly
+    at 256 levels (about 0.99985 per step), and the fixed point is ill-conditioned for the
+    map's rounding errors (they are amplified about 10^4 times), so: Lloyd steps from the
+    same start, Newton's method on lloyd_step(c) - c = 0 in fp64 (Jacobian lloyd_jacobian -
+    I), then Newton in 40-digit arithmetic (mpmath) to finish; the result is exact to far
+    below the binary32 resolution the kernels use."""
+    import mpmath as mp
+    L = levels
+    c = np.array([-2.0 + 4.0 * (k + 0.5) / L for k in range(L)])
+    for _ in range(lloyd_steps):
+        c = lloyd_step(c)
+    for _ in range(40):
+        g = lloyd_step(c) - c
+        sub, diag, sup = lloyd_jacobian(c)
+        delta = solve_tridiagonal(sub, diag - 1.0, sup, -g)
+        c = c + delta
+        c = (c - c[::-1]) / 2.0
+        if float(np.max(np.abs(delta))) < 1e-9:
+            break
+    with mp.workdps(40):
+        cm = [mp.mpf(float(v)) for v in c]
+        for it in range(1, 21):
+            g, sub, diag, sup = _mp_lloyd_residual_and_jacobian(cm)
+            # Thomas algorithm in mpmath
+            n = L
+            cp, dp = [mp.mpf(0)] * n, [mp.mpf(0)] * n
+            cp[0], dp[0] = sup[0] / diag[0], -g[0] / diag[0]
+            for k in range(1, n):
+                den = diag[k] - sub[k] * cp[k - 1]
+                cp[k] = sup[k] / den
+                dp[k] = (-g[k] - sub[k] * dp[k - 1]) / den
+            d = [mp.mpf(0)] * n
+            d[-1] = dp[-1]
+            for k in range(n - 2, -1, -1):
+                d[k] = dp[k] - cp[k] * d[k + 1]
+            cm = [cm[k] + d[k] for k in range(n)]
+            cm = [(cm[k] - cm[n - 1 - k]) / 2 for k in range(n)]
+            if max(abs(x) for x in d) < mp.mpf(10) ** -30:
+                break
+        else:
+            raise RuntimeError(f"Newton polish for L={L} did not converge")
+        c = np.array([float(x) for x in cm])
+    t = midpoints(c)  # as for every codebook: midpoints of the (fp64) centroids
+    edges = [-math.inf] + [float(v) for v in t] + [math.inf]
+    p = np.array([cell_probability(edges[k], edges[k + 1]) for k in range(L)])
+    D = 1.0 - float(np.sum(p * c * c))
+    return c, t, D, lloyd_steps + it
+
+
 def lloyd_max(levels, tol=1e-15, max_iter=200000):
     """Return (centroids, thresholds, distortion, iterations) of the L-level N(0,1) quantizer.
 
-    ``centroids`` is ascending, length L; ``thresholds`` has length L-1.
+    ``centroids`` is ascending, length L; ``thresholds`` has length L-1. Codebooks of up to
+    16 levels come from plain Lloyd iteration; larger ones (the 256-level table of 8-bit KV
+    keys) from Lloyd steps finished by Newton's method on the same fixed-point equations.
     """
     if levels < 2:
         raise ValueError("a codebook needs at least two levels")
-    c, t, D, it = _solve(int(levels), float(tol), int(max_iter))
+    if levels > 16:
+        c, t, D, it = _solve_newton(int(levels), 2000)
+    else:
+        c, t, D, it = _solve(int(levels), float(tol), int(max_iter))
     return c.copy(), t.copy(), D, it
 
 
@@ -135,8 +257,12 @@ def snap(u, levels):
     """
     u32 = np.asarray(u, dtype=np.float64).astype(np.float32)
     t32 = thresholds_f32(levels)
+    if levels > 16:
+        # the same count for the 255 thresholds of the 8-bit codebook, without a
+        # [.., 255] comparison array: #{k : t_k < u} by binary search (side='left')
+        return np.searchsorted(t32, u32, side="left").astype(np.int64)
     return np.sum(u32[..., None] > t32, axis=-1).astype(np.int64)
 
 
-SUPPORTED_LEVELS = (3, 4, 8, 16)
-BITS_OF_LEVELS = {4: 2, 8: 3, 16: 4}
+SUPPORTED_LEVELS = (3, 4, 8, 16, 256)
+BITS_OF_LEVELS = {4: 2, 8: 3, 16: 4, 256: 8}

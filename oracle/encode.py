@@ -164,3 +164,11 @@ def dequant(codes, scales, levels, group, K):
 def dequant_unrotated(codes, scales, levels, group, K, seed):
     """w_hat = R^T w'_hat: the quantized weight in the original basis."""
     return hd.unrotate(dequant(codes, scales, levels, group, K), seed)
+
+
+def kv_fetch(codes, scales, levels, group, K, seed):
+    """The fetch half of a compressed KV cache: each stored row dequantized and rotated back
+    ("your SSD is a GPU", KV-cache section: rotate, quantize, store, then dequantize and
+    de-rotate; turboquant-mlx "How it works", "The KV cache": the weights' rotation and
+    codebook, 8-bit keys and 3-bit values). Rows are (token, head) vectors of head_dim K."""
+    return dequant_unrotated(codes, scales, levels, group, K, seed)

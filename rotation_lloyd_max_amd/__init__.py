@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "TqError", "QWeight", "lib", "codebook", "words_per_row", "signs", "encode", "fwht",
     "qmv", "gather_qmv", "multi_gather_qmv", "gather_qmm", "workspace_bytes", "dequant",
-    "encode_stream", "multi_gather_qmv_static", "ExpertCache",
+    "encode_stream", "multi_gather_qmv_static", "ExpertCache", "kv_fetch",
     "F32", "BF16", "F16", "X_ROTATED",
 ]
 
@@ -72,6 +72,7 @@ SIGNATURES = [
     ("tq_dequant", ctypes.c_int, [_QW, _P, _I64, _P, ctypes.c_int, _P]),
     ("tq_encode_stream", ctypes.c_int,
      [_P, ctypes.c_int, _I64, _I64, _I32, _I32, _U64, _P, _P, _P, _SZ, _P, _P]),
+    ("tq_kv_fetch", ctypes.c_int, [_QW, _P, ctypes.c_int, _P]),
     ("tq_expert_cache_bytes", _SZ, [_I32, _I64]),
     ("tq_expert_cache_init", ctypes.c_int, [_P, _SZ, _I32, _I64]),
     ("tq_expert_cache_fetch", ctypes.c_int, [_P, _QW, _QW, _P, _I32, _P, _P, _P, _P, _P]),
@@ -122,8 +123,8 @@ def words_per_row(K, levels):
 
 def codebook(levels):
     """(centroids, thresholds) as float32 numpy arrays, from the library."""
-    c = np.zeros(16, dtype=np.float32)
-    t = np.zeros(15, dtype=np.float32)
+    c = np.zeros(256, dtype=np.float32)
+    t = np.zeros(255, dtype=np.float32)
     _check(lib().tq_codebook(levels, c.ctypes.data, t.ctypes.data))
     return c[:levels].copy(), t[:levels - 1].copy()
 
@@ -279,6 +280,17 @@ def qmv(qw, x, out_dtype=torch.float32, rotated=False, out=None):
     _check(lib().tq_qmv(ctypes.byref(d), _ptr(x), _dt(x), _ptr(y), _dt(y),
                         X_ROTATED if rotated else 0, None, 0, _stream()))
     return y
+
+
+def kv_fetch(qw, out_dtype=torch.bfloat16, out=None):
+    """Every row of a compressed KV cache (a QWeight of E x N rows of head_dim K, typically
+    from encode(x, 256 or 8, group, seed)) dequantized and rotated back: [E, N, K]."""
+    o = out if out is not None else torch.empty((qw.E, qw.N, qw.K), dtype=out_dtype,
+                                                device=qw.codes.device)
+    d = qw.desc()
+    with torch.cuda.device(qw.codes.device):
+        _check(lib().tq_kv_fetch(ctypes.byref(d), _ptr(o), _dt(o), _stream(qw.codes.device)))
+    return o
 
 
 def dequant(qw, ids=None, out_dtype=torch.bfloat16, out=None):

@@ -40,7 +40,8 @@ struct EncP2Params {
   uint32_t* codes;
   uint16_t* scales;
   double inv_sqrt_k;
-  uint32_t tbits[8];  // the positive decision thresholds (binary32 bit patterns), ascending
+  uint32_t tbits[8];    // the positive decision thresholds (binary32 bit patterns), ascending
+  uint32_t tbig[128];   // the same for the 256-level codebook (127 used)
   int lg_k, wpr;
 };
 
@@ -124,6 +125,9 @@ template <int WDT, int LEVELS, int LG_G, bool BP>
 __global__ __launch_bounds__(kP2Threads) void k_encode_p2(EncP2Params p) {
   extern __shared__ u32x4_t p2_smem[];
   __shared__ uint32_t sw[kP2Batch / 32];
+  __shared__ uint32_t tk[LEVELS == 256 ? 128 : 1];  // 8-bit codebook: searched thresholds
+  if constexpr (LEVELS == 256)
+    if (threadIdx.x < 128) tk[threadIdx.x] = p.tbig[threadIdx.x];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lg = p.lg_k, K = 1 << lg;
   const int lg_tr = lg - 6, tr = 1 << lg_tr;  // lanes per row
@@ -163,7 +167,7 @@ __global__ __launch_bounds__(kP2Threads) void k_encode_p2(EncP2Params p) {
   constexpr int G = 1 << LG_G;
   constexpr int GL = G < 64 ? G : 64;  // elements of one group inside a lane
   constexpr int NG = 64 / GL;          // groups (or half groups) per lane
-  constexpr int NPOS = LEVELS == 3 ? 1 : LEVELS / 2 - 1;
+  constexpr int NPOS = LEVELS == 3 ? 1 : LEVELS == 256 ? 8 : LEVELS / 2 - 1;
   constexpr int CPOS = LEVELS == 3 ? 1 : LEVELS / 2;      // idx of the smallest u > 0
   constexpr int CNEG = LEVELS == 3 ? 1 : LEVELS / 2 - 1;  // idx of u = 0
   const int64_t nbatch = (p.rows + rpb - 1) / rpb;
@@ -290,8 +294,14 @@ __global__ __launch_bounds__(kP2Threads) void k_encode_p2(EncP2Params p) {
       const bool pos = static_cast<int32_t>(ub) > 0;  // u > 0 (never NaN here)
       const uint32_t key = (ub & 0x7fffffffu) + (pos ? 0u : 1u);
       uint32_t cnt = 0;
+      if constexpr (LEVELS == 256) {
+        // 127 positive thresholds: a branch-free binary search for #{q : key > tk[q]}
 #pragma unroll
-      for (int q = 0; q < NPOS; ++q) cnt += key > p.tbits[q] ? 1u : 0u;
+        for (int st = 64; st >= 1; st >>= 1) cnt += key > tk[cnt + st - 1] ? st : 0u;
+      } else {
+#pragma unroll
+        for (int q = 0; q < NPOS; ++q) cnt += key > p.tbits[q] ? 1u : 0u;
+      }
       const uint32_t idx = pos ? CPOS + cnt : CNEG - cnt;
       const int bp = BITS * j;
       w[bp >> 5] |= idx << (bp & 31);
@@ -355,6 +365,7 @@ hipError_t launch_p2_w(const EncP2Params& p, int levels, int group, int grid, hi
     case 3: return launch_p2_l<WDT, 3, BP>(p, group, grid, s);
     case 4: return launch_p2_l<WDT, 4, BP>(p, group, grid, s);
     case 8: return launch_p2_l<WDT, 8, BP>(p, group, grid, s);
+    case 256: return launch_p2_l<WDT, 256, BP>(p, group, grid, s);
     default: return launch_p2_l<WDT, 16, BP>(p, group, grid, s);
   }
 }
@@ -365,23 +376,25 @@ bool encode_p2_supported(int K, int m) { return m == 1 && K >= 64 && K <= kP2Bat
 
 hipError_t launch_encode_p2(const void* W, int wdt, int64_t rows, int K, int levels, int group,
                             uint64_t seed, uint32_t* codes, uint16_t* scales, hipStream_t s) {
-  const CodebookArgs* cb = codebook_for(levels);
   EncP2Params p{};
   p.W = W; p.rows = rows; p.seed = seed; p.codes = codes; p.scales = scales;
   int lg = 0;
   while ((1 << lg) < K) ++lg;
   p.lg_k = lg;
   p.inv_sqrt_k = 1.0 / __builtin_sqrt(static_cast<double>(K));
-  p.wpr = levels == 3 ? (K + 19) / 20 : (K * (levels == 4 ? 2 : levels == 8 ? 3 : 4)) / 32;
+  p.wpr = levels == 3 ? (K + 19) / 20
+                      : (K * (levels == 4 ? 2 : levels == 8 ? 3 : levels == 16 ? 4 : 8)) / 32;
   // positive thresholds of the symmetric codebook (the negative ones are their negations)
+  const float* t = levels == 256 ? codebook256()->t : codebook_for(levels)->t;
   const int npos = levels == 3 ? 1 : levels / 2 - 1;
+  uint32_t* dst = levels == 256 ? p.tbig : p.tbits;
   for (int q = 0; q < npos; ++q) {
-    const float tq = cb->t[levels - 1 - npos + q];
-    const float tn = cb->t[npos - 1 - q];
+    const float tq = t[levels - 1 - npos + q];
+    const float tn = t[npos - 1 - q];
     if (!(tq > 0.f) || tn != -tq) return hipErrorInvalidValue;  // not symmetric: never
-    p.tbits[q] = __builtin_bit_cast(uint32_t, tq);
+    dst[q] = __builtin_bit_cast(uint32_t, tq);
   }
-  if (levels != 3 && cb->t[levels / 2 - 1] != 0.f) return hipErrorInvalidValue;
+  if (levels != 3 && t[levels / 2 - 1] != 0.f) return hipErrorInvalidValue;
   const int rpb = kP2Batch / K;
   const int64_t nbatch = (rows + rpb - 1) / rpb;
   const int64_t want = (nbatch + kP2Waves - 1) / kP2Waves;

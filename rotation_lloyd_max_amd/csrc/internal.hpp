@@ -19,6 +19,14 @@ struct CodebookArgs {
 // Lloyd-Max codebook for `levels` in {3, 4, 8, 16}; nullptr otherwise.
 const CodebookArgs* codebook_for(int levels);
 
+// The 256-level codebook (8-bit codes of KV-cache rows), binary32 and fp16.
+struct BigCodebook {
+  float c[256];
+  float t[255];
+  uint16_t h[256];
+};
+const BigCodebook* codebook256();
+
 // K = m * P with m in {1, 12, 20, 28}, P a power of two.
 bool split_dim(int64_t K, int* m, int* P);
 
@@ -73,6 +81,10 @@ size_t gather_qmm_workspace(const WeightArgs& w, int64_t M, int64_t T);
 hipError_t launch_gather_qmm(const WeightArgs& w, const void* x, int xdt, int64_t T,
                              const int32_t* row_token, const int32_t* offsets, int64_t M,
                              bool x_rotated, void* y, int ydt, void* ws, hipStream_t s);
+
+// KV-cache fetch: out[r] = R^T (c[idx] * scale) for `rows` rows of a power-of-two K <= 2048.
+bool kv_fetch_supported(int K, int levels);
+hipError_t launch_kv_fetch(const WeightArgs& w, int64_t rows, void* out, int odt, hipStream_t s);
 
 // Up to kMaxSlotIds int32 values passed by value to a kernel (tq_expert_cache_fetch).
 constexpr int kMaxSlotIds = 512;

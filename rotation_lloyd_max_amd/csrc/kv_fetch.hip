@@ -1,0 +1,168 @@
+// The fetch half of a compressed KV cache: every stored row dequantized and rotated back,
+//     out[r] = R^T w'_r,   w'_r[j] = c[idx_rj] * scale_{r, j / group},
+//     R^T = diag(s) H_d / sqrt(d)   (H_d is a symmetric Sylvester matrix for d = 2^p).
+// (turboquant-mlx "How it works", "The KV cache": the weights' rotation and codebook compress
+// the cache, 8-bit keys and 3-bit values; "your SSD is a GPU", the KV-cache section: rotate,
+// quantize, store, then dequantize and de-rotate on the way out.)
+//
+// Work layout: a lane holds 32 consecutive elements of one row, d / 32 lanes per row,
+// 2048 / d rows per wave. Its packed codes are b whole words (b bits per code) and its signs
+// one sign word. The Sylvester transform runs its five low stages in registers and the
+// rest across the row's lanes with lane exchanges (no LDS buffer, no barrier). fp32
+// throughout; the output is rounded once.
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace tq {
+namespace {
+
+constexpr int kKvThreads = 256;
+constexpr int kKvEl = 32;  // elements per lane
+
+struct KvParams {
+  const uint32_t* codes;
+  const uint16_t* scales;
+  const uint32_t* signs;
+  void* out;
+  int64_t rows;
+  int K, wpr, ngk, lg_group, lg_tr;
+  float inv_sqrt_k;
+  float lut[256];  // centroids, binary32 (the first n_levels used)
+};
+
+template <int S>
+__device__ __forceinline__ void kv_bfly(float (&v)[kKvEl]) {
+#pragma unroll
+  for (int j = 0; j < kKvEl; ++j) {
+    if (j & (1 << S)) continue;
+    const float a = v[j], b = v[j | (1 << S)];
+    v[j] = a + b;
+    v[j | (1 << S)] = a - b;
+  }
+}
+
+// One butterfly stage between lanes `lane` and `lane ^ m`: the lower lane keeps the sum, the
+// upper one the difference (partner - own).
+__device__ __forceinline__ void kv_lane_stage(float (&v)[kKvEl], int m) {
+  const bool upper = (threadIdx.x & m) != 0;
+#pragma unroll
+  for (int j = 0; j < kKvEl; ++j) {
+    const float o = __shfl_xor(v[j], m);
+    v[j] = upper ? o - v[j] : v[j] + o;
+  }
+}
+
+// G16: groups of 16 (two scales per lane); otherwise one scale per lane.
+template <int LEVELS, bool G16, int ODT>
+__global__ __launch_bounds__(kKvThreads) void k_kv_fetch(KvParams p) {
+  constexpr int B = LEVELS == 4 ? 2 : LEVELS == 8 ? 3 : LEVELS == 16 ? 4 : 8;
+  constexpr int NW = kKvEl * B / 32;  // code words per lane
+  __shared__ float lut[LEVELS];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tr = 1 << p.lg_tr;    // lanes per row
+  const int rpw = 64 >> p.lg_tr;  // rows per wave batch
+  const int rl = lane >> p.lg_tr, t = lane & (tr - 1);
+  const int col0 = t * kKvEl;     // first element of this lane's chunk
+  for (int k = threadIdx.x; k < LEVELS; k += kKvThreads) lut[k] = p.lut[k];
+  __syncthreads();
+  const uint32_t sgn = p.signs[t];  // sign bits of elements col0 .. col0 + 31
+  const int gi0 = col0 >> p.lg_group;
+
+  const int64_t nb = (p.rows + rpw - 1) / rpw;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * (kKvThreads / 64);
+  for (int64_t b = static_cast<int64_t>(blockIdx.x) * (kKvThreads / 64) + wave; b < nb; b += stride) {
+    const int64_t row = b * rpw + rl;
+    if (row >= p.rows) continue;  // a row's lanes pass or fail this test together
+    uint32_t w[NW];
+    const uint32_t* src = p.codes + row * p.wpr + t * NW;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) w[k] = src[k];
+    const uint16_t* srow = p.scales + row * p.ngk + gi0;
+    const float s0 = half_bits_to_float(srow[0]);
+    const float s1 = G16 ? half_bits_to_float(srow[1]) : s0;
+    float v[kKvEl];
+#pragma unroll
+    for (int j = 0; j < kKvEl; ++j) {
+      const int bp = B * j;
+      uint32_t idx = w[bp >> 5] >> (bp & 31);
+      if ((bp & 31) + B > 32) idx |= w[(bp >> 5) + 1] << (32 - (bp & 31));
+      idx &= (1u << B) - 1u;
+      v[j] = lut[idx] * (G16 && j >= 16 ? s1 : s0);
+    }
+    // H_d: the five low index bits in registers, the rest across the row's lanes
+    kv_bfly<0>(v); kv_bfly<1>(v); kv_bfly<2>(v); kv_bfly<3>(v); kv_bfly<4>(v);
+    for (int m = 1; m < tr; m <<= 1) kv_lane_stage(v, m);
+    // R^T = diag(s) H / sqrt(d)
+#pragma unroll
+    for (int j = 0; j < kKvEl; ++j) {
+      const float x = v[j] * p.inv_sqrt_k;
+      v[j] = ((sgn >> j) & 1u) ? -x : x;
+    }
+    if constexpr (ODT == 0) {
+      float4* dst = reinterpret_cast<float4*>(static_cast<float*>(p.out) + row * p.K + col0);
+#pragma unroll
+      for (int k = 0; k < kKvEl / 4; ++k)
+        dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+    } else {
+      uint32_t hw[kKvEl / 2];
+#pragma unroll
+      for (int k = 0; k < kKvEl / 2; ++k) {
+        const uint16_t a = ODT == 1 ? float_to_bf16_rne(v[2 * k]) : float_to_half_rne(v[2 * k]);
+        const uint16_t c = ODT == 1 ? float_to_bf16_rne(v[2 * k + 1]) : float_to_half_rne(v[2 * k + 1]);
+        hw[k] = static_cast<uint32_t>(a) | (static_cast<uint32_t>(c) << 16);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + row * p.K + col0);
+#pragma unroll
+      for (int k = 0; k < kKvEl / 8; ++k)
+        dst[k] = make_uint4(hw[4 * k], hw[4 * k + 1], hw[4 * k + 2], hw[4 * k + 3]);
+    }
+  }
+}
+
+template <int LEVELS, bool G16>
+hipError_t launch_kv_l(const KvParams& p, int odt, int grid, hipStream_t s) {
+  switch (odt) {
+    case 0: hipLaunchKernelGGL((k_kv_fetch<LEVELS, G16, 0>), dim3(grid), dim3(kKvThreads), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((k_kv_fetch<LEVELS, G16, 1>), dim3(grid), dim3(kKvThreads), 0, s, p); break;
+    default: hipLaunchKernelGGL((k_kv_fetch<LEVELS, G16, 2>), dim3(grid), dim3(kKvThreads), 0, s, p); break;
+  }
+  return hipGetLastError();
+}
+
+template <int LEVELS>
+hipError_t launch_kv_g(const KvParams& p, bool g16, int odt, int grid, hipStream_t s) {
+  return g16 ? launch_kv_l<LEVELS, true>(p, odt, grid, s) : launch_kv_l<LEVELS, false>(p, odt, grid, s);
+}
+
+}  // namespace
+
+bool kv_fetch_supported(int K, int levels) {
+  return levels != 3 && K >= 64 && K <= 2048 && (K & (K - 1)) == 0;
+}
+
+hipError_t launch_kv_fetch(const WeightArgs& w, int64_t rows, void* out, int odt, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  KvParams p{};
+  p.codes = w.codes; p.scales = w.scales; p.signs = w.signs; p.out = out; p.rows = rows;
+  p.K = w.K; p.wpr = w.wpr; p.ngk = w.K / w.group;
+  p.lg_group = __builtin_ctz(w.group);
+  int lg = 0;
+  while ((1 << lg) < w.K) ++lg;
+  p.lg_tr = lg - 5;
+  p.inv_sqrt_k = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(w.K)));
+  const float* c = w.levels == 256 ? codebook256()->c : codebook_for(w.levels)->c;
+  for (int k = 0; k < w.levels; ++k) p.lut[k] = c[k];
+  const int64_t rpw = 64 >> p.lg_tr;
+  const int64_t nb = (rows + rpw - 1) / rpw;
+  const int64_t want = (nb + 3) / 4;
+  const int grid = static_cast<int>(want < 2048 ? want : 2048);
+  const bool g16 = w.group == 16;
+  switch (w.levels) {
+    case 4: return launch_kv_g<4>(p, g16, odt, grid, s);
+    case 8: return launch_kv_g<8>(p, g16, odt, grid, s);
+    case 16: return launch_kv_g<16>(p, g16, odt, grid, s);
+    default: return launch_kv_g<256>(p, g16, odt, grid, s);
+  }
+}
+
+}  // namespace tq

@@ -14,6 +14,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/tq.h"
 #include "internal.hpp"
@@ -77,7 +78,74 @@ void lloyd(int L, double* c, double* t) {
   for (int k = 0; k + 1 < L; ++k) t[k] = 0.5 * (c[k] + c[k + 1]);
 }
 
+// The 256-level codebook (8-bit KV-cache keys): the same fixed point, but plain Lloyd
+// iteration contracts at about 0.99985 per step there and the fixed point amplifies the
+// map's rounding errors about 10^4 times, so it is computed in 80-bit long double: Lloyd
+// steps from the same start, then Newton's method on lloyd(c) - c = 0 with the tridiagonal
+// Jacobian of the map (d mean / d b = pdf(b) (b - mean) / P, d mean / d a = pdf(a)
+// (mean - a) / P, each threshold the midpoint of its neighbours).
+typedef long double ldbl;
+ldbl pdf_l(ldbl x) { return std::exp(-0.5L * x * x) / std::sqrt(2.0L * 3.14159265358979323846264338327950288L); }
+ldbl sf_l(ldbl x) { return 0.5L * std::erfc(x / std::sqrt(2.0L)); }
+ldbl mass_l(ldbl a, ldbl b, bool a_inf, bool b_inf) {
+  const ldbl Qa = a_inf ? 1.0L : sf_l(a), Qb = b_inf ? 0.0L : sf_l(b);
+  if (!a_inf && a >= 0) return Qa - Qb;
+  if (!b_inf && b <= 0) return (b_inf ? 1.0L : sf_l(-b)) - (a_inf ? 0.0L : sf_l(-a));
+  return 1.0L - (a_inf ? 0.0L : sf_l(-a)) - Qb;
+}
+
+void lloyd_big(int L, double* c_out, double* t_out) {
+  std::vector<ldbl> c(L), nc(L), t(L - 1), g(L), sub(L), dia(L), sup(L), cp(L), dp(L), d(L);
+  for (int k = 0; k < L; ++k) c[k] = -2.0L + 4.0L * (k + 0.5L) / L;
+  auto step = [&](bool jac) {
+    for (int k = 0; k + 1 < L; ++k) t[k] = 0.5L * (c[k] + c[k + 1]);
+    for (int k = 0; k < L; ++k) {
+      const bool ai = k == 0, bi = k == L - 1;
+      const ldbl a = ai ? 0.0L : t[k - 1], b = bi ? 0.0L : t[k];
+      const ldbl pa = ai ? 0.0L : pdf_l(a), pb = bi ? 0.0L : pdf_l(b);
+      const ldbl P = mass_l(a, b, ai, bi);
+      const ldbl m = (pa - pb) / P;
+      nc[k] = m;
+      if (jac) {
+        const ldbl da = ai ? 0.0L : pa * (m - a) / P;
+        const ldbl db = bi ? 0.0L : pb * (b - m) / P;
+        sub[k] = da / 2;
+        dia[k] = (da + db) / 2 - 1;
+        sup[k] = db / 2;
+      }
+    }
+  };
+  for (int it = 0; it < 2000; ++it) {
+    step(false);
+    for (int k = 0; k < L; ++k) c[k] = 0.5L * (nc[k] - nc[L - 1 - k]);
+  }
+  for (int it = 0; it < 40; ++it) {
+    step(true);
+    for (int k = 0; k < L; ++k) g[k] = nc[k] - c[k];
+    cp[0] = sup[0] / dia[0];
+    dp[0] = -g[0] / dia[0];
+    for (int k = 1; k < L; ++k) {
+      const ldbl den = dia[k] - sub[k] * cp[k - 1];
+      cp[k] = sup[k] / den;
+      dp[k] = (-g[k] - sub[k] * dp[k - 1]) / den;
+    }
+    d[L - 1] = dp[L - 1];
+    for (int k = L - 2; k >= 0; --k) d[k] = dp[k] - cp[k] * d[k + 1];
+    ldbl dmax = 0;
+    for (int k = 0; k < L; ++k) {
+      c[k] += d[k];
+      dmax = std::fmax(dmax, std::fabs(d[k]));
+    }
+    for (int k = 0; k < L; ++k) nc[k] = 0.5L * (c[k] - c[L - 1 - k]);
+    for (int k = 0; k < L; ++k) c[k] = nc[k];
+    if (dmax < 1e-17L) break;
+  }
+  for (int k = 0; k < L; ++k) c_out[k] = static_cast<double>(c[k]);
+  for (int k = 0; k + 1 < L; ++k) t_out[k] = static_cast<double>(0.5L * (c[k] + c[k + 1]));
+}
+
 CodebookArgs g_books[4];
+BigCodebook g_big;
 std::once_flag g_books_once;
 
 void init_books() {
@@ -96,6 +164,16 @@ void init_books() {
     }
     for (int k = 0; k + 1 < L; ++k) b.t[k] = static_cast<float>(t[k]);
   }
+  {
+    std::vector<double> c(256), t(255);
+    lloyd_big(256, c.data(), t.data());
+    for (int k = 0; k < 256; ++k) {
+      g_big.c[k] = static_cast<float>(c[k]);
+      const _Float16 h = static_cast<_Float16>(c[k]);
+      std::memcpy(&g_big.h[k], &h, 2);
+    }
+    for (int k = 0; k < 255; ++k) g_big.t[k] = static_cast<float>(t[k]);
+  }
 }
 
 int64_t words_per_row(int64_t K, int levels) {
@@ -104,6 +182,7 @@ int64_t words_per_row(int64_t K, int levels) {
     case 4: return (2 * K + 31) / 32;
     case 8: return (3 * K + 31) / 32;
     case 16: return (4 * K + 31) / 32;
+    case 256: return (8 * K + 31) / 32;
     default: return 0;
   }
 }
@@ -112,9 +191,16 @@ bool valid_dtype(int d) { return d == TQ_F32 || d == TQ_BF16 || d == TQ_F16; }
 size_t dtype_size(int d) { return d == TQ_F32 ? 4 : 2; }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-int check_shape(int64_t K, int levels, int group, int* m, int* P) {
-  if (levels != 3 && levels != 4 && levels != 8 && levels != 16)
-    return fail(TQ_ERR_UNSUPPORTED, "n_levels must be 3, 4, 8 or 16 (got %d)", levels);
+// allow256: the 8-bit codebook (KV-cache rows), for power-of-two K up to 4096 only
+int check_shape(int64_t K, int levels, int group, int* m, int* P, bool allow256 = false) {
+  if (levels == 256 && allow256) {
+    if (K < 64 || K > 4096 || (K & (K - 1)) != 0)
+      return fail(TQ_ERR_UNSUPPORTED, "256 levels need K a power of two in [64, 4096] (got %lld)",
+                  static_cast<long long>(K));
+  } else if (levels != 3 && levels != 4 && levels != 8 && levels != 16) {
+    return fail(TQ_ERR_UNSUPPORTED, "n_levels must be 3, 4, 8 or 16%s (got %d)",
+                allow256 ? " (or 256)" : "", levels);
+  }
   if (group != 16 && group != 32 && group != 64 && group != 128)
     return fail(TQ_ERR_UNSUPPORTED, "group must be 16, 32, 64 or 128 (got %d)", group);
   if (K < 64 || K > 8192 || K % 32 != 0)
@@ -129,10 +215,10 @@ int check_shape(int64_t K, int levels, int group, int* m, int* P) {
   return TQ_OK;
 }
 
-int check_weight(const tq_qweight* w, WeightArgs* out) {
+int check_weight(const tq_qweight* w, WeightArgs* out, bool allow256 = false) {
   if (!w) return fail(TQ_ERR_ARG, "weight descriptor is NULL");
   int m = 1, P = 1;
-  const int rc = check_shape(w->K, w->n_levels, w->group, &m, &P);
+  const int rc = check_shape(w->K, w->n_levels, w->group, &m, &P, allow256);
   if (rc != TQ_OK) return rc;
   if (w->N < 0 || w->N > (1 << 24)) return fail(TQ_ERR_ARG, "N out of range");
   if (w->E < 1 || w->E > 8192) return fail(TQ_ERR_ARG, "E must be in [1, 8192]");
@@ -168,6 +254,11 @@ int check_io(const void* x, int xdt, const void* y, int ydt, bool need) {
 }
 
 }  // namespace
+
+const BigCodebook* codebook256() {
+  std::call_once(g_books_once, init_books);
+  return &g_big;
+}
 
 const CodebookArgs* codebook_for(int levels) {
   std::call_once(g_books_once, init_books);
@@ -206,6 +297,13 @@ int64_t tq_words_per_row(int64_t K, int32_t n_levels) {
 }
 
 int tq_codebook(int32_t n_levels, float* centroids, float* thresholds) {
+  if (n_levels == 256) {
+    if (!centroids) return fail(TQ_ERR_ARG, "centroids is NULL");
+    const BigCodebook* g = codebook256();
+    std::memcpy(centroids, g->c, sizeof(float) * 256);
+    if (thresholds) std::memcpy(thresholds, g->t, sizeof(float) * 255);
+    return TQ_OK;
+  }
   const CodebookArgs* b = codebook_for(n_levels);
   if (!b) return fail(TQ_ERR_UNSUPPORTED, "n_levels must be 3, 4, 8 or 16 (got %d)", n_levels);
   if (!centroids) return fail(TQ_ERR_ARG, "centroids is NULL");
@@ -225,7 +323,7 @@ int tq_signs(uint64_t seed, int64_t K, uint32_t* bits, void* stream) {
 int tq_encode(const void* W, tq_dtype w_dtype, int64_t rows, int64_t K, int32_t n_levels,
               int32_t group, uint64_t seed, uint32_t* codes, uint16_t* scales, void* stream) {
   int m = 1, P = 1;
-  const int rc = check_shape(K, n_levels, group, &m, &P);
+  const int rc = check_shape(K, n_levels, group, &m, &P, /*allow256=*/true);
   if (rc != TQ_OK) return rc;
   if (!valid_dtype(w_dtype)) return fail(TQ_ERR_ARG, "bad weight dtype");
   if (rows < 0) return fail(TQ_ERR_ARG, "rows must be >= 0");
@@ -233,6 +331,8 @@ int tq_encode(const void* W, tq_dtype w_dtype, int64_t rows, int64_t K, int32_t 
   if (!W || !codes || !scales) return fail(TQ_ERR_ARG, "W, codes and scales must be non-NULL");
   if (!aligned(W, dtype_size(w_dtype)) || !aligned(codes, 4) || !aligned(scales, 2))
     return fail(TQ_ERR_ALIGN, "W, codes or scales misaligned");
+  if (n_levels == 256 && !aligned(W, 16))
+    return fail(TQ_ERR_ALIGN, "256-level encode reads W with 16-byte loads: W must be 16-byte aligned");
   return hip_status(launch_encode(W, w_dtype, rows, static_cast<int>(K), m, P, n_levels, group,
                                   seed, codes, scales, static_cast<hipStream_t>(stream)),
                     "tq_encode");
@@ -243,7 +343,7 @@ int tq_encode_stream(const void* W_host, tq_dtype w_dtype, int64_t rows, int64_t
                      uint16_t* scales, void* staging, size_t staging_bytes, void* stream,
                      void* copy_stream) {
   int m = 1, P = 1;
-  const int rc = check_shape(K, n_levels, group, &m, &P);
+  const int rc = check_shape(K, n_levels, group, &m, &P, /*allow256=*/true);
   if (rc != TQ_OK) return rc;
   if (!valid_dtype(w_dtype)) return fail(TQ_ERR_ARG, "bad weight dtype");
   if (rows < 0) return fail(TQ_ERR_ARG, "rows must be >= 0");
@@ -407,6 +507,23 @@ int tq_multi_gather_qmv_static(const tq_qweight* w, const int32_t* ids, int64_t 
   return hip_status(launch_multi_gather(a, ids, P, x, x_dtype, (flags & TQ_X_ROTATED) != 0, y,
                                         y_dtype, ws, static_cast<hipStream_t>(stream)),
                     "tq_multi_gather_qmv_static");
+}
+
+int tq_kv_fetch(const tq_qweight* w, void* out, tq_dtype out_dtype, void* stream) {
+  WeightArgs a{};
+  int rc = check_weight(w, &a, /*allow256=*/true);
+  if (rc != TQ_OK) return rc;
+  if (!kv_fetch_supported(a.K, a.levels))
+    return fail(TQ_ERR_UNSUPPORTED,
+                "tq_kv_fetch needs a bit format (4, 8, 16 or 256 levels) and K a power of two "
+                "in [64, 2048] (got %d levels, K=%d)", a.levels, a.K);
+  if (!valid_dtype(out_dtype)) return fail(TQ_ERR_ARG, "bad dtype");
+  const int64_t rows = static_cast<int64_t>(a.E) * a.N;
+  if (rows == 0) return TQ_OK;
+  if (!out) return fail(TQ_ERR_ARG, "out is NULL");
+  if (!aligned(out, 16)) return fail(TQ_ERR_ALIGN, "out must be 16-byte aligned");
+  return hip_status(launch_kv_fetch(a, rows, out, out_dtype, static_cast<hipStream_t>(stream)),
+                    "tq_kv_fetch");
 }
 
 int tq_dequant(const tq_qweight* w, const int32_t* ids, int64_t n, void* out,

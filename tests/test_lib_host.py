@@ -35,14 +35,14 @@ def header_functions():
 
 def test_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     handle = ctypes.CDLL(tq.LIB_PATH)
     for n in names:
         assert hasattr(handle, n), n
     assert sorted(s[0] for s in tq.SIGNATURES) == names
 
 
-@pytest.mark.parametrize("L", [3, 4, 8, 16])
+@pytest.mark.parametrize("L", [3, 4, 8, 16, 256])
 def test_codebook_matches_oracle_bitwise(L):
     c, t = tq.codebook(L)
     oc, ot, _, _ = ocb.lloyd_max(L)
@@ -51,7 +51,7 @@ def test_codebook_matches_oracle_bitwise(L):
 
 
 def test_codebook_rejects_other_levels():
-    for L in (0, 1, 2, 5, 32):
+    for L in (0, 1, 2, 5, 32, 255):
         with pytest.raises(tq.TqError) as e:
             tq.codebook(L)
         assert e.value.status == ERR_UNSUPPORTED
@@ -152,6 +152,16 @@ def test_validation_statuses():
     assert b"8388608" in L.tq_last_error()
     assert L.tq_multi_gather_qmv_static(ctypes.byref(d2), None, 4, 16, 1, 16, 0, 0,
                                         None) == ERR_ARG
+    # KV fetch: formats and lengths outside its set are refused; 256 levels only there
+    assert L.tq_kv_fetch(ctypes.byref(desc(n_levels=3, group=16)), 256, 1, None) == ERR_UNSUPPORTED
+    assert L.tq_kv_fetch(ctypes.byref(desc(K=4096)), 256, 1, None) == ERR_UNSUPPORTED
+    assert L.tq_kv_fetch(ctypes.byref(desc(K=768, group=64)), 256, 1, None) == ERR_UNSUPPORTED
+    assert L.tq_kv_fetch(ctypes.byref(desc(n_levels=256)), 258, 1, None) == ERR_ALIGN
+    assert L.tq_kv_fetch(ctypes.byref(desc(n_levels=256)), 256, 9, None) == ERR_ARG
+    assert qmv_status(desc(n_levels=256)) == ERR_UNSUPPORTED
+    assert L.tq_encode(16, 1, 4, 768, 256, 64, 0, 16, 16, None) == ERR_UNSUPPORTED
+    assert L.tq_encode(18, 1, 4, 512, 256, 64, 0, 16, 16, None) == ERR_ALIGN
+    assert L.tq_words_per_row(128, 256) == 32
     # expert cache: sizes, set-up checks, and fetches refused before anything is enqueued
     assert L.tq_expert_cache_bytes(0, 10) == ctypes.c_size_t(-1).value
     nb = L.tq_expert_cache_bytes(4, 10)

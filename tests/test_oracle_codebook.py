@@ -9,6 +9,9 @@
 * 3 levels: the one-parameter fixed point c = phi(c/2) / (1 - Phi(c/2)) by root finding.
 * Monte Carlo: nearest-centroid quantization of N(0,1) samples by brute force argmin has
   the oracle's distortion and agrees with the threshold snap.
+* 256 levels (8-bit KV-cache keys): the same quadrature stationarity and MSE, the
+  Panter-Dite high-resolution distortion (sqrt(3) pi / 2) 4^-b within 1 %, a fixed point of
+  the plain Lloyd map, Monte Carlo distortion and snap.
 """
 
 import math
@@ -19,7 +22,7 @@ from scipy import integrate, optimize, stats
 
 from oracle import codebook as cb
 
-LEVELS = (2, 3, 4, 8, 16)
+LEVELS = (2, 3, 4, 8, 16, 256)
 
 
 def test_two_levels_closed_form():
@@ -89,20 +92,22 @@ def test_ternary_fixed_point():
 
 
 def test_middle_threshold_is_exact_zero():
-    for L in (2, 4, 8, 16):
+    for L in (2, 4, 8, 16, 256):
         assert cb.thresholds(L)[L // 2 - 1] == 0.0
 
 
-@pytest.mark.parametrize("L", (3, 4, 8, 16))
+@pytest.mark.parametrize("L", (3, 4, 8, 16, 256))
 def test_monte_carlo_nearest_centroid(L):
     rng = np.random.default_rng(1234 + L)
-    x = rng.standard_normal(1_000_000)
+    x = rng.standard_normal(1_000_000 if L <= 16 else 200_000)
     c = cb.centroids(L)
     nearest = np.argmin(np.abs(x[:, None] - c[None, :]), axis=1)
     mse = np.mean((x - c[nearest]) ** 2)
     D = cb.distortion(L)
-    # std of the MSE estimate is below 0.2% of D at these sizes
-    assert abs(mse - D) / D < 0.01
+    # std of the MSE estimate is below 0.2% of D at these sizes for up to 16 levels; at
+    # 256 levels one sample beyond the outermost centroid (|x| > 4.6) moves the estimate
+    # by about 1 %, so the bound is wider there (quadrature pins D itself)
+    assert abs(mse - D) / D < (0.01 if L <= 16 else 0.05)
     idx = cb.snap(x, L)
     far = ~np.any(np.abs(x[:, None] - cb.thresholds(L)[None, :]) < 1e-6, axis=1)
     np.testing.assert_array_equal(idx[far], nearest[far])
@@ -114,3 +119,28 @@ def test_snap_tie_goes_low():
         # a value exactly on a (binary32) threshold goes to the lower cell
         u = np.array([float(np.float32(v)) for v in t])
         np.testing.assert_array_equal(cb.snap(u, L), np.arange(L - 1))
+
+
+def test_256_levels_panter_dite_and_lloyd_fixed_point():
+    # high-resolution theory: D ~ (sqrt(3) pi / 2) 4^-b for a Gaussian quantized with 2^b
+    # optimal levels; at b = 8 the asymptote is within 1 % of the exact optimum
+    c, t, D, _ = cb.lloyd_max(256)
+    pd = math.sqrt(3.0) * math.pi / 2.0 * 4.0 ** -8
+    assert abs(D / pd - 1.0) < 0.01
+    assert 4.0e-5 < D < 4.2e-5
+    # the result is a fixed point of the plain Lloyd map itself (to its rounding)
+    assert np.max(np.abs(cb.lloyd_step(c) - c)) < 1e-13
+    # and it sits between the 16-level table's neighbours: 8-bit refines 4-bit
+    assert D < cb.distortion(16) / 200
+    # tails: the outermost centroid is the conditional mean beyond the last threshold
+    tail = stats.norm.pdf(t[-1]) / stats.norm.sf(t[-1])
+    assert abs(c[-1] - tail) < 1e-12
+
+
+def test_256_level_snap_counts_thresholds():
+    # the searchsorted count used for 255 thresholds equals the comparison count
+    rng = np.random.default_rng(99)
+    u = np.concatenate([rng.standard_normal(20000) * 1.5, cb.thresholds(256)[::7]])
+    t32 = cb.thresholds_f32(256)
+    want = np.sum(u.astype(np.float32)[:, None] > t32[None, :], axis=1)
+    np.testing.assert_array_equal(cb.snap(u, 256), want)

@@ -55,3 +55,12 @@ def test_padding_bits_zero():
     assert int(w[0, 1]) == 1  # only stream bit 32 is set in the second word
     t = enc.pack_trits(np.full((1, 21), 2))
     assert int(t[0, 1]) == 2  # padding digits of the last word are 0
+
+
+def test_eight_bit_words_are_bytes():
+    # 8-bit codes (the 256-level KV-cache codebook): element j is byte j % 4 of word j // 4
+    from oracle import encode as enc
+    idx = np.array([[1, 2, 3, 4, 255, 0, 128, 7]])
+    w = enc.pack(idx, 256)
+    assert w.tolist() == [[0x04030201, 0x078000FF]]
+    np.testing.assert_array_equal(enc.unpack(w, 256, 8), idx)

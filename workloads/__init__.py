@@ -53,6 +53,18 @@ def gaussian(g, rows, K, outliers=0, factor=20.0):
     return x
 
 
+def kv_rows(g, tokens, heads, d, outliers=4, factor=20.0):
+    """fp32 [tokens * heads, d]: N(0,1) head vectors (token-major, then head), with
+    `outliers` channels of every head scaled by `factor` in every token: the fixed
+    large-magnitude channels attention keys are known for, which give the raw vectors a
+    heavy-tailed distribution that the rotation then spreads."""
+    x = g.standard_normal((tokens, heads, d)).astype(np.float32)
+    for h in range(heads):
+        ch = g.choice(d, outliers, replace=False)
+        x[:, h, ch] *= factor
+    return x.reshape(tokens * heads, d)
+
+
 def torch_student_rows(gen, rows, K, device, dtype):
     """Same distribution as student_rows, drawn on the GPU with a seeded torch generator:
     t(4) = Z / sqrt(chi2_4 / 4) with chi2_4 the sum of four squared normals."""
