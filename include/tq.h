@@ -83,7 +83,8 @@ typedef enum {
 enum { TQ_X_ROTATED = 1 }; /* x is already R x: skip the input rotation */
 
 /* operation ids for tq_workspace_bytes */
-enum { TQ_OP_QMV = 1, TQ_OP_GATHER_QMV = 2, TQ_OP_MULTI_GATHER_QMV = 3, TQ_OP_GATHER_QMM = 4 };
+enum { TQ_OP_QMV = 1, TQ_OP_GATHER_QMV = 2, TQ_OP_MULTI_GATHER_QMV = 3, TQ_OP_GATHER_QMM = 4,
+       TQ_OP_ENCODE_DENSE = 5 };
 
 /* A packed quantized weight: E experts of N x K (E = 1 for a dense layer). Read only
  * during the call.
@@ -158,8 +159,9 @@ int tq_fwht(const void *x, tq_dtype x_dtype, int64_t rows, int64_t K, uint64_t s
             void *out, tq_dtype out_dtype, void *stream);
 
 /* Bytes of workspace an operation needs (0 if none). `count` is n (ids) for
- * gather_qmv, P (pairs) for multi_gather_qmv, M (rows) for gather_qmm; T is the number
- * of input rows of gather_qmm. Returns SIZE_MAX for invalid arguments. Workspaces are
+ * gather_qmv, P (pairs) for multi_gather_qmv, M (rows) for gather_qmm, the number of rows
+ * for encode_dense (w gives K; its other fields must be valid); T is the number of input
+ * rows of gather_qmm. Returns SIZE_MAX for invalid arguments. Workspaces are
  * 16-byte aligned (multi_gather_qmv) or 256-byte aligned (gather_qmm). */
 size_t tq_workspace_bytes(int32_t op, const tq_qweight *w, int64_t count, int64_t T);
 
@@ -220,6 +222,32 @@ int tq_gather_qmm(const tq_qweight *w, const void *x, tq_dtype x_dtype, int64_t 
  * NaN. n must be at most 65535. Workspace: none. */
 int tq_dequant(const tq_qweight *w, const int32_t *ids, int64_t n, void *out,
                tq_dtype out_dtype, void *stream);
+
+/* Dense rotations, for input dimensions the Hadamard transform does not cover (VeloxQuant-MLX,
+ * "What already existed" and "Where the time actually went": a rotation derived by QR from a
+ * seeded random matrix for dimensions such as 4864, which is neither a power of two nor a
+ * multiple of the transform's special sizes). The rotation is a caller-owned K x K binary32
+ * matrix R (device, row-major, R[i][k]); the library applies it and never makes it, so the
+ * page's "persist the matrix or regenerate it from the seed" choice stays with the caller.
+ * A layer with a dense rotation is encoded with tq_encode_dense, its inputs are rotated with
+ * tq_rotate_dense, and the qmv family then runs with TQ_X_ROTATED on a descriptor of that K
+ * (K any multiple of 32 in [64, 8192]; the signs pointer may be NULL). */
+
+/* out[r] = R x[r] for `rows` rows of length K (x device [rows][K] of x_dtype; out device
+ * [rows][K] of out_dtype). Computed on the fp64 matrix cores (exact products, fp64 sums) and
+ * rounded once to out_dtype. K a multiple of 32 in [64, 8192]; rows below 64 * 65536. */
+int tq_rotate_dense(const void *x, tq_dtype x_dtype, int64_t rows, int64_t K, const float *R,
+                    void *out, tq_dtype out_dtype, void *stream);
+
+/* tq_encode with the dense rotation R in place of the randomized Hadamard one: v = R w per
+ * row, computed in fp64 as tq_encode computes its rotation, then group RMS, fp16 scale, snap
+ * and pack as in tq_encode (scale = fp16(r), R being orthonormal). ws: device, 8-byte
+ * aligned, at least K * 8 bytes; rows go through it in chunks of ws_bytes / (K * 8) rows
+ * (tq_workspace_bytes(TQ_OP_ENCODE_DENSE, ...) gives the size for all rows at once).
+ * n_levels 3, 4, 8 or 16; group dividing K; K a multiple of 32 in [64, 8192]. */
+int tq_encode_dense(const void *W, tq_dtype w_dtype, int64_t rows, int64_t K, const float *R,
+                    int32_t n_levels, int32_t group, uint32_t *codes, uint16_t *scales,
+                    void *ws, size_t ws_bytes, void *stream);
 
 /* KV-cache compression (turboquant-mlx "How it works", "The KV cache": the weights' rotation
  * and codebook compress the cache at run time, 8-bit keys and 3-bit values; "your SSD is a

@@ -133,12 +133,29 @@ def encode(W, levels, group, seed):
     W = np.asarray(W, dtype=np.float64)
     if W.ndim != 2:
         raise ValueError("W must be 2-D [rows][K]")
-    rows, K = W.shape
+    return encode_rotated(hd.rotate(W, seed), levels, group)      # v = R w
+
+
+def encode_dense(W, R, levels, group):
+    """The same quantizer with a dense orthogonal rotation R (shape [K][K]) in place of the
+    randomized Hadamard one: v = R w for every row (VeloxQuant-MLX, "What already existed"
+    and "Where the time actually went": a QR-derived rotation for input dimensions the fast
+    Hadamard transform does not cover, such as 4864)."""
+    W = np.asarray(W, dtype=np.float64)
+    R = np.asarray(R, dtype=np.float64)
+    return encode_rotated(W @ R.T, levels, group)
+
+
+def encode_rotated(V, levels, group):
+    """Group RMS -> fp16 scale -> snap -> pack of rows that are already rotated."""
+    V = np.asarray(V, dtype=np.float64)
+    if V.ndim != 2:
+        raise ValueError("V must be 2-D [rows][K]")
+    rows, K = V.shape
     if levels not in cb.SUPPORTED_LEVELS:
         raise ValueError(f"unsupported number of levels {levels}")
     if group not in (16, 32, 64, 128) or K % group:
         raise ValueError(f"group {group} must be 16/32/64/128 and divide K={K}")
-    V = hd.rotate(W, seed)                                  # v = R w
     G = V.reshape(rows, K // group, group)
     r = np.sqrt(np.mean(G * G, axis=-1))                    # group RMS
     safe = np.where(r > 0.0, r, 1.0)

@@ -66,3 +66,17 @@ def row_bound(codes, scales, levels, group, K, x, rel=2e-3):
     Wq = enc.dequant(codes, scales, levels, group, K)
     xn = np.linalg.norm(np.asarray(x, dtype=np.float64), axis=-1)
     return rel * np.multiply.outer(xn, np.linalg.norm(Wq, axis=-1))
+
+
+def qmv_dense(codes, scales, levels, group, K, R, x):
+    """y = w'_hat . (R x) with a dense orthogonal rotation R [K][K] (VeloxQuant-MLX's
+    QR-derived rotation; "Running a quantized layer" of turboquant-mlx: rotate the input,
+    multiply by the decoded rotated weights)."""
+    Wq = enc.dequant(codes, scales, levels, group, K)
+    xr = np.asarray(x, dtype=np.float64) @ np.asarray(R, dtype=np.float64).T
+    return xr @ Wq.T
+
+
+def rotate_dense(X, R):
+    """Rows of X mapped to R x."""
+    return np.asarray(X, dtype=np.float64) @ np.asarray(R, dtype=np.float64).T

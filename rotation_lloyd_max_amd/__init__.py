@@ -20,13 +20,14 @@ import torch
 __all__ = [
     "TqError", "QWeight", "lib", "codebook", "words_per_row", "signs", "encode", "fwht",
     "qmv", "gather_qmv", "multi_gather_qmv", "gather_qmm", "workspace_bytes", "dequant",
-    "encode_stream", "multi_gather_qmv_static", "ExpertCache", "kv_fetch",
+    "encode_stream", "multi_gather_qmv_static", "ExpertCache", "kv_fetch", "rotate_dense",
+    "encode_dense",
     "F32", "BF16", "F16", "X_ROTATED",
 ]
 
 F32, BF16, F16 = 0, 1, 2
 X_ROTATED = 1
-OP_QMV, OP_GATHER_QMV, OP_MULTI_GATHER_QMV, OP_GATHER_QMM = 1, 2, 3, 4
+OP_QMV, OP_GATHER_QMV, OP_MULTI_GATHER_QMV, OP_GATHER_QMM, OP_ENCODE_DENSE = 1, 2, 3, 4, 5
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
 
@@ -73,6 +74,9 @@ SIGNATURES = [
     ("tq_encode_stream", ctypes.c_int,
      [_P, ctypes.c_int, _I64, _I64, _I32, _I32, _U64, _P, _P, _P, _SZ, _P, _P]),
     ("tq_kv_fetch", ctypes.c_int, [_QW, _P, ctypes.c_int, _P]),
+    ("tq_rotate_dense", ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _P, _P, ctypes.c_int, _P]),
+    ("tq_encode_dense", ctypes.c_int,
+     [_P, ctypes.c_int, _I64, _I64, _P, _I32, _I32, _P, _P, _P, _SZ, _P]),
     ("tq_expert_cache_bytes", _SZ, [_I32, _I64]),
     ("tq_expert_cache_init", ctypes.c_int, [_P, _SZ, _I32, _I64]),
     ("tq_expert_cache_fetch", ctypes.c_int, [_P, _QW, _QW, _P, _I32, _P, _P, _P, _P, _P]),
@@ -152,7 +156,8 @@ class QWeight:
     seed: int
 
     def desc(self):
-        return _QWeight(self.codes.data_ptr(), self.scales.data_ptr(), self.signs.data_ptr(),
+        sg = self.signs.data_ptr() if self.signs.numel() else 0
+        return _QWeight(self.codes.data_ptr(), self.scales.data_ptr(), sg,
                         self.levels, self.group, self.K, self.N, self.E)
 
     def expert(self, e):
@@ -280,6 +285,49 @@ def qmv(qw, x, out_dtype=torch.float32, rotated=False, out=None):
     _check(lib().tq_qmv(ctypes.byref(d), _ptr(x), _dt(x), _ptr(y), _dt(y),
                         X_ROTATED if rotated else 0, None, 0, _stream()))
     return y
+
+
+def rotate_dense(x, R, out_dtype=torch.float32, out=None):
+    """R x for each row of x ([rows, K]); R a [K, K] float32 rotation on the same device."""
+    x = x.contiguous()
+    K = x.shape[-1]
+    rows = x.numel() // K
+    if R.dtype != torch.float32 or tuple(R.shape) != (K, K):
+        raise ValueError("R must be a float32 [K, K] tensor")
+    R = R.contiguous()
+    o = out if out is not None else torch.empty(x.shape, dtype=out_dtype, device=x.device)
+    with torch.cuda.device(x.device):
+        _check(lib().tq_rotate_dense(_ptr(x), _dt(x), rows, K, _ptr(R), _ptr(o), _dt(o),
+                                     _stream(x.device)))
+    return o
+
+
+def encode_dense(W, R, levels, group, ws_bytes=256 << 20, out=None):
+    """encode() with the dense rotation R ([K, K] float32) in place of the Hadamard one. The
+    returned QWeight has no sign bits (signs is an empty tensor): run its layers on inputs
+    rotated with rotate_dense(x, R) and rotated=True. seed is recorded as -1."""
+    if W.dim() == 2:
+        W = W.unsqueeze(0)
+    W = W.contiguous()
+    E, N, K = W.shape
+    if R.dtype != torch.float32 or tuple(R.shape) != (K, K):
+        raise ValueError("R must be a float32 [K, K] tensor")
+    R = R.contiguous()
+    wpr = words_per_row(K, levels)
+    if out is None:
+        codes = torch.empty((E, N, wpr), dtype=torch.int32, device=W.device)
+        scales = torch.empty((E, N, K // group), dtype=torch.float16, device=W.device)
+    else:
+        codes, scales = out.codes, out.scales
+    nbytes = min(ws_bytes, E * N * K * 8)
+    nbytes = max(nbytes, K * 8)
+    ws = _workspace(nbytes, W.device)
+    with torch.cuda.device(W.device):
+        _check(lib().tq_encode_dense(_ptr(W), _dt(W), E * N, K, _ptr(R), levels, group,
+                                     _ptr(codes), _ptr(scales), _ptr(ws), nbytes,
+                                     _stream(W.device)))
+    empty = torch.empty(0, dtype=torch.int32, device=W.device)
+    return QWeight(codes, scales, empty, levels, group, K, N, E, -1)
 
 
 def kv_fetch(qw, out_dtype=torch.bfloat16, out=None):

@@ -43,17 +43,23 @@ __global__ __launch_bounds__(kBlock) void k_encode(const void* W, int64_t rows, 
   uint32_t* sb = reinterpret_cast<uint32_t*>(rinv + ngroups);  // ceil(K / 32)
   uint8_t* idx = reinterpret_cast<uint8_t*>(sb + (K + 31) / 32);  // K
 
-  fill_sign_words(sb, K, seed);
+  // WDT 3: rows already rotated (fp64, a dense rotation applied by k_dense_rot): no signs,
+  // no Hadamard transform, and the caller passes inv_sqrt_k = 1
+  if constexpr (WDT != 3) fill_sign_words(sb, K, seed);
   __syncthreads();
 
   for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
     const int64_t base = row * K;
     for (int i = threadIdx.x; i < K; i += kBlock) {
-      const double w = static_cast<double>(load_elem<WDT>(W, base + i));
-      v[i] = ((sb[i >> 5] >> (i & 31)) & 1u) ? -w : w;
+      if constexpr (WDT == 3) {
+        v[i] = static_cast<const double*>(W)[base + i];
+      } else {
+        const double w = static_cast<double>(load_elem<WDT>(W, base + i));
+        v[i] = ((sb[i >> 5] >> (i & 31)) & 1u) ? -w : w;
+      }
     }
     __syncthreads();
-    hadamard_lds<double>(v, 1, m, P);
+    if constexpr (WDT != 3) hadamard_lds<double>(v, 1, m, P);
 
     // group sums of squares: partial sums over runs, then per group
     for (int r = threadIdx.x; r < K / run; r += kBlock) {
@@ -119,7 +125,7 @@ static hipError_t launch_encode_l(const void* W, int64_t rows, int K, int m, int
                      ((K + 31) / 32) * 4 + K;
   int wpr = levels == 3 ? (K + 19) / 20 : (K * (levels == 4 ? 2 : levels == 8 ? 3 : 4) + 31) / 32;
   const int grid = static_cast<int>(rows < 4096 ? rows : 4096);
-  const double isk = 1.0 / __builtin_sqrt(static_cast<double>(K));
+  const double isk = WDT == 3 ? 1.0 : 1.0 / __builtin_sqrt(static_cast<double>(K));
   void (*kern)(const void*, int64_t, int, int, int, int, uint64_t, CodebookArgs, uint32_t*,
                uint16_t*, int, double) = nullptr;
   switch (levels) {
@@ -151,6 +157,12 @@ hipError_t launch_encode(const void* W, int wdt, int64_t rows, int K, int m, int
     case 1: return launch_encode_l<1>(W, rows, K, m, P, levels, group, seed, codes, scales, s);
     default: return launch_encode_l<2>(W, rows, K, m, P, levels, group, seed, codes, scales, s);
   }
+}
+
+hipError_t launch_encode_rotated(const double* V, int64_t rows, int K, int levels, int group,
+                                 uint32_t* codes, uint16_t* scales, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  return launch_encode_l<3>(V, rows, K, 1, K, levels, group, 0, codes, scales, s);
 }
 
 }  // namespace tq

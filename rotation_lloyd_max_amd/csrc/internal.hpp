@@ -48,6 +48,13 @@ hipError_t launch_fwht(const void* x, int xdt, int64_t rows, int K, int m, int P
 hipError_t launch_encode(const void* W, int wdt, int64_t rows, int K, int m, int P,
                          int levels, int group, uint64_t seed, uint32_t* codes,
                          uint16_t* scales, hipStream_t s);
+// Encode of rows already rotated (fp64): group RMS, fp16 scale, snap, pack.
+hipError_t launch_encode_rotated(const double* V, int64_t rows, int K, int levels, int group,
+                                 uint32_t* codes, uint16_t* scales, hipStream_t s);
+// out = x R^T (dense rotation, fp64 matrix cores); odt 3 = fp64 output.
+hipError_t launch_dense_rot(const void* x, int xdt, int64_t rows, int K, const float* R, void* out,
+                            int odt, hipStream_t s);
+
 // The register-resident encode for K = 2^p, 64 <= K <= 4096 (W 16-byte aligned).
 bool encode_p2_supported(int K, int m);
 hipError_t launch_encode_p2(const void* W, int wdt, int64_t rows, int K, int levels, int group,

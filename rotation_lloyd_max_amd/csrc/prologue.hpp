@@ -30,7 +30,8 @@ struct InputLoad {
   int dt;
 
   // Segment j of thread t covers elements 16 * (t + NT * j) + 0..15 of row `row`.
-  // `signs` must be a valid pointer (finish() ignores the signs of a rotated input).
+  // `signs` is null for an input that is already rotated: then no sign word is read (the
+  // weight may have none) and finish() applies none.
   __device__ __forceinline__ void issue(const void* x, int xdt, int64_t row, int K,
                                         const uint32_t* signs) {
     dt = xdt;
@@ -50,7 +51,7 @@ struct InputLoad {
         raw[j][4 * v + 0] = a.x; raw[j][4 * v + 1] = a.y;
         raw[j][4 * v + 2] = a.z; raw[j][4 * v + 3] = a.w;
       }
-      sw[j] = signs[sgi >> 1];
+      sw[j] = signs ? signs[sgi >> 1] : 0u;
     }
   }
 

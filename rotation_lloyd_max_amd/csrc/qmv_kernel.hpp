@@ -174,7 +174,7 @@ struct QmvInput {
     mrot = false;
     if constexpr (!X32 && HALF) mrot = p.mrot != 0;
     if (mrot) mr.issue(p.x, p.signs);
-    else xin.issue(p.x, p.xdt, 0, p.K, p.signs);
+    else xin.issue(p.x, p.xdt, 0, p.K, p.rotated ? nullptr : p.signs);
   }
 
   // Returns sc (x' in xh is sc times the rotated input, rounded to fp16); *out_scale gets

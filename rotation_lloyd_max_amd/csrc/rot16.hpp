@@ -54,7 +54,7 @@ __global__ __launch_bounds__(NT) void k_rot16(Rot16Params p) {
   }
   const int64_t src = p.rows ? p.rows[r] : r;
   InputLoad<X32, NT, MAXK> xin;
-  xin.issue(p.x, p.xdt, src, p.K, p.signs);
+  xin.issue(p.x, p.xdt, src, p.K, p.rotated ? nullptr : p.signs);
   float out_scale;
   const bool rotated = p.rotated != 0;
   const float sc = xin.template finish_a<true>(xf, red, p.K, p.lk, p.P, rotated, p.inv_sqrt_k,

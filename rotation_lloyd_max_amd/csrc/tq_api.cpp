@@ -191,8 +191,11 @@ bool valid_dtype(int d) { return d == TQ_F32 || d == TQ_BF16 || d == TQ_F16; }
 size_t dtype_size(int d) { return d == TQ_F32 ? 4 : 2; }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// allow256: the 8-bit codebook (KV-cache rows), for power-of-two K up to 4096 only
-int check_shape(int64_t K, int levels, int group, int* m, int* P, bool allow256 = false) {
+// allow256: the 8-bit codebook (KV-cache rows), for power-of-two K up to 4096 only;
+// any_k: no Hadamard transform is applied (pre-rotated inputs, dense rotations,
+// dequantization), so K need only be a multiple of 32 in [64, 8192]
+int check_shape(int64_t K, int levels, int group, int* m, int* P, bool allow256 = false,
+                bool any_k = false) {
   if (levels == 256 && allow256) {
     if (K < 64 || K > 4096 || (K & (K - 1)) != 0)
       return fail(TQ_ERR_UNSUPPORTED, "256 levels need K a power of two in [64, 4096] (got %lld)",
@@ -206,27 +209,36 @@ int check_shape(int64_t K, int levels, int group, int* m, int* P, bool allow256 
   if (K < 64 || K > 8192 || K % 32 != 0)
     return fail(TQ_ERR_UNSUPPORTED, "K must be a multiple of 32 in [64, 8192] (got %lld)",
                 static_cast<long long>(K));
-  if (!split_dim(K, m, P))
-    return fail(TQ_ERR_UNSUPPORTED, "K=%lld is not m*2^k with m in {1, 12, 20, 28}",
-                static_cast<long long>(K));
+  if (!split_dim(K, m, P)) {
+    if (!any_k)
+      return fail(TQ_ERR_UNSUPPORTED,
+                  "K=%lld is not m*2^k with m in {1, 12, 20, 28} (a dense rotation and "
+                  "TQ_X_ROTATED inputs take any multiple of 32)",
+                  static_cast<long long>(K));
+    *m = 1;
+    *P = static_cast<int>(K);
+  }
   if (K % group != 0)
     return fail(TQ_ERR_UNSUPPORTED, "group %d does not divide K=%lld", group,
                 static_cast<long long>(K));
   return TQ_OK;
 }
 
-int check_weight(const tq_qweight* w, WeightArgs* out, bool allow256 = false) {
+// rotated: the call applies no rotation of its own (TQ_X_ROTATED inputs, dequantization), so
+// K may be any multiple of 32 in [64, 8192] and the sign bits are not needed
+int check_weight(const tq_qweight* w, WeightArgs* out, bool allow256 = false,
+                 bool rotated = false) {
   if (!w) return fail(TQ_ERR_ARG, "weight descriptor is NULL");
   int m = 1, P = 1;
-  const int rc = check_shape(w->K, w->n_levels, w->group, &m, &P, allow256);
+  const int rc = check_shape(w->K, w->n_levels, w->group, &m, &P, allow256, rotated);
   if (rc != TQ_OK) return rc;
   if (w->N < 0 || w->N > (1 << 24)) return fail(TQ_ERR_ARG, "N out of range");
   if (w->E < 1 || w->E > 8192) return fail(TQ_ERR_ARG, "E must be in [1, 8192]");
   if (w->N > 0) {
-    if (!w->codes || !w->scales || !w->signs)
+    if (!w->codes || !w->scales || (!w->signs && !rotated))
       return fail(TQ_ERR_ARG, "codes, scales and signs must be non-NULL");
     if (!aligned(w->codes, 16)) return fail(TQ_ERR_ALIGN, "codes must be 16-byte aligned");
-    if (!aligned(w->scales, 2) || !aligned(w->signs, 4))
+    if (!aligned(w->scales, 2) || (w->signs && !aligned(w->signs, 4)))
       return fail(TQ_ERR_ALIGN, "scales/signs misaligned");
   }
   out->codes = w->codes;
@@ -419,12 +431,13 @@ int tq_fwht(const void* x, tq_dtype x_dtype, int64_t rows, int64_t K, uint64_t s
 
 size_t tq_workspace_bytes(int32_t op, const tq_qweight* w, int64_t count, int64_t T) {
   WeightArgs a{};
-  if (check_weight(w, &a) != TQ_OK || count < 0 || T < 0) return SIZE_MAX;
+  if (check_weight(w, &a, false, /*rotated=*/true) != TQ_OK || count < 0 || T < 0) return SIZE_MAX;
   switch (op) {
     case TQ_OP_QMV:
     case TQ_OP_GATHER_QMV: return 0;
     case TQ_OP_MULTI_GATHER_QMV: return multi_gather_workspace(a, count);
     case TQ_OP_GATHER_QMM: return gather_qmm_workspace(a, count, T);
+    case TQ_OP_ENCODE_DENSE: return static_cast<size_t>(count) * a.K * 8;
     default: fail(TQ_ERR_ARG, "unknown op %d", op); return SIZE_MAX;
   }
 }
@@ -434,7 +447,7 @@ int tq_qmv(const tq_qweight* w, const void* x, tq_dtype x_dtype, void* y, tq_dty
   (void)ws;
   (void)ws_bytes;
   WeightArgs a{};
-  int rc = check_weight(w, &a);
+  int rc = check_weight(w, &a, false, (flags & TQ_X_ROTATED) != 0);
   if (rc != TQ_OK) return rc;
   if (a.E != 1) return fail(TQ_ERR_ARG, "tq_qmv needs E = 1 (use tq_gather_qmv for experts)");
   rc = check_io(x, x_dtype, y, y_dtype, a.N > 0);
@@ -450,7 +463,7 @@ int tq_gather_qmv(const tq_qweight* w, const int32_t* ids, int32_t n, const void
   (void)ws;
   (void)ws_bytes;
   WeightArgs a{};
-  int rc = check_weight(w, &a);
+  int rc = check_weight(w, &a, false, (flags & TQ_X_ROTATED) != 0);
   if (rc != TQ_OK) return rc;
   if (n < 0) return fail(TQ_ERR_ARG, "n must be >= 0");
   if (n > 0 && !ids) return fail(TQ_ERR_ARG, "ids is NULL");
@@ -466,7 +479,7 @@ int tq_multi_gather_qmv(const tq_qweight* w, const int32_t* ids, int64_t P, cons
                         tq_dtype x_dtype, void* y, tq_dtype y_dtype, uint32_t flags, void* ws,
                         size_t ws_bytes, void* stream) {
   WeightArgs a{};
-  int rc = check_weight(w, &a);
+  int rc = check_weight(w, &a, false, (flags & TQ_X_ROTATED) != 0);
   if (rc != TQ_OK) return rc;
   if (P < 0 || P > (1 << 30)) return fail(TQ_ERR_ARG, "P out of range");
   if (P > 0 && !ids) return fail(TQ_ERR_ARG, "ids is NULL");
@@ -487,7 +500,7 @@ int tq_multi_gather_qmv_static(const tq_qweight* w, const int32_t* ids, int64_t 
                                const void* x, tq_dtype x_dtype, void* y, tq_dtype y_dtype,
                                uint32_t flags, void* stream) {
   WeightArgs a{};
-  int rc = check_weight(w, &a);
+  int rc = check_weight(w, &a, false, (flags & TQ_X_ROTATED) != 0);
   if (rc != TQ_OK) return rc;
   if (P < 0 || P > (1 << 30)) return fail(TQ_ERR_ARG, "P out of range");
   if (P > 0 && !ids) return fail(TQ_ERR_ARG, "ids is NULL");
@@ -507,6 +520,57 @@ int tq_multi_gather_qmv_static(const tq_qweight* w, const int32_t* ids, int64_t 
   return hip_status(launch_multi_gather(a, ids, P, x, x_dtype, (flags & TQ_X_ROTATED) != 0, y,
                                         y_dtype, ws, static_cast<hipStream_t>(stream)),
                     "tq_multi_gather_qmv_static");
+}
+
+int tq_rotate_dense(const void* x, tq_dtype x_dtype, int64_t rows, int64_t K, const float* R,
+                    void* out, tq_dtype out_dtype, void* stream) {
+  if (K < 64 || K > 8192 || K % 32 != 0)
+    return fail(TQ_ERR_UNSUPPORTED, "K must be a multiple of 32 in [64, 8192] (got %lld)",
+                static_cast<long long>(K));
+  if (rows < 0) return fail(TQ_ERR_ARG, "rows must be >= 0");
+  if (!valid_dtype(x_dtype) || !valid_dtype(out_dtype)) return fail(TQ_ERR_ARG, "bad dtype");
+  if (rows == 0) return TQ_OK;
+  if (!x || !R || !out) return fail(TQ_ERR_ARG, "x, R and out must be non-NULL");
+  if (!aligned(x, dtype_size(x_dtype)) || !aligned(R, 4) || !aligned(out, dtype_size(out_dtype)))
+    return fail(TQ_ERR_ALIGN, "x, R or out misaligned");
+  if ((rows + 63) / 64 > 65535) return fail(TQ_ERR_ARG, "rows must be below 64 * 65536");
+  return hip_status(launch_dense_rot(x, x_dtype, rows, static_cast<int>(K), R, out, out_dtype,
+                                     static_cast<hipStream_t>(stream)),
+                    "tq_rotate_dense");
+}
+
+int tq_encode_dense(const void* W, tq_dtype w_dtype, int64_t rows, int64_t K, const float* R,
+                    int32_t n_levels, int32_t group, uint32_t* codes, uint16_t* scales,
+                    void* ws, size_t ws_bytes, void* stream) {
+  int m = 1, P = 1;
+  const int rc = check_shape(K, n_levels, group, &m, &P, false, /*any_k=*/true);
+  if (rc != TQ_OK) return rc;
+  if (!valid_dtype(w_dtype)) return fail(TQ_ERR_ARG, "bad weight dtype");
+  if (rows < 0) return fail(TQ_ERR_ARG, "rows must be >= 0");
+  if (rows == 0) return TQ_OK;
+  if (!W || !R || !codes || !scales) return fail(TQ_ERR_ARG, "W, R, codes and scales must be non-NULL");
+  if (!aligned(W, dtype_size(w_dtype)) || !aligned(R, 4) || !aligned(codes, 4) ||
+      !aligned(scales, 2))
+    return fail(TQ_ERR_ALIGN, "W, R, codes or scales misaligned");
+  const size_t row_bytes = static_cast<size_t>(K) * 8;
+  if (!ws || ws_bytes < row_bytes)
+    return fail(TQ_ERR_WORKSPACE, "workspace of at least %zu bytes (one fp64 row) needed", row_bytes);
+  if (!aligned(ws, 8)) return fail(TQ_ERR_ALIGN, "workspace must be 8-byte aligned");
+  int64_t chunk = static_cast<int64_t>(ws_bytes / row_bytes);
+  if (chunk > 64 * 65535) chunk = 64 * 65535;
+  const int64_t wpr = words_per_row(K, n_levels), ngk = K / group;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const char* src = static_cast<const char*>(W);
+  hipError_t e = hipSuccess;
+  for (int64_t r0 = 0; r0 < rows && e == hipSuccess; r0 += chunk) {
+    const int64_t n = rows - r0 < chunk ? rows - r0 : chunk;
+    e = launch_dense_rot(src + static_cast<size_t>(r0) * K * dtype_size(w_dtype), w_dtype, n,
+                         static_cast<int>(K), R, ws, 3, st);
+    if (e == hipSuccess)
+      e = launch_encode_rotated(static_cast<const double*>(ws), n, static_cast<int>(K), n_levels,
+                                group, codes + r0 * wpr, scales + r0 * ngk, st);
+  }
+  return hip_status(e, "tq_encode_dense");
 }
 
 int tq_kv_fetch(const tq_qweight* w, void* out, tq_dtype out_dtype, void* stream) {
@@ -529,7 +593,7 @@ int tq_kv_fetch(const tq_qweight* w, void* out, tq_dtype out_dtype, void* stream
 int tq_dequant(const tq_qweight* w, const int32_t* ids, int64_t n, void* out,
                tq_dtype out_dtype, void* stream) {
   WeightArgs a{};
-  int rc = check_weight(w, &a);
+  int rc = check_weight(w, &a, false, /*rotated=*/true);
   if (rc != TQ_OK) return rc;
   if (!valid_dtype(out_dtype)) return fail(TQ_ERR_ARG, "bad dtype");
   if (n < 0 || n > 65535) return fail(TQ_ERR_ARG, "n must be in [0, 65535]");
@@ -547,7 +611,7 @@ int tq_gather_qmm(const tq_qweight* w, const void* x, tq_dtype x_dtype, int64_t 
                   const int32_t* row_token, const int32_t* expert_offsets, int64_t M, void* y,
                   tq_dtype y_dtype, uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
   WeightArgs a{};
-  int rc = check_weight(w, &a);
+  int rc = check_weight(w, &a, false, (flags & TQ_X_ROTATED) != 0);
   if (rc != TQ_OK) return rc;
   if (T < 0 || M < 0 || M > (1ll << 31) - 1 || T > (1ll << 31) - 1)
     return fail(TQ_ERR_ARG, "T and M must be in [0, 2^31)");

@@ -35,7 +35,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 19, names
+    assert len(names) == 21, names
     handle = ctypes.CDLL(tq.LIB_PATH)
     for n in names:
         assert hasattr(handle, n), n
@@ -96,7 +96,12 @@ def test_validation_statuses():
     assert qmv_status(None) == ERR_ARG
     assert qmv_status(desc(n_levels=5)) == ERR_UNSUPPORTED
     assert qmv_status(desc(group=8)) == ERR_UNSUPPORTED
-    assert qmv_status(desc(K=4864)) == ERR_UNSUPPORTED     # 4864 = 19 * 256
+    assert qmv_status(desc(K=4864)) == ERR_UNSUPPORTED     # 4864 = 19 * 256: no Hadamard
+    # ...but a pre-rotated input needs none (N = 0: accepted, and nothing is launched)
+    assert tq.lib().tq_qmv(ctypes.byref(desc(K=4864, signs=0, N=0)), 16, 0, 16, 0, 1, None, 0,
+                           None) == 0
+    assert tq.lib().tq_qmv(ctypes.byref(desc(K=4864, signs=0, N=0)), 16, 0, 16, 0, 0, None, 0,
+                           None) == ERR_UNSUPPORTED
     assert qmv_status(desc(K=16384)) == ERR_UNSUPPORTED    # above the size limit
     assert qmv_status(desc(K=96, group=64)) == ERR_UNSUPPORTED  # group does not divide K
     assert qmv_status(desc(codes=0)) == ERR_ARG
@@ -152,6 +157,16 @@ def test_validation_statuses():
     assert b"8388608" in L.tq_last_error()
     assert L.tq_multi_gather_qmv_static(ctypes.byref(d2), None, 4, 16, 1, 16, 0, 0,
                                         None) == ERR_ARG
+    # dense rotation: shapes, pointers, workspace
+    assert L.tq_rotate_dense(16, 0, 2, 100, 16, 16, 0, None) == ERR_UNSUPPORTED
+    assert L.tq_rotate_dense(16, 0, 2, 4864, 0, 16, 0, None) == ERR_ARG
+    assert L.tq_rotate_dense(16, 0, 2, 4864, 18, 16, 0, None) == ERR_ALIGN
+    assert L.tq_rotate_dense(0, 0, 0, 4864, 0, 0, 0, None) == 0
+    assert L.tq_encode_dense(16, 1, 4, 4864, 16, 8, 128, 16, 16, 16, 4864 * 8 - 1,
+                             None) == ERR_WORKSPACE
+    assert L.tq_encode_dense(16, 1, 4, 4864, 16, 8, 100, 16, 16, 16, 1 << 20,
+                             None) == ERR_UNSUPPORTED
+    assert L.tq_workspace_bytes(5, ctypes.byref(desc(K=4864, signs=0)), 10, 0) == 10 * 4864 * 8
     # KV fetch: formats and lengths outside its set are refused; 256 levels only there
     assert L.tq_kv_fetch(ctypes.byref(desc(n_levels=3, group=16)), 256, 1, None) == ERR_UNSUPPORTED
     assert L.tq_kv_fetch(ctypes.byref(desc(K=4096)), 256, 1, None) == ERR_UNSUPPORTED

@@ -16,6 +16,7 @@ exact bytes back.
 """
 
 from dataclasses import dataclass, field
+from functools import lru_cache
 
 import numpy as np
 
@@ -51,6 +52,21 @@ def gaussian(g, rows, K, outliers=0, factor=20.0):
         ch = g.choice(K, outliers, replace=False)
         x[:, ch] *= factor
     return x
+
+
+@lru_cache(maxsize=8)
+def haar_rotation(K, seed):
+    """A random K x K rotation from a seeded Gaussian matrix G: the orthogonal factor Q of
+    G = Q R with the signs of R's diagonal moved into Q (Q diag(sign(diag R))), which makes Q
+    Haar-distributed; rounded to float32, the form both sides read. This is the rotation's
+    random draw (the QR-derived rotation of VeloxQuant-MLX), generated here like every
+    other seeded input."""
+    G = np.random.Generator(np.random.PCG64(np.random.SeedSequence([77, K, seed]))).standard_normal((K, K))
+    Q, Rr = np.linalg.qr(G)
+    Q = Q * np.sign(np.diag(Rr))[None, :]
+    Q = Q.astype(np.float32)
+    Q.flags.writeable = False  # cached: shared by every caller
+    return Q
 
 
 def kv_rows(g, tokens, heads, d, outliers=4, factor=20.0):
