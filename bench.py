@@ -28,8 +28,8 @@ not in the timed region.
 
 Other workloads (--config 3, 4, 5, 6, 7, 8) time gather_qmv, multi_gather_qmv, gather_qmm,
 dequant, the streamed encode from pinned host memory, the MoE decode with its experts
-streamed from pinned host memory and the KV-cache fetch (--config 9), for reference; the
-default line is the dense decode layer.
+streamed from pinned host memory, the KV-cache fetch (--config 9) and a layer with a dense
+rotation (--config 10), for reference; the default line is the dense decode layer.
 """
 
 import argparse
@@ -50,11 +50,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5, 6, 7, 8, 9],
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5, 6, 7, 8, 9, 10],
                     help="2 dense qmv (default), 3 gather_qmv, 4 multi_gather_qmv, "
                          "5 gather_qmm, 6 dequant of an expert stack, 7 encode of an "
                          "expert stack streamed from pinned host memory, 8 MoE decode with "
-                         "its experts streamed from pinned host memory, 9 KV-cache fetch")
+                         "its experts streamed from pinned host memory, 9 KV-cache fetch, "
+                         "10 a layer with a dense (QR) rotation, K = 4864")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-moe", action="store_true",
                     help="default line without the MoE decode (gather_qmv) sub-measurement")
@@ -762,6 +763,66 @@ def bench_kv(args):
     }
 
 
+def bench_dense_rotation(args):
+    """A layer whose input dimension has no Hadamard matrix (K = 4864 = 19 x 256, the
+    dimension VeloxQuant-MLX falls back to a QR rotation for): W 4096 x 4864 bf16, a Haar
+    rotation R (4864 x 4864 fp32, 95 MB), 3-bit g128. Timed: the encode (R applied on the
+    fp64 matrix cores, then snap and pack), R applied to one token (the whole matrix read
+    per token) and to a batch of 4096 tokens, and one pre-rotated qmv."""
+    import numpy as np
+    import torch
+    import rotation_lloyd_max_amd as tq
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    N, K, L, G = 4096, 4864, 8, 128
+    R = torch.from_numpy(np.array(wl.haar_rotation(K, 1))).to(dev)
+    gen = wl.torch_generator(dev, 10, wl.T_W)
+    W = wl.torch_student_rows(gen, N, K, dev, torch.bfloat16)
+    x1 = torch.randn((1, K), generator=gen, device=dev).to(torch.bfloat16)
+    xb = torch.randn((4096, K), generator=gen, device=dev).to(torch.bfloat16)
+    qw = tq.encode_dense(W, R, L, G)
+    y1 = torch.empty((1, K), dtype=torch.float32, device=dev)
+    yb = torch.empty((4096, K), dtype=torch.bfloat16, device=dev)
+    out = torch.empty(N, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    enc_ms = timed(lambda: tq.encode_dense(W, R, L, G, out=qw), max(2, args.steps // 5))
+    r1_ms = timed(lambda: tq.rotate_dense(x1, R, out=y1), args.steps)
+    rb_ms = timed(lambda: tq.rotate_dense(xb, R, out=yb), max(2, args.steps // 5))
+    q_ms = timed(lambda: tq.qmv(qw, y1[0], rotated=True, out=out), args.steps)
+    fl_enc = 2.0 * N * K * K
+    fl_b = 2.0 * 4096 * K * K
+    return {
+        "metric": "dense-rotation layer (K = 4864): encode and batch rotation on fp64 matrix cores, TFLOP/s",
+        "value": round(fl_enc / (enc_ms / 1e3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": 1, "ms_per_step": round(enc_ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f64 MFMA (rotation), f16*f16->f32 (qmv)", "data": "synthetic",
+        "config": {"workload": "W 4096 x 4864 bf16, Haar rotation 4864 x 4864 fp32, 3-bit g128"},
+        "roofline": {"bound": "mfma", "achieved": round(fl_enc / (enc_ms / 1e3) / 1e12, 3),
+                     "peak": 78.6, "unit": "TFLOP/s",
+                     "frac": round(fl_enc / (enc_ms / 1e3) / 1e12 / 78.6, 4), "traffic": None},
+        "encode_ms": round(enc_ms, 4),
+        "rotate_one_token_us": round(r1_ms * 1e3, 3),
+        "rotate_one_token_gb_per_s_of_R": round(K * K * 4 / (r1_ms / 1e3) / 1e9, 3),
+        "rotate_4096_tokens_ms": round(rb_ms, 4),
+        "rotate_4096_tokens_tflops": round(fl_b / (rb_ms / 1e3) / 1e12, 3),
+        "qmv_pre_rotated_us": round(q_ms * 1e3, 3),
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -788,6 +849,8 @@ def main():
         out = bench_expert_stream(args)
     elif args.config == 9:
         out = bench_kv(args)
+    elif args.config == 10:
+        out = bench_dense_rotation(args)
     else:
         out = bench_moe(args)
     print(json.dumps(out), flush=True)

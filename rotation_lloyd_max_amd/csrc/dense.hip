@@ -6,7 +6,8 @@
 // sums keep fp64 precision, so the encode that follows makes the same decisions as an fp64
 // evaluation; activations are rounded once to their output type.
 //
-// Tiling: one 256-thread workgroup per 64 x 64 output tile, each wave a 32 x 32 quarter as
+// Up to eight rows (decode) take k_dense_rot_vec, a streaming read of R. More rows:
+// tiling: one 256-thread workgroup per 64 x 64 output tile, each wave a 32 x 32 quarter as
 // 2 x 2 MFMA tiles; K in steps of 16 through LDS (rows padded to 17 values, so the 16 rows
 // a fragment reads fall on distinct banks). Fragment layout of the 16x16x4 f64 instruction:
 // lane l holds A[l % 16][l / 16] and B[l / 16][l % 16] and receives D[l / 16 + 4 r][l % 16]
@@ -90,8 +91,68 @@ __global__ __launch_bounds__(kDrThreads) void k_dense_rot(DenseParams p) {
       }
 }
 
+// Few rows (decode): the product is a read of R, so one wave per output element i streams
+// row i of R with coalesced 16-byte loads and multiplies it by up to kDrVecRows input rows
+// held in LDS as fp64; fp64 sums as in k_dense_rot, reduced across the wave at the end.
+constexpr int kDrVecRows = 8;
+constexpr int kDrVecWaves = 4;
+
+template <int XDT, int ODT>
+__global__ __launch_bounds__(64 * kDrVecWaves) void k_dense_rot_vec(DenseParams p) {
+  extern __shared__ double xv[];  // [rows][K]
+  const int K = p.K, rows = static_cast<int>(p.rows);
+  for (int i = threadIdx.x; i < rows * K; i += 64 * kDrVecWaves) xv[i] = dr_load<XDT>(p.x, i);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * kDrVecWaves + (threadIdx.x >> 6);
+  if (n >= K) return;
+  const float* rrow = p.R + static_cast<int64_t>(n) * K;
+  double acc[kDrVecRows];
+#pragma unroll
+  for (int t = 0; t < kDrVecRows; ++t) acc[t] = 0.0;
+  for (int k = 4 * lane; k < K; k += 256) {
+    const float4 r = *reinterpret_cast<const float4*>(rrow + k);
+    const double rv[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int t = 0; t < kDrVecRows; ++t) {
+      if (t >= rows) break;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[t] = __builtin_fma(rv[q], xv[t * K + k + q], acc[t]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kDrVecRows; ++t) {
+    if (t >= rows) break;
+    double v = acc[t];
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    if (lane == 0) {
+      if constexpr (ODT == 3) static_cast<double*>(p.out)[static_cast<int64_t>(t) * K + n] = v;
+      else store_any(p.out, ODT, static_cast<int64_t>(t) * K + n, static_cast<float>(v));
+    }
+  }
+}
+
+template <int XDT>
+hipError_t launch_dr_vec(const DenseParams& p, int odt, hipStream_t s) {
+  const dim3 grid((p.K + kDrVecWaves - 1) / kDrVecWaves);
+  const size_t lds = static_cast<size_t>(p.rows) * p.K * 8;
+  void (*k)(DenseParams) = odt == 0 ? k_dense_rot_vec<XDT, 0>
+                           : odt == 1 ? k_dense_rot_vec<XDT, 1>
+                           : odt == 2 ? k_dense_rot_vec<XDT, 2> : k_dense_rot_vec<XDT, 3>;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k, grid, dim3(64 * kDrVecWaves), lds, s, p);
+  return hipGetLastError();
+}
+
 template <int XDT>
 hipError_t launch_dr_x(const DenseParams& p, int odt, hipStream_t s) {
+  // up to kDrVecRows rows whose fp64 copies fit LDS: the streaming product
+  if (p.rows <= kDrVecRows && p.rows * p.K * 8 <= 160 * 1024) return launch_dr_vec<XDT>(p, odt, s);
   const dim3 grid((p.K + kDrTile - 1) / kDrTile, static_cast<unsigned>((p.rows + kDrTile - 1) / kDrTile));
   switch (odt) {
     case 0: hipLaunchKernelGGL((k_dense_rot<XDT, 0>), grid, dim3(kDrThreads), 0, s, p); break;

@@ -25,7 +25,7 @@ def rot(K, seed=1):
     return R, torch.from_numpy(np.array(R)).cuda()
 
 
-@pytest.mark.parametrize("K,rows", [(4864, 1), (4864, 70), (160, 130), (640, 65)])
+@pytest.mark.parametrize("K,rows", [(4864, 1), (4864, 3), (4864, 70), (160, 130), (640, 65), (640, 8)])
 @pytest.mark.parametrize("xdt,odt", [(torch.bfloat16, torch.float32), (torch.float32, torch.float32),
                                      (torch.float16, torch.bfloat16)])
 def test_rotate_dense(K, rows, xdt, odt):
