@@ -131,9 +131,10 @@ __device__ __forceinline__ T hadamard_row(const T (&x)[M], std::integer_sequence
   return acc;
 }
 
-// One side of H_28 x (SIDE 0: the 14 outputs y_2R; SIDE 1: the outputs y_2R+1).
-template <typename T, int SIDE>
-__device__ __forceinline__ void hadamard28_side(const T (&x)[28], T (&out)[14]) {
+// One side of H_28 x (SIDE 0: the 14 outputs y_2R; SIDE 1: the outputs y_2R+1), each
+// handed to put(R, y) as soon as it is computed (few registers live at once).
+template <typename T, int SIDE, typename Put>
+__device__ __forceinline__ void hadamard28_side(const T (&x)[28], Put put) {
   T u[14], v[14];
 #pragma unroll
   for (int c = 0; c < 14; ++c) { u[c] = x[2 * c] + x[2 * c + 1]; v[c] = x[2 * c] - x[2 * c + 1]; }
@@ -145,13 +146,13 @@ __device__ __forceinline__ void hadamard28_side(const T (&x)[28], T (&out)[14]) 
 #pragma unroll
   for (int k = 0; k < 13; ++k) pr[k] = a[1 + k] + a[1 + (k + 1) % 13];
   const T base = a[0] - W;
-  out[0] = SIDE == 0 ? W + v[0] : W - u[0];
+  put(0, SIDE == 0 ? W + v[0] : W - u[0]);
 #pragma unroll
   for (int r = 0; r < 13; ++r) {
     const T q = a[1 + (r + 12) % 13] + a[1 + (r + 1) % 13];
     const T A = pr[(r + 9) % 13] + pr[(r + 3) % 13] + q;
     const T sum = 2 * A + (base + a[1 + r]);
-    out[r + 1] = SIDE == 0 ? sum + v[r + 1] : sum - u[r + 1];
+    put(r + 1, SIDE == 0 ? sum + v[r + 1] : sum - u[r + 1]);
   }
 }
 
@@ -167,17 +168,8 @@ __device__ __forceinline__ void hadamard_part(T* col, int pstride, const T (&x)[
   };
   if constexpr (M == 28) {
     static_assert(TPC <= 2, "H_28 is split into at most two sides");
-    T out[14];
-    if constexpr (TPC == 1 || Q == 0) {
-      hadamard28_side<T, 0>(x, out);
-#pragma unroll
-      for (int R = 0; R < 14; ++R) put(2 * R, out[R]);
-    }
-    if constexpr (TPC == 1 || Q == 1) {
-      hadamard28_side<T, 1>(x, out);
-#pragma unroll
-      for (int R = 0; R < 14; ++R) put(2 * R + 1, out[R]);
-    }
+    if constexpr (TPC == 1 || Q == 0) hadamard28_side<T, 0>(x, [&](int R, T y) { put(2 * R, y); });
+    if constexpr (TPC == 1 || Q == 1) hadamard28_side<T, 1>(x, [&](int R, T y) { put(2 * R + 1, y); });
   } else {
     [&]<int... A>(std::integer_sequence<int, A...>) {
       ((A % TPC == Q ? (put(A, hadamard_row<T, M, A>(x, std::make_integer_sequence<int, M>{})), 0)

@@ -90,52 +90,130 @@ struct MgTile {
   int row0;    // first weight row of the workgroup
   int cnt;     // pairs of this tile (<= 16)
   int spc;     // scale groups per chunk (KC / group, at least 1)
+  uint32_t spc_inv;  // ceil(2^32 / spc): i / spc = umulhi(i, spc_inv) for i < 2^16
   int sst;     // LDS halves per row of scales
+  bool full;   // every row of the workgroup exists (row0 + ROWS <= N)
+  bool s32;    // scales staged as 4-byte pairs (K / group and spc even: 4-byte aligned)
   const uint32_t* cexp;   // the expert's codes
   const uint16_t* sexp;   // the expert's scales
   const int32_t* pairs;   // the tile's pair indices
+  // the row of staging index i (i / spc; i < 2^16)
+  __device__ __forceinline__ int row_of(int i) const {
+    return spc_inv ? static_cast<int>(__umulhi(static_cast<uint32_t>(i), spc_inv)) : i;
+  }
 };
 
-// Global -> registers for chunk c.
+// A thread's input units for the tile: byte offset of unit j's 16 bytes at K position 0
+// (chunk c adds 2 KC c), or kNoUnit for a unit that belongs to no pair of the tile.
+constexpr uint32_t kNoUnit = 0xffffffffu;
+template <int L>
+struct MgInputs {
+  uint32_t off[MgChunk<L>::AU];
+  __device__ __forceinline__ bool on(int j) const { return off[j] != kNoUnit; }
+};
+
+template <int L>
+__device__ __forceinline__ void mg_inputs(MgInputs<L>& in, const MgParams& p, const MgTile& t) {
+  using C = MgChunk<L>;
+  int tid = static_cast<int>(threadIdx.x);
+  __asm__ volatile("" : "+v"(tid));
+#pragma unroll
+  for (int j = 0; j < C::AU; ++j) {
+    const int i = tid + j * kMgThreads;
+    const int m = i / (C::KC / 8), u = i - m * (C::KC / 8);
+    in.off[j] = m < t.cnt
+                    ? (static_cast<uint32_t>(t.pairs[m]) * static_cast<uint32_t>(p.rowh) + 8u * u) * 2u
+                    : kNoUnit;
+  }
+}
+
+// Global -> registers for chunk c. Where the workgroup's rows all exist, consecutive load
+// steps move by whole rows, so their row offsets are uniform (scalar) and each load costs
+// no vector arithmetic; otherwise rows are clamped per lane.
 template <int L>
 __device__ __forceinline__ void mg_fetch(MgStage<L>& st, const MgParams& p, const MgTile& t, int c) {
   using C = MgChunk<L>;
+  MgInputs<L> in;
+  mg_inputs<L>(in, p, t);
   const int w0 = c * C::WPC;
   // the thread index is made opaque so that the per-load offsets are recomputed for every
   // chunk instead of being kept in registers for the whole loop
   int tid = static_cast<int>(threadIdx.x);
   __asm__ volatile("" : "+v"(tid));
-#pragma unroll
-  for (int j = 0; j < C::CW; ++j) {
-    const int i = tid + j * kMgThreads;
-    const int r = i / C::WPC, w = i - r * C::WPC;
-    int row = t.row0 + r;
-    row = row < p.N ? row : p.N - 1;
+  if constexpr (kMgThreads % C::WPC == 0) {
+    constexpr int RS = kMgThreads / C::WPC;  // rows per load step
+    const int r0 = tid / C::WPC, w = tid % C::WPC;
     int wi = w0 + w;
     wi = wi < p.wpr ? wi : p.wpr - 1;
-    st.c[j] = ld_at<uint32_t>(t.cexp, (static_cast<uint32_t>(row) * p.wpr + wi) * 4u);
+    if (t.full) {
+      // a running offset: one add per load, nothing kept across chunks
+      uint32_t off = (__umul24(static_cast<uint32_t>(t.row0 + r0), p.wpr) + wi) * 4u;
+      const uint32_t step = static_cast<uint32_t>(RS * 4) * p.wpr;
+#pragma unroll
+      for (int j = 0; j < C::CW; ++j) {
+        st.c[j] = ld_at<uint32_t>(t.cexp, off);
+        off += step;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < C::CW; ++j) {
+        int row = t.row0 + r0 + j * RS;
+        row = row < p.N ? row : p.N - 1;
+        st.c[j] = ld_at<uint32_t>(t.cexp, (__umul24(static_cast<uint32_t>(row), p.wpr) + wi) * 4u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < C::CW; ++j) {
+      const int i = tid + j * kMgThreads;
+      const int r = i / C::WPC, w = i - r * C::WPC;
+      int row = t.row0 + r;
+      row = row < p.N ? row : p.N - 1;
+      int wi = w0 + w;
+      wi = wi < p.wpr ? wi : p.wpr - 1;
+      // 24-bit multiplies (full rate; rows and words per row are below 2^24, checked on
+      // the host)
+      st.c[j] = ld_at<uint32_t>(t.cexp, (__umul24(static_cast<uint32_t>(row), p.wpr) + wi) * 4u);
+    }
   }
   const int g0 = (c * C::KC) >> p.lg_group;
   constexpr int NS = sizeof(st.s) / sizeof(st.s[0]);
+  if (kMgThreads % C::WPC == 0 && t.full && t.s32) {
+    // 4-byte pairs of groups: thread -> (row tid / 32 + 16 j, pair tid % 32); pairs past
+    // the chunk's groups read a valid pair and are not stored
+    static_assert(NS >= C::ROWS / (kMgThreads / 32), "scale staging registers");
+    const int r0 = tid >> 5;
+    int gi = g0 + 2 * (tid & 31);
+    gi = gi < p.ngk - 1 ? gi : p.ngk - 2;
+    uint32_t off = (__umul24(static_cast<uint32_t>(t.row0 + r0), p.ngk) + gi) * 2u;
+    const uint32_t step = static_cast<uint32_t>((kMgThreads / 32) * 2) * p.ngk;
 #pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    const int i = tid + j * kMgThreads;
-    const int r = i / t.spc, k = i - r * t.spc;
-    int row = t.row0 + (r < C::ROWS ? r : C::ROWS - 1);
-    row = row < p.N ? row : p.N - 1;
-    int gi = g0 + k;
-    gi = gi < p.ngk ? gi : p.ngk - 1;
-    st.s[j] = ld_at<uint16_t>(t.sexp, (static_cast<uint32_t>(row) * p.ngk + gi) * 2u);
+    for (int j = 0; j < C::ROWS / (kMgThreads / 32); ++j) {
+      st.s[j] = ld_at<uint32_t>(t.sexp, off);
+      off += step;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int i = tid + j * kMgThreads;
+      const int r = t.row_of(i), k = i - static_cast<int>(__umul24(r, t.spc));
+      int row = t.row0 + (r < C::ROWS ? r : C::ROWS - 1);
+      row = row < p.N ? row : p.N - 1;
+      int gi = g0 + k;
+      gi = gi < p.ngk ? gi : p.ngk - 1;
+      st.s[j] = ld_at<uint16_t>(t.sexp, (__umul24(static_cast<uint32_t>(row), p.ngk) + gi) * 2u);
+    }
   }
+  const uint32_t kbyte = static_cast<uint32_t>(c * C::KC) * 2u;
 #pragma unroll
   for (int j = 0; j < C::AU; ++j) {
     const int i = tid + j * kMgThreads;
-    const int m = i / (C::KC / 8), u = i - m * (C::KC / 8);
+    const int u = i % (C::KC / 8);
     const int e = c * C::KC + 8 * u;
-    if (m < t.cnt) {
-      const uint32_t row = static_cast<uint32_t>(t.pairs[m]);
-      const int ec = e < p.K ? e : p.K - 8;
-      const u32x4_t v = ld_at<u32x4_t>(p.xh, (row * static_cast<uint32_t>(p.rowh) + ec) * 2u);
+    if (in.on(j)) {
+      // a unit past K reads the row's last unit and is stored as zero
+      const uint32_t back = e < p.K ? 0u : static_cast<uint32_t>(e - (p.K - 8)) * 2u;
+      const u32x4_t v = ld_at<u32x4_t>(p.xh, in.off[j] + kbyte - back);
       st.a[j] = e < p.K ? v : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
@@ -153,11 +231,21 @@ __device__ __forceinline__ void mg_stash(const MgStage<L>& st, const MgTile& t, 
     lc[r * C::CST + w] = st.c[j];
   }
   constexpr int NS = sizeof(st.s) / sizeof(st.s[0]);
+  if (kMgThreads % C::WPC == 0 && t.full && t.s32) {
+    const int r0 = threadIdx.x >> 5, d = threadIdx.x & 31;
+    if (2 * d < t.spc) {
+      uint32_t* ls32 = reinterpret_cast<uint32_t*>(ls);
 #pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    const int i = threadIdx.x + j * kMgThreads;
-    const int r = i / t.spc, k = i - r * t.spc;
-    if (r < C::ROWS) ls[r * t.sst + k] = static_cast<uint16_t>(st.s[j]);
+      for (int j = 0; j < C::ROWS / (kMgThreads / 32); ++j)
+        ls32[__umul24(r0 + j * (kMgThreads / 32), t.sst >> 1) + d] = st.s[j];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int i = threadIdx.x + j * kMgThreads;
+      const int r = t.row_of(i), k = i - static_cast<int>(__umul24(r, t.spc));
+      if (r < C::ROWS) ls[__umul24(r, t.sst) + k] = static_cast<uint16_t>(st.s[j]);
+    }
   }
 #pragma unroll
   for (int j = 0; j < C::AU; ++j) {
@@ -175,7 +263,7 @@ __global__ __launch_bounds__(kMgThreads, 4) void k_mg(MgParams p) {
   __shared__ __attribute__((aligned(16))) uint32_t lut[mlut_bytes<L>() / 4];
   __shared__ __attribute__((aligned(16))) uint32_t lc[C::ROWS * C::CST];
   __shared__ __attribute__((aligned(16))) _Float16 la[16 * C::AST];
-  __shared__ uint16_t ls[C::ROWS * (kMaxScalesPerChunk + 2)];
+  __shared__ __attribute__((aligned(16))) uint16_t ls[C::ROWS * (kMaxScalesPerChunk + 2)];
   __shared__ uint16_t hs[16];
   const int e = blockIdx.y;
   const int off0 = p.offsets[e], cnt_all = p.offsets[e + 1] - off0;
@@ -187,7 +275,12 @@ __global__ __launch_bounds__(kMgThreads, 4) void k_mg(MgParams p) {
   MgTile t;
   t.row0 = blockIdx.x * C::ROWS;
   t.spc = (C::KC >> p.lg_group) > 0 ? (C::KC >> p.lg_group) : 1;
+  // the staging index i stays below 2^16, where the quotient by a multiply-high is exact
+  // (ceil(2^32 / d) d - 2^32 < d); d = 1 would need 2^32
+  t.spc_inv = t.spc > 1 ? 0xffffffffu / static_cast<uint32_t>(t.spc) + 1u : 0u;
   t.sst = t.spc + 2;
+  t.full = t.row0 + C::ROWS <= p.N;
+  t.s32 = (p.ngk % 2 == 0) && (t.spc % 2 == 0);
   t.cexp = p.codes + static_cast<int64_t>(e) * p.N * p.wpr;
   t.sexp = p.scales + static_cast<int64_t>(e) * p.N * p.ngk;
   const int nrow = wave * 16 + col;  // this lane's weight row within the workgroup
@@ -205,7 +298,6 @@ __global__ __launch_bounds__(kMgThreads, 4) void k_mg(MgParams p) {
       __syncthreads();
       build_mlut<L, kMgThreads>(lut, hs);
     }
-    const bool valid = col < t.cnt;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     for (int c = 0; c < nchunk; ++c) {
       __syncthreads();  // previous chunk's LDS reads are done
@@ -233,8 +325,10 @@ __global__ __launch_bounds__(kMgThreads, 4) void k_mg(MgParams p) {
         span_fragments<L>(w, lut, slot, s2, b);
 #pragma unroll
         for (int f = 0; f < S::mf; ++f) {
+          // input rows at or past the tile's pair count hold stale values; they only reach
+          // rows of D that are never stored (row i of D depends on row i of A alone)
           const u32x4_t a = *reinterpret_cast<const u32x4_t*>(la + col * C::AST + e0 + 8 * f);
-          acc = mfma_f16(valid ? a : u32x4_t{0u, 0u, 0u, 0u}, b[f], acc);
+          acc = mfma_f16(a, b[f], acc);
         }
       }
     }

@@ -35,6 +35,10 @@ namespace tq {
 constexpr int kQmvThreads = 1024;
 constexpr int kQmvWaves = kQmvThreads / 64;
 constexpr int kMaxRowPartBytes = 32768;
+// Row groups whose loads are issued before the input rotation (the rest of the ring after
+// it). Fewer (2, which also removes the 8 registers the 2-bit gate kernel spills) measured
+// slower on the MoE decode layer: the loads in flight during the rotation matter more.
+constexpr int kQmvPreGroups = 3;
 
 struct QmvParams {
   const uint32_t* codes;
@@ -255,14 +259,21 @@ __global__ __launch_bounds__(kQmvThreads) void k_qmv(QmvParams p) {
   GroupRegs<L, CPL> buf[D];
   // D == 1: the launch gives every workgroup exactly one row group (grp0 < ngroups)
   if constexpr (D == 1) qmv_load_group<L, CPL, G16>(buf[0], p, ln, grp0, cexp, sexp, ngroups_k);
+  // PRE of the D - 1 groups ahead are requested before the rotation, the rest after it
+  constexpr int PRE = D - 1 > kQmvPreGroups ? kQmvPreGroups : D - 1;
 #pragma unroll
-  for (int d = 0; d < D - 1; ++d) {
+  for (int d = 0; d < PRE; ++d) {
     const int g = grp0 + d * stride;
     qmv_load_group<L, CPL, G16>(buf[d], p, ln, g < p.ngroups ? g : grp0, cexp, sexp, ngroups_k);
   }
 
   float out_scale;
   in.rotate(p, lut, xh, xf, red, hs, &out_scale);
+#pragma unroll
+  for (int d = PRE; d < D - 1; ++d) {
+    const int g = grp0 + d * stride;
+    qmv_load_group<L, CPL, G16>(buf[d], p, ln, g < p.ngroups ? g : grp0, cexp, sexp, ngroups_k);
+  }
   const float nan = __builtin_nanf("");
   const int rloc = ln.rset * ln.rpw + ln.sub;
   int grp = grp0, it = 0;
