@@ -100,8 +100,9 @@ template <typename T, int R>
 __device__ __forceinline__ void sylvester_pass(T* buf, int total, int h) {
   constexpr int n = 1 << R;
   const int ngroups = total >> R;
+  const int lh = __builtin_ctz(h);  // h is a power of two
   for (int g = threadIdx.x; g < ngroups; g += kBlock) {
-    const int blk = g / h, off = g - blk * h;
+    const int blk = g >> lh, off = g & (h - 1);
     T* base = buf + blk * (h << R) + off;
     T v[n];
 #pragma unroll
@@ -132,43 +133,6 @@ __device__ __forceinline__ void sylvester_lds(T* buf, int total, int P, int h0 =
     else if (left == 3) { sylvester_pass<T, 3>(buf, total, h); h <<= 3; }
     else if (left == 2) { sylvester_pass<T, 2>(buf, total, h); h <<= 2; }
     else { sylvester_pass<T, 1>(buf, total, h); h <<= 1; }
-  }
-}
-
-// H_m along the strided dimension: row r of `nrows` rows of length M*P, element (a, b) at
-// r*M*P + a*P + b; y[a][b] = sum_a' H_m[a][a'] x[a'][b]. The outputs are produced one at a
-// time from a table of +-1 factors read with uniform (scalar) loads, which keeps register
-// use at about M values per lane; multiplying by +-1 is exact.
-template <typename T, int M>
-__device__ __forceinline__ void hadamard_m_lds(T* buf, int nrows, int P) {
-  const float(*sgn)[M] = HadamardTable<M>::value.sgn;
-  const int cols = nrows * P;
-  for (int col = threadIdx.x; col < cols; col += kBlock) {
-    const int r = col / P, b = col - r * P;
-    T* base = buf + r * M * P + b;
-    T x[M];
-#pragma unroll
-    for (int a = 0; a < M; ++a) x[a] = base[a * P];
-#pragma unroll 1
-    for (int a = 0; a < M; ++a) {
-      T acc = 0;
-#pragma unroll
-      for (int c = 0; c < M; ++c) acc += static_cast<T>(sgn[a][c]) * x[c];
-      base[a * P] = acc;
-    }
-  }
-  __syncthreads();
-}
-
-// Full unnormalized H_K = H_m (x) H_P on `nrows` rows of length m*P held in LDS.
-template <typename T>
-__device__ __forceinline__ void hadamard_lds(T* buf, int nrows, int m, int P) {
-  sylvester_lds<T>(buf, nrows * m * P, P);
-  switch (m) {
-    case 12: hadamard_m_lds<T, 12>(buf, nrows, P); break;
-    case 20: hadamard_m_lds<T, 20>(buf, nrows, P); break;
-    case 28: hadamard_m_lds<T, 28>(buf, nrows, P); break;
-    default: break;
   }
 }
 

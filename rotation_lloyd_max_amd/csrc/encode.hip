@@ -11,6 +11,7 @@
 //   packing. Rotation and RMS are computed in double precision, so the decision sees the
 //   same u, to within a few units of the 53-bit significand, as an fp64 evaluation.
 #include "device_common.hpp"
+#include "fwht_block.hpp"
 #include "internal.hpp"
 
 namespace tq {
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(kBlock) void k_encode(const void* W, int64_t rows, 
       }
     }
     __syncthreads();
-    if constexpr (WDT != 3) hadamard_lds<double>(v, 1, m, P);
+    if constexpr (WDT != 3) hadamard_lds<double, kBlock>(v, 1, m, P);
 
     // group sums of squares: partial sums over runs, then per group
     for (int r = threadIdx.x; r < K / run; r += kBlock) {
@@ -82,8 +83,9 @@ __global__ __launch_bounds__(kBlock) void k_encode(const void* W, int64_t rows, 
     __syncthreads();
 
     // snap: count thresholds below u, in binary32
+    const int lg_group = __builtin_ctz(group);  // groups are powers of two
     for (int i = threadIdx.x; i < K; i += kBlock) {
-      const float u = static_cast<float>(v[i] * rinv[i / group]);
+      const float u = static_cast<float>(v[i] * rinv[i >> lg_group]);
       int q = 0;
 #pragma unroll
       for (int k = 0; k < nthr; ++k) q += (u > cb.t[k]) ? 1 : 0;

@@ -156,6 +156,49 @@ __device__ __forceinline__ void hadamard28_side(const T (&x)[28], Put put) {
   }
 }
 
+// H_m along the strided dimension of rows held in LDS (padding-free layout): row r of
+// `nrows` rows of length M*P, element (a, b) at r*M*P + a*P + b; y[a][b] = sum_a'
+// H_m[a][a'] x[a'][b], one column per thread: the rows of H_12 and H_20 as fixed chains of
+// m - 1 adds and subtracts, H_28 by its Paley II structure (about 120 adds per side
+// instead of 28 * 28 products). P is a power of two.
+template <typename T, int M, int NT>
+__device__ __forceinline__ void hadamard_m_lds(T* buf, int nrows, int P) {
+  const int lp = __builtin_ctz(P);
+  const int cols = nrows * P;
+  for (int col = threadIdx.x; col < cols; col += NT) {
+    const int r = col >> lp, b = col & (P - 1);
+    T* base = buf + r * M * P + b;
+    T x[M];
+#pragma unroll
+    for (int a = 0; a < M; ++a) x[a] = base[a * P];
+    if constexpr (M == 28) {
+      hadamard28_side<T, 0>(x, [&](int R, T y) { base[(2 * R) * P] = y; });
+      hadamard28_side<T, 1>(x, [&](int R, T y) { base[(2 * R + 1) * P] = y; });
+    } else {
+      T y[M];
+      [&]<int... A>(std::integer_sequence<int, A...>) {
+        ((y[A] = hadamard_row<T, M, A>(x, std::make_integer_sequence<int, M>{})), ...);
+      }(std::make_integer_sequence<int, M>{});
+#pragma unroll
+      for (int a = 0; a < M; ++a) base[a * P] = y[a];
+    }
+  }
+  __syncthreads();
+}
+
+// Full unnormalized H_K = H_m (x) H_P on `nrows` rows of length m*P held in LDS
+// (padding-free layout, NT threads).
+template <typename T, int NT>
+__device__ __forceinline__ void hadamard_lds(T* buf, int nrows, int m, int P) {
+  sylvester_lds<T>(buf, nrows * m * P, P);
+  switch (m) {
+    case 12: hadamard_m_lds<T, 12, NT>(buf, nrows, P); break;
+    case 20: hadamard_m_lds<T, 20, NT>(buf, nrows, P); break;
+    case 28: hadamard_m_lds<T, 28, NT>(buf, nrows, P); break;
+    default: break;
+  }
+}
+
 // Outputs of part Q of TPC parts of one column: rows a (or row pairs R) with
 // a % TPC == Q. Q is a template constant, so only this part's rows are computed. For H_28
 // TPC is 1 or 2, and part Q computes side Q.

@@ -5,6 +5,7 @@
 // rotation as the weight rows). One workgroup rotates one row at a time in LDS, in fp32,
 // looping over rows with a grid stride.
 #include "device_common.hpp"
+#include "fwht_block.hpp"
 #include "internal.hpp"
 
 namespace tq {
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(kBlock) void k_fwht(const void* x, int64_t rows, in
       buf[i] = ((sb[i >> 5] >> (i & 31)) & 1u) ? -v : v;
     }
     __syncthreads();
-    hadamard_lds<float>(buf, 1, m, P);
+    hadamard_lds<float, kBlock>(buf, 1, m, P);
     for (int i = threadIdx.x; i < K; i += kBlock) store_any(out, odt, base + i, buf[i] * inv_sqrt_k);
     __syncthreads();
   }
