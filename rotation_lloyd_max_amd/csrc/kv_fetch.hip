@@ -41,23 +41,50 @@ __device__ __forceinline__ void kv_bfly(float (&v)[kKvEl]) {
   }
 }
 
-// One butterfly stage between lanes `lane` and `lane ^ m`: the lower lane keeps the sum, the
-// upper one the difference (partner - own).
-__device__ __forceinline__ void kv_lane_stage(float (&v)[kKvEl], int m) {
-  const bool upper = (threadIdx.x & m) != 0;
+// One butterfly stage between lanes `lane` and `lane ^ M`: the lower lane keeps the sum, the
+// upper one the difference (partner - own). M = 1 and 2 move data with DPP quad
+// permutations (no LDS instruction), larger strides with a lane shuffle.
+template <int M>
+__device__ __forceinline__ float kv_partner(float x) {
+  if constexpr (M == 1 || M == 2) {
+    constexpr int sel = M == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), sel, 0xf, 0xf, false));
+  } else {
+    return __shfl_xor(x, M);
+  }
+}
+
+template <int M>
+__device__ __forceinline__ void kv_lane_stage(float (&v)[kKvEl]) {
+  const bool upper = (threadIdx.x & M) != 0;
 #pragma unroll
   for (int j = 0; j < kKvEl; ++j) {
-    const float o = __shfl_xor(v[j], m);
+    const float o = kv_partner<M>(v[j]);
     v[j] = upper ? o - v[j] : v[j] + o;
   }
 }
 
+// A lane's packed codes and scales of one batch.
+template <int NW>
+struct KvIn {
+  uint32_t w[NW];
+  uint16_t s0, s1;
+};
+
 // G16: groups of 16 (two scales per lane); otherwise one scale per lane.
+//
+// Each wave works through batches of 2048 / d rows, the next batch's codes and scales
+// loaded while the current one is decoded. A full batch's outputs are consecutive in memory
+// (the wave's rows are consecutive, a lane's 32 elements contiguous within its row), so
+// they go through a per-wave LDS buffer and leave in store instructions that each write
+// 1 KB of consecutive bytes; a partial last batch stores lane by lane.
 template <int LEVELS, bool G16, int ODT>
 __global__ __launch_bounds__(kKvThreads) void k_kv_fetch(KvParams p) {
   constexpr int B = LEVELS == 4 ? 2 : LEVELS == 8 ? 3 : LEVELS == 16 ? 4 : 8;
-  constexpr int NW = kKvEl * B / 32;  // code words per lane
+  constexpr int NW = kKvEl * B / 32;          // code words per lane
+  constexpr int SU = kKvEl * (ODT == 0 ? 4 : 2) / 16;  // 16-byte output units per lane
   __shared__ float lut[LEVELS];
+  __shared__ u32x4_t stage[kKvThreads / 64][64 * SU];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tr = 1 << p.lg_tr;    // lanes per row
   const int rpw = 64 >> p.lg_tr;  // rows per wave batch
@@ -67,54 +94,103 @@ __global__ __launch_bounds__(kKvThreads) void k_kv_fetch(KvParams p) {
   __syncthreads();
   const uint32_t sgn = p.signs[t];  // sign bits of elements col0 .. col0 + 31
   const int gi0 = col0 >> p.lg_group;
+  u32x4_t* st = stage[wave];
 
   const int64_t nb = (p.rows + rpw - 1) / rpw;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * (kKvThreads / 64);
-  for (int64_t b = static_cast<int64_t>(blockIdx.x) * (kKvThreads / 64) + wave; b < nb; b += stride) {
-    const int64_t row = b * rpw + rl;
-    if (row >= p.rows) continue;  // a row's lanes pass or fail this test together
-    uint32_t w[NW];
+  int64_t b = static_cast<int64_t>(blockIdx.x) * (kKvThreads / 64) + wave;
+  auto fetch = [&](int64_t bb, KvIn<NW>& in) {
+    int64_t row = bb * rpw + rl;
+    row = row < p.rows ? row : p.rows - 1;  // lanes past the rows load a valid row
     const uint32_t* src = p.codes + row * p.wpr + t * NW;
 #pragma unroll
-    for (int k = 0; k < NW; ++k) w[k] = src[k];
+    for (int k = 0; k < NW; ++k) in.w[k] = src[k];
     const uint16_t* srow = p.scales + row * p.ngk + gi0;
-    const float s0 = half_bits_to_float(srow[0]);
-    const float s1 = G16 ? half_bits_to_float(srow[1]) : s0;
+    in.s0 = srow[0];
+    in.s1 = G16 ? srow[1] : in.s0;
+  };
+  KvIn<NW> nxt;
+  if (b < nb) fetch(b, nxt);
+  for (; b < nb; b += stride) {
+    const KvIn<NW> in = nxt;
+    if (b + stride < nb) fetch(b + stride, nxt);
+    const int64_t row = b * rpw + rl;
+    const float s0 = half_bits_to_float(in.s0);
+    const float s1 = G16 ? half_bits_to_float(in.s1) : s0;
     float v[kKvEl];
 #pragma unroll
     for (int j = 0; j < kKvEl; ++j) {
       const int bp = B * j;
-      uint32_t idx = w[bp >> 5] >> (bp & 31);
-      if ((bp & 31) + B > 32) idx |= w[(bp >> 5) + 1] << (32 - (bp & 31));
+      uint32_t idx = in.w[bp >> 5] >> (bp & 31);
+      if ((bp & 31) + B > 32) idx |= in.w[(bp >> 5) + 1] << (32 - (bp & 31));
       idx &= (1u << B) - 1u;
       v[j] = lut[idx] * (G16 && j >= 16 ? s1 : s0);
     }
     // H_d: the five low index bits in registers, the rest across the row's lanes
     kv_bfly<0>(v); kv_bfly<1>(v); kv_bfly<2>(v); kv_bfly<3>(v); kv_bfly<4>(v);
-    for (int m = 1; m < tr; m <<= 1) kv_lane_stage(v, m);
+    if (tr > 1) kv_lane_stage<1>(v);
+    if (tr > 2) kv_lane_stage<2>(v);
+    if (tr > 4) kv_lane_stage<4>(v);
+    if (tr > 8) kv_lane_stage<8>(v);
+    if (tr > 16) kv_lane_stage<16>(v);
+    if (tr > 32) kv_lane_stage<32>(v);
     // R^T = diag(s) H / sqrt(d)
 #pragma unroll
     for (int j = 0; j < kKvEl; ++j) {
       const float x = v[j] * p.inv_sqrt_k;
       v[j] = ((sgn >> j) & 1u) ? -x : x;
     }
+    u32x4_t u[SU];
     if constexpr (ODT == 0) {
-      float4* dst = reinterpret_cast<float4*>(static_cast<float*>(p.out) + row * p.K + col0);
 #pragma unroll
-      for (int k = 0; k < kKvEl / 4; ++k)
-        dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+      for (int k = 0; k < SU; ++k)
+        u[k] = u32x4_t{__float_as_uint(v[4 * k]), __float_as_uint(v[4 * k + 1]),
+                       __float_as_uint(v[4 * k + 2]), __float_as_uint(v[4 * k + 3])};
     } else {
       uint32_t hw[kKvEl / 2];
 #pragma unroll
       for (int k = 0; k < kKvEl / 2; ++k) {
-        const uint16_t a = ODT == 1 ? float_to_bf16_rne(v[2 * k]) : float_to_half_rne(v[2 * k]);
-        const uint16_t c = ODT == 1 ? float_to_bf16_rne(v[2 * k + 1]) : float_to_half_rne(v[2 * k + 1]);
+        // round to nearest even (bf16: the hardware conversion, v_cvt_pk_bf16_f32)
+        uint16_t a, c;
+        if constexpr (ODT == 1) {
+          a = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[2 * k]));
+          c = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[2 * k + 1]));
+        } else {
+          a = float_to_half_rne(v[2 * k]);
+          c = float_to_half_rne(v[2 * k + 1]);
+        }
         hw[k] = static_cast<uint32_t>(a) | (static_cast<uint32_t>(c) << 16);
       }
-      uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + row * p.K + col0);
 #pragma unroll
-      for (int k = 0; k < kKvEl / 8; ++k)
-        dst[k] = make_uint4(hw[4 * k], hw[4 * k + 1], hw[4 * k + 2], hw[4 * k + 3]);
+      for (int k = 0; k < SU; ++k) u[k] = u32x4_t{hw[4 * k], hw[4 * k + 1], hw[4 * k + 2], hw[4 * k + 3]};
+    }
+    const int esz = ODT == 0 ? 4 : 2;
+    if ((b + 1) * rpw <= p.rows) {  // uniform: a full batch, one contiguous block
+      // unit q (16 bytes of the block) of lane q / SU; slot q ^ ((q >> 4) & 3) spreads the
+      // lanes' writes over the banks
+#pragma unroll
+      for (int k = 0; k < SU; ++k) {
+        const int q = SU * lane + k;
+        st[q ^ ((q >> 4) & 3)] = u[k];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      char* dst = static_cast<char*>(p.out) + (b * rpw) * static_cast<int64_t>(p.K) * esz;
+#pragma unroll
+      for (int k = 0; k < SU; ++k) {
+        const int q = 64 * k + lane;
+        reinterpret_cast<u32x4_t*>(dst)[q] = st[q ^ ((q >> 4) & 3)];
+      }
+      // the next batch's LDS writes come after these reads
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else if (row < p.rows) {
+      u32x4_t* dst = reinterpret_cast<u32x4_t*>(static_cast<char*>(p.out) +
+                                                (row * p.K + col0) * static_cast<int64_t>(esz));
+#pragma unroll
+      for (int k = 0; k < SU; ++k) dst[k] = u[k];
     }
   }
 }
