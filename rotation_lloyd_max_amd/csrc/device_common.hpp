@@ -141,11 +141,9 @@ __device__ __forceinline__ void sylvester_lds(T* buf, int total, int P, int h0 =
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
+// round to nearest even; the hardware conversion (v_cvt_pk_bf16_f32 on gfx950), NaN stays NaN
 __device__ __forceinline__ uint16_t float_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u) return static_cast<uint16_t>((u >> 16) | ((u & 0xffff) ? 0x40 : 0));
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, h));
