@@ -224,7 +224,9 @@ __global__ __launch_bounds__(kQmvThreads) void k_qmv(QmvParams p) {
   uint16_t* hs = reinterpret_cast<uint16_t*>(red + kQmvWaves);  // 16 fp16 centroids
   float* rowpart = red + kQmvWaves + 8;                    // slice sums of the rows
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index is uniform: held in a scalar register, so are the per-wave constants
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
   const uint32_t lslot = lut_slot<L>(lane);  // this lane's copy inside every table entry
   const int KS = 1 << p.ks_log;
   Lane ln;
