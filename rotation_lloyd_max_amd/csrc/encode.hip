@@ -152,7 +152,7 @@ hipError_t launch_encode(const void* W, int wdt, int64_t rows, int K, int m, int
                          hipStream_t s) {
   if (rows == 0) return hipSuccess;
   // power-of-two rows up to 4096 long, read with 16-byte loads: the register kernel
-  if (encode_p2_supported(K, m) && (reinterpret_cast<uintptr_t>(W) & 15) == 0)
+  if (encode_p2_supported(K, m, levels) && (reinterpret_cast<uintptr_t>(W) & 15) == 0)
     return launch_encode_p2(W, wdt, rows, K, levels, group, seed, codes, scales, s);
   switch (wdt) {
     case 0: return launch_encode_l<0>(W, rows, K, m, P, levels, group, seed, codes, scales, s);

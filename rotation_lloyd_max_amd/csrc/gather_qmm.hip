@@ -21,6 +21,7 @@
 // the K order inside an instruction is free: lane group g = l / 32 takes a contiguous span
 // of SPAN elements of the step (Span<L>), fed to MF consecutive instructions 8 at a time.
 #include <type_traits>
+#include <utility>
 
 #include "internal.hpp"
 #include "mfma_decode.hpp"
@@ -185,12 +186,21 @@ constexpr int span_scales() {
   return L == 3 ? Span<L>::mf : (G16 ? 2 : 1);
 }
 
-// Registers of one pipeline stage: the codes and scales of both column tiles of a lane
-// for one K step, and the thread's share of the step's input tile.
+// Pipeline registers: the codes and scales of both column tiles of a lane for one K step
+// (a ring of qmm_code_ring steps), and the thread's share of one step's input tile (a ring of
+// two). Three steps of codes in flight for the bit formats whose scales are staged in LDS;
+// the other kernels have no registers for the third.
+template <int L, bool SL>
+constexpr int qmm_code_ring() {
+  return SL && L != 3 ? 3 : 2;
+}
 template <int L, bool G16>
-struct QmmStage {
+struct QmmCodes {
   uint32_t w[2][Span<L>::words];
   uint16_t s[2][span_scales<L, G16>()];
+};
+template <int L>
+struct QmmA {
   u32x4_t a[QmmStep<L>::AU];
 };
 
@@ -289,14 +299,12 @@ __device__ __forceinline__ void qmm_tile(const QmmParams& p, int e, int m0, int 
     aoff[j] = r * Q::AST + 8 * u;
     ak[j] = 8 * u;
   }
-  // an even number of steps, so that the loop below runs both halves every time; steps
-  // past K read zero inputs
-  const int nsteps = ((p.K + 2 * Q::BK - 1) / (2 * Q::BK)) * 2;
   const int last = (p.K - 1) / Q::BK;  // last step holding elements
+  const int nsteps = last + 1;
 
   // Loads are issued unconditionally (indices clamped) so that every loop iteration has the
   // same memory operations and the compiler's count of outstanding loads stays exact.
-  auto load_codes = [&](QmmStage<L, G16>& st, int step) {
+  auto load_codes = [&](QmmCodes<L, G16>& st, int step) {
     step = step < last ? step : last;
     const int e0 = step * Q::BK + g * S::elems;
     // With K an odd multiple of 32, the second lane group's span of the last step starts at
@@ -331,7 +339,7 @@ __device__ __forceinline__ void qmm_tile(const QmmParams& p, int e, int m0, int 
       }
     }
   };
-  auto fetch_a = [&](QmmStage<L, G16>& st, int step) {
+  auto fetch_a = [&](QmmA<L>& st, int step) {
     const int k0 = step * Q::BK;
 #pragma unroll
     for (int j = 0; j < Q::AU; ++j) {
@@ -339,7 +347,7 @@ __device__ __forceinline__ void qmm_tile(const QmmParams& p, int e, int m0, int 
       st.a[j] = *reinterpret_cast<const u32x4_t*>(asrc[j] + kc);
     }
   };
-  auto stash_a = [&](const QmmStage<L, G16>& st, int buf, int step) {
+  auto stash_a = [&](const QmmA<L>& st, int buf, int step) {
     const int k0 = step * Q::BK;
 #pragma unroll
     for (int j = 0; j < Q::AU; ++j) {
@@ -356,15 +364,19 @@ __device__ __forceinline__ void qmm_tile(const QmmParams& p, int e, int m0, int 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mt][j][r] = 0.f;
 
-  // Two stages in flight: step t's codes and inputs live in stage t % 2 and are loaded two
-  // steps ahead; step t's inputs are copied to LDS buffer t % 2 at the end of step t - 1.
-  QmmStage<L, G16> st[2];
-  fetch_a(st[0], 0);
-  load_codes(st[0], 0);
-  fetch_a(st[1], 1);
-  load_codes(st[1], 1);
-  stash_a(st[0], 0, 0);
-  fetch_a(st[0], 2);
+  // Step t's codes live in ring slot t % CR, loaded CR steps ahead (the table indices of
+  // step t + 1 are formed during step t, so a code load has CR - 1 steps to arrive); its
+  // inputs live in slot t % 2, loaded three steps ahead and copied to LDS buffer t % 2 at the
+  // end of step t - 1. Loads past the last step are clamped to it.
+  constexpr int CR = qmm_code_ring<L, SL>();
+  QmmCodes<L, G16> cr[CR];
+  QmmA<L> ar[2];
+  fetch_a(ar[0], 0);
+#pragma unroll
+  for (int c = 0; c < CR; ++c) load_codes(cr[c], c);
+  fetch_a(ar[1], 1);
+  stash_a(ar[0], 0, 0);
+  fetch_a(ar[0], 2);
   __syncthreads();
 
   // Table lookups run LA fragments ahead of the multiplies that use them, across step
@@ -376,14 +388,15 @@ __device__ __forceinline__ void qmm_tile(const QmmParams& p, int e, int m0, int 
   u32x4_t raw[MF][2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    span_index<L>(st[0].w[j], xc[j]);
+    span_index<L>(cr[0].w[j], xc[j]);
 #pragma unroll
     for (int q = 0; q < LA; ++q) raw[q][j] = span_lookup<L>(xc[j], q, lut, slot);
   }
 
-  auto body = [&](auto parity, int step) {
-    constexpr int P = decltype(parity)::value;
-    QmmStage<L, G16>& cur = st[P];
+  auto body = [&](auto slot_of_step, int step) {
+    constexpr int P = decltype(slot_of_step)::value & 1;  // input slot and LDS buffer
+    constexpr int C = decltype(slot_of_step)::value >> 1;  // code slot
+    QmmCodes<L, G16>& cur = cr[C];
     const int e0 = (step < last ? step : last) * Q::BK + g * S::elems;
     uint32_t s2[2][MF];
 #pragma unroll
@@ -420,7 +433,7 @@ __device__ __forceinline__ void qmm_tile(const QmmParams& p, int e, int m0, int 
         if (q == MF) {
           // the next step's codes (loaded two steps ago) become table indices
 #pragma unroll
-          for (int j = 0; j < 2; ++j) span_index<L>(st[P ^ 1].w[j], xn[j]);
+          for (int j = 0; j < 2; ++j) span_index<L>(cr[(C + 1) % CR].w[j], xn[j]);
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) raw[q - MF][j] = span_lookup<L>(xn[j], q - MF, lut, slot);
@@ -433,12 +446,12 @@ __device__ __forceinline__ void qmm_tile(const QmmParams& p, int e, int m0, int 
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[mt][j] = mfma32_f16(a[mt], b[j], acc[mt][j]);
     }
-    // this step's indices are consumed: its code registers take step + 2
-    load_codes(cur, step + 2);
+    // this step's indices are consumed: its code registers take step + CR
+    load_codes(cur, step + CR);
 #pragma unroll
     for (int j = 0; j < 2; ++j) xc[j] = xn[j];
-    stash_a(st[P ^ 1], P ^ 1, step + 1);
-    fetch_a(st[P ^ 1], step + 3);
+    stash_a(ar[P ^ 1], P ^ 1, step + 1);
+    fetch_a(ar[P ^ 1], step + 3);
     __syncthreads();
   };
   // Before a step whose groups run past the window, the window restarts at the step's first
@@ -456,11 +469,18 @@ __device__ __forceinline__ void qmm_tile(const QmmParams& p, int e, int m0, int 
       }
     }
   };
-  for (int step = 0; step < nsteps; step += 2) {
-    advance_window(step);
-    body(std::integral_constant<int, 0>{}, step);
-    advance_window(step + 1);
-    body(std::integral_constant<int, 1>{}, step + 1);
+  // The loop body runs PER steps, the period of the two rings (slot value (t % CR) * 2 + t % 2),
+  // and stops after step nsteps - 1.
+  constexpr int PER = CR == 3 ? 6 : 2;
+  auto run = [&]<int... U>(std::integer_sequence<int, U...>, int step) {
+    bool more = true;
+    ((more = more && (advance_window(step + U),
+                      body(std::integral_constant<int, (U % CR) * 2 + U % 2>{}, step + U),
+                      step + U + 1 < nsteps)),
+     ...);
+    return more;
+  };
+  for (int step = 0; run(std::make_integer_sequence<int, PER>{}, step); step += PER) {
   }
 
   // D[8 (r / 4) + 4 g + r % 4][c32] of sub-tile (mt, j), times the row's input scale
