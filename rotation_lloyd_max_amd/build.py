@@ -12,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtq.so")
 
-SOURCES = ["tq_api.cpp", "rotate.hip", "encode.hip", "encode_p2.hip", "qmv.hip", "qmv_16.hip", "qmv_8.hip",
+SOURCES = ["tq_api.cpp", "rotate.hip", "encode.hip", "encode_p2.hip", "encode_m.hip", "qmv.hip", "qmv_16.hip", "qmv_8.hip",
            "qmv_4.hip", "qmv_3.hip", "rot16.hip", "multi_gather.hip", "gather_qmm.hip",
            "dequant.hip", "slot_ids.hip", "kv_fetch.hip", "dense.hip"]
 

@@ -1,7 +1,9 @@
 // Encode kernel: rotate -> group RMS -> fp16 scale -> snap -> pack, one row at a time per
-// workgroup (grid-stride over rows). Rows of 12, 20 or 28 times a power of two, rows of
-// 8192, and sources not 16-byte aligned take this kernel; power-of-two rows up to 4096
-// take k_encode_p2 (encode_p2.hip).
+// workgroup (grid-stride over rows). Power-of-two rows up to 4096 take k_encode_p2
+// (encode_p2.hip) and rows of 12, 20 or 28 times 32 .. 256 take k_encode_m (encode_m.hip);
+// this kernel takes the other lengths (rows of 8192, factors with fewer than 32 or more
+// than 256 columns), power-of-two sources not 16-byte aligned, trit rows of 4096, and
+// rows already rotated by a dense rotation.
 //
 // Steps (turboquant-mlx "How it works", "Quantizing a weight, with no data"; "The ternary
 // tier (1.58 bits)"):
@@ -154,6 +156,9 @@ hipError_t launch_encode(const void* W, int wdt, int64_t rows, int K, int m, int
   // power-of-two rows up to 4096 long, read with 16-byte loads: the register kernel
   if (encode_p2_supported(K, m, levels) && (reinterpret_cast<uintptr_t>(W) & 15) == 0)
     return launch_encode_p2(W, wdt, rows, K, levels, group, seed, codes, scales, s);
+  // rows of 12, 20 or 28 times 32 .. 256: the register kernel with the m-point factor
+  if (encode_m_supported(K, m))
+    return launch_encode_m(W, wdt, rows, K, m, levels, group, seed, codes, scales, s);
   switch (wdt) {
     case 0: return launch_encode_l<0>(W, rows, K, m, P, levels, group, seed, codes, scales, s);
     case 1: return launch_encode_l<1>(W, rows, K, m, P, levels, group, seed, codes, scales, s);

@@ -28,6 +28,7 @@
 // The exchanges go through the wave's own 16 KB buffer, addressed so that none has bank
 // conflicts (pair_slot), and need no workgroup barrier.
 #include "device_common.hpp"
+#include "encode_lane.hpp"
 #include "internal.hpp"
 
 namespace tq {
@@ -65,35 +66,6 @@ __device__ __forceinline__ constexpr int slot_mix(int P) {
   const int y = P >> 3;
   return ((y ^ (y >> 2)) & 1) | ((((y >> 1) ^ (y >> 3)) & 1) << 1) |
          ((((y >> 1) ^ (y >> 4)) & 1) << 2);
-}
-
-// Orders a wave's LDS writes before its later LDS reads (other lanes' data): the LDS
-// executes one wave's instructions in order, so only the compiler has to be held back.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-template <int S>
-__device__ __forceinline__ void bfly(double (&v)[32]) {
-#pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    if (j & (1 << S)) continue;
-    const double a = v[j], b = v[j | (1 << S)];
-    v[j] = a + b;
-    v[j | (1 << S)] = a - b;
-  }
-}
-
-// x of the lane M apart (M = 1, 2: DPP quad permutations; M = 8: row rotation by 8, which
-// is lane ^ 8 inside each row of 16 lanes), as two 32-bit moves.
-template <int M>
-__device__ __forceinline__ double lane_xor(double x) {
-  constexpr int ctrl = M == 1 ? 0xB1 : M == 2 ? 0x4E : 0x128;
-  const int lo = __builtin_amdgcn_mov_dpp(__double2loint(x), ctrl, 0xf, 0xf, false);
-  const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(x), ctrl, 0xf, 0xf, false);
-  return __hiloint2double(hi, lo);
 }
 
 // WDT: 0 fp32, 1 bf16, 2 fp16 source rows; NH source halves (2 for a row of 4096).
@@ -222,12 +194,6 @@ __global__ __launch_bounds__(kP2Threads, 2) void k_encode_p2(EncP2Params p) {
     for (int k = 0; k < 8; ++k) cbase[k] = 16 * (pc + (F ^ k));
   }
 
-  constexpr int G = 1 << LG_G;
-  constexpr int GL = G < 32 ? G : 32;  // elements of one group inside a lane
-  constexpr int NG = 32 / GL;          // groups (or parts of a group) per lane
-  constexpr int NPOS = LEVELS == 3 ? 1 : LEVELS == 256 ? 8 : LEVELS / 2 - 1;
-  constexpr int CPOS = LEVELS == 3 ? 1 : LEVELS / 2;      // idx of the smallest u > 0
-  constexpr int CNEG = LEVELS == 3 ? 1 : LEVELS / 2 - 1;  // idx of u = 0
   if (b >= nbatch) return;
 
   // C lanes: virtual row and first element of the lane's 32
@@ -314,61 +280,9 @@ __global__ __launch_bounds__(kP2Threads, 2) void k_encode_p2(EncP2Params p) {
     const int off = SPLIT ? 2048 * static_cast<int>(b & 1) + ci0 : ci0;
     const bool live = row < p.rows;
 
-    // group RMS and fp16 scales
-    double rinv[NG];
-#pragma unroll
-    for (int k = 0; k < NG; ++k) {
-      // eight independent partial sums (a single chain of GL dependent fp64 adds would
-      // leave the wave waiting on each one)
-      constexpr int NA = GL < 8 ? GL : 8;
-      double part[NA];
-#pragma unroll
-      for (int a = 0; a < NA; ++a) part[a] = v[GL * k + a] * v[GL * k + a];
-#pragma unroll
-      for (int j = NA; j < GL; ++j) part[j % NA] = __builtin_fma(v[GL * k + j], v[GL * k + j], part[j % NA]);
-#pragma unroll
-      for (int w = NA / 2; w >= 1; w /= 2)
-#pragma unroll
-        for (int a = 0; a < w; ++a) part[a] += part[a + w];
-      double sq = part[0];
-      if constexpr (G >= 64) sq += lane_xor<1>(sq);
-      if constexpr (G == 128) sq += lane_xor<2>(sq);
-      const double rr = __builtin_sqrt(sq / G);
-      rinv[k] = rr > 0.0 ? 1.0 / rr : 0.0;
-      const uint16_t sc = double_to_half_rne_sat(rr * p.inv_sqrt_k);
-      if (live && (G <= 32 || (lane & (G / 32 - 1)) == 0))
-        p.scales[row * (K >> LG_G) + ((off + GL * k) >> LG_G)] = sc;
-    }
-
-    // snap: idx = #{k : u > t_k} in binary32, from the positive thresholds alone (the
-    // codebook is symmetric): u > 0 takes CPOS + #{t > 0 : u > t}; u <= 0 takes
-    // CNEG - #{t > 0 : |u| >= t}; key = bits(|u|) + (u <= 0) turns both into one count.
-    // The indices go straight into their packed words.
-    constexpr int BITS = LEVELS == 4 ? 2 : LEVELS == 8 ? 3 : LEVELS == 16 ? 4 : 8;
-    constexpr int NW = BITS;  // words of 32 codes (bytes for trits)
+    constexpr int NW = lane_code_bits<LEVELS>();  // words of the lane's 32 codes
     uint32_t w[NW];
-#pragma unroll
-    for (int k = 0; k < NW; ++k) w[k] = 0;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const float u = static_cast<float>(v[j] * rinv[j / GL]);
-      const uint32_t ub = __float_as_uint(u);
-      const bool pos = static_cast<int32_t>(ub) > 0;  // u > 0 (never NaN here)
-      const uint32_t key = (ub & 0x7fffffffu) + (pos ? 0u : 1u);
-      uint32_t cnt = 0;
-      if constexpr (LEVELS == 256) {
-        // 127 positive thresholds: a branch-free binary search for #{q : key > tk[q]}
-#pragma unroll
-        for (int st = 64; st >= 1; st >>= 1) cnt += key > tk[cnt + st - 1] ? st : 0u;
-      } else {
-#pragma unroll
-        for (int k = 0; k < NPOS; ++k) cnt += key > p.tbits[k] ? 1u : 0u;
-      }
-      const uint32_t idx = pos ? CPOS + cnt : CNEG - cnt;
-      const int bp = BITS * j;
-      w[bp >> 5] |= idx << (bp & 31);
-      if ((bp & 31) + BITS > 32) w[(bp >> 5) + 1] |= idx >> (32 - (bp & 31));
-    }
+    lane_encode<LEVELS, LG_G>(v, p.tbits, tk, p.inv_sqrt_k, lane, row, off, live, K, p.scales, w);
 
     if constexpr (LEVELS != 3) {
       if (live) {
@@ -434,6 +348,19 @@ hipError_t launch_p2_w(const EncP2Params& p, int levels, int group, int grid, hi
 
 }  // namespace
 
+bool positive_threshold_bits(int levels, uint32_t* dst) {
+  // the negative thresholds of a symmetric codebook are the negations of the positive ones
+  const float* t = levels == 256 ? codebook256()->t : codebook_for(levels)->t;
+  const int npos = levels == 3 ? 1 : levels / 2 - 1;
+  for (int q = 0; q < npos; ++q) {
+    const float tq = t[levels - 1 - npos + q];
+    const float tn = t[npos - 1 - q];
+    if (!(tq > 0.f) || tn != -tq) return false;
+    dst[q] = __builtin_bit_cast(uint32_t, tq);
+  }
+  return levels == 3 || t[levels / 2 - 1] == 0.f;
+}
+
 // Trit words of a row of 4096 would straddle the two halves' batches: that case takes
 // k_encode.
 bool encode_p2_supported(int K, int m, int levels) {
@@ -450,17 +377,7 @@ hipError_t launch_encode_p2(const void* W, int wdt, int64_t rows, int K, int lev
   p.inv_sqrt_k = 1.0 / __builtin_sqrt(static_cast<double>(K));
   p.wpr = levels == 3 ? (K + 19) / 20
                       : (K * (levels == 4 ? 2 : levels == 8 ? 3 : levels == 16 ? 4 : 8)) / 32;
-  // positive thresholds of the symmetric codebook (the negative ones are their negations)
-  const float* t = levels == 256 ? codebook256()->t : codebook_for(levels)->t;
-  const int npos = levels == 3 ? 1 : levels / 2 - 1;
-  uint32_t* dst = levels == 256 ? p.tbig : p.tbits;
-  for (int q = 0; q < npos; ++q) {
-    const float tq = t[levels - 1 - npos + q];
-    const float tn = t[npos - 1 - q];
-    if (!(tq > 0.f) || tn != -tq) return hipErrorInvalidValue;  // not symmetric: never
-    dst[q] = __builtin_bit_cast(uint32_t, tq);
-  }
-  if (levels != 3 && t[levels / 2 - 1] != 0.f) return hipErrorInvalidValue;
+  if (!positive_threshold_bits(levels, levels == 256 ? p.tbig : p.tbits)) return hipErrorInvalidValue;
   const bool split = K > kP2Batch;
   const int64_t nbatch = split ? 2 * rows : (rows + kP2Batch / K - 1) / (kP2Batch / K);
   const int64_t want = (nbatch + kP2Waves - 1) / kP2Waves;

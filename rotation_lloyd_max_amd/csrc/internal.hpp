@@ -56,6 +56,11 @@ hipError_t launch_dense_rot(const void* x, int xdt, int64_t rows, int K, const f
                             int odt, hipStream_t s);
 
 // The register-resident encode for K = 2^p, 64 <= K <= 4096 (W 16-byte aligned).
+// rows of m * 2^k (m = 12, 20, 28; 32 <= 2^k <= 256) with the rotation in registers
+bool encode_m_supported(int K, int m);
+hipError_t launch_encode_m(const void* W, int wdt, int64_t rows, int K, int m, int levels,
+                           int group, uint64_t seed, uint32_t* codes, uint16_t* scales,
+                           hipStream_t s);
 bool encode_p2_supported(int K, int m, int levels);
 hipError_t launch_encode_p2(const void* W, int wdt, int64_t rows, int K, int levels, int group,
                             uint64_t seed, uint32_t* codes, uint16_t* scales, hipStream_t s);

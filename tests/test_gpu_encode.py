@@ -112,6 +112,31 @@ def test_encode_power_of_two_rows(K, dtype):
     check_scales(torch_to_np(qw.scales).reshape(70, -1), ref)
 
 
+@pytest.mark.parametrize("m", [12, 20, 28])
+@pytest.mark.parametrize("P", [32, 64, 128, 256])
+def test_encode_m_layouts(m, P):
+    # every layout of the register kernel for rows of m * P (P = 32: no middle exchange;
+    # 64 .. 256: one, with 1 .. 3 stages), every input dtype and bit or trit format across the
+    # cases (256 levels are for power-of-two rows only),
+    # edge rows among ordinary ones, and a row count that leaves a partial batch
+    K = m * P
+    levels = [3, 4, 8, 16][(m + P // 32) % 4]
+    group = [16, 32, 64, 128][(m // 4 + P // 64) % 4]
+    dtype = DTYPES[(m + P) % 3]
+    rows = 16384 // K * 2 + 3
+    g = wl.rng(911, m, P)
+    W = wl.student_rows(g, rows, K)
+    W[1] = 0.0
+    W[2, :] = 1.0
+    W[4] *= 1e2 if dtype == torch.float16 else 1e5
+    Wd = to_dev(W, dtype)
+    qw = tq.encode(Wd, levels, group, seed=23)
+    torch.cuda.synchronize()
+    ref = oenc.encode(as_f64(Wd), levels, group, 23)
+    check_codes(torch_to_np(qw.codes).reshape(rows, -1), ref, levels, K, f"m{m} P{P} L{levels} g{group}")
+    check_scales(torch_to_np(qw.scales).reshape(rows, -1), ref)
+
+
 def test_encode_edge_rows():
     # zero rows, a row with one zero group, huge and tiny magnitudes (fp16 scale saturation
     # and subnormal scales), and a constant row
