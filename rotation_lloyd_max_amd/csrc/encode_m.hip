@@ -8,11 +8,12 @@
 // r = 0), idx = #{k : u > t_k} decided in binary32, then bit or trit packing. Rotation and
 // RMS in double precision, as in k_encode and k_encode_p2.
 //
-// Work layout. One 8-wave workgroup per CU takes batches of R = floor(16384 / K) rows,
-// transformed in 128 KB of LDS (fp64), in three phases separated by barriers:
+// Work layout. A 4-wave workgroup takes batches of R = floor(8192 / K) rows, transformed in
+// 64 KB of LDS (fp64), in three phases separated by barriers; two workgroups share a CU,
+// so one computes while the other waits at a barrier:
 //   A: lane (row, b) loads column b of its row (m elements, P apart), applies the signs
 //      and the m-point factor in registers (fast forms of fwht_block.hpp) and writes the m
-//      outputs; 512 / P rows per pass;
+//      outputs; 256 / P rows per pass;
 //   B (P >= 64): lane (sub-row, l) holds 32 elements of one length-P sub-row whose index
 //      bits 5..k-1 are in registers (with the 10 - k filler bits 1..10-k; bit 0 and the
 //      rest come from l): the stages of bits 5..k-1;
@@ -33,9 +34,9 @@
 namespace tq {
 namespace {
 
-constexpr int kMWaves = 8;
+constexpr int kMWaves = 4;
 constexpr int kMThreads = 64 * kMWaves;
-constexpr int kMBatch = 16384;  // elements of a workgroup's batch of rows
+constexpr int kMBatch = 8192;  // elements of a workgroup's batch of rows
 constexpr int kMMaxK = 28 * 256;
 
 struct EncMParams {
@@ -48,7 +49,7 @@ struct EncMParams {
   uint32_t tbits[8];   // positive decision thresholds (binary32 bits), ascending
   uint32_t tbig[128];  // the same for the 256-level codebook (127 used)
   int K, lg_p, R, wpr, wdt;
-  uint32_t inv_k;  // ceil(2^32 / K): t / K = mulhi(t, inv_k) for t < 2^18
+  uint32_t inv_k;  // ceil(2^32 / K): t / K = mulhi(t, inv_k) for t < 2^13
 };
 
 __device__ __forceinline__ constexpr int mslot_mix(int P2) {
@@ -106,8 +107,20 @@ __device__ __forceinline__ void m_phase_b(char* buf, int tid, int nsub) {
   }
 }
 
+// Passes of phase A (256 / P rows each, floor(8192 / K) rows per batch): at most 3 for
+// m = 12 and 2 otherwise. The loads of the first NP passes of a batch are requested one
+// batch ahead (all of them for m = 12; the registers of more m = 20 or 28 columns would
+// spill), later passes' loads at their start.
+template <int M>
+constexpr int prefetch_passes() {
+  return M == 12 ? 3 : 1;
+}
+
 template <int M, int LEVELS, int LG_G>
 __global__ __launch_bounds__(kMThreads, 2) void k_encode_m(EncMParams p) {
+  constexpr int NP = prefetch_passes<M>();
+  constexpr int MAXP = M == 12 ? 3 : 2;
+  constexpr bool UNROLL = M == 12;  // passes unrolled (prefetched registers of every pass)
   extern __shared__ double mbuf[];  // R K fp64 elements of the batch (swizzled)
   __shared__ uint32_t sw[kMMaxK / 32];
   __shared__ uint32_t tk[LEVELS == 256 ? 128 : 1];
@@ -123,21 +136,29 @@ __global__ __launch_bounds__(kMThreads, 2) void k_encode_m(EncMParams p) {
   int64_t bt = blockIdx.x;
   const size_t esz = wdt == 0 ? 4 : 2;
 
-  // column ab of row ar of pass ps of batch b (clamped to the last row)
+  // column ab of row ar of pass ps of batch b (clamped to the last row), addressed from
+  // the batch's first row (uniform) by 32-bit offsets
   auto load_col = [&](uint32_t (&raw)[M], int64_t b, int ps) {
-    int64_t row = b * R + ps * rpp + ar;
+    const int64_t r0 = b * R;
+    int64_t row = r0 + ps * rpp + ar;
     row = row < p.rows ? row : p.rows - 1;
-    const char* src = static_cast<const char*>(p.W) + (row * K + ab) * static_cast<int64_t>(esz);
+    const char* src = static_cast<const char*>(p.W) + r0 * K * static_cast<int64_t>(esz);
+    const uint32_t lo = static_cast<uint32_t>((row - r0) * K + ab);
     if (wdt == 0) {
 #pragma unroll
-      for (int a = 0; a < M; ++a) raw[a] = ld_at<uint32_t>(src, static_cast<uint32_t>(a * P) * 4u);
+      for (int a = 0; a < M; ++a) raw[a] = ld_at<uint32_t>(src, (lo + static_cast<uint32_t>(a * P)) * 4u);
     } else {
 #pragma unroll
-      for (int a = 0; a < M; ++a) raw[a] = ld_at<uint16_t>(src, static_cast<uint32_t>(a * P) * 2u);
+      for (int a = 0; a < M; ++a) raw[a] = ld_at<uint16_t>(src, (lo + static_cast<uint32_t>(a * P)) * 2u);
     }
   };
-  uint32_t raw[M];
-  if (bt < nbatch) load_col(raw, bt, 0);
+  uint32_t raw[NP][M];
+  auto load_batch = [&](int64_t b) {
+#pragma unroll
+    for (int ps = 0; ps < NP; ++ps)
+      if (ps < npass) load_col(raw[ps], b, ps);
+  };
+  if (bt < nbatch) load_batch(bt);
 
   // the rotation's sign bits, once per workgroup (lane l of a wave: element 64 n + l)
   for (int n = wave; n < (K >> 6); n += kMWaves) {
@@ -170,21 +191,24 @@ __global__ __launch_bounds__(kMThreads, 2) void k_encode_m(EncMParams p) {
   for (; bt < nbatch; bt += gridDim.x) {
     const int64_t row0 = bt * R;
     // phase A: signs and the m-point factor on each column
-    for (int ps = 0; ps < npass; ++ps) {
-      if (ps > 0) load_col(raw, bt, ps);
+#pragma unroll
+    for (int ps = 0; ps < (UNROLL ? MAXP : npass); ++ps) {
+      if (ps >= npass) break;
+      uint32_t(&rw)[M] = raw[UNROLL ? (ps < NP ? ps : NP - 1) : 0];
+      if (ps >= NP) load_col(rw, bt, ps);
       double x[M];
       if (wdt == 0) {
 #pragma unroll
-        for (int a = 0; a < M; ++a) x[a] = m_elem(raw[a], (smask >> a) & 1u, 0);
+        for (int a = 0; a < M; ++a) x[a] = m_elem(rw[a], (smask >> a) & 1u, 0);
       } else if (wdt == 1) {
 #pragma unroll
-        for (int a = 0; a < M; ++a) x[a] = m_elem(raw[a], (smask >> a) & 1u, 1);
+        for (int a = 0; a < M; ++a) x[a] = m_elem(rw[a], (smask >> a) & 1u, 1);
       } else {
 #pragma unroll
-        for (int a = 0; a < M; ++a) x[a] = m_elem(raw[a], (smask >> a) & 1u, 2);
+        for (int a = 0; a < M; ++a) x[a] = m_elem(rw[a], (smask >> a) & 1u, 2);
       }
-      // the next batch's first pass is requested as soon as its registers are free
-      if (ps == npass - 1 && bt + gridDim.x < nbatch) load_col(raw, bt + gridDim.x, 0);
+      // the next batch is requested as soon as the last pass's registers are free
+      if (ps == npass - 1 && bt + gridDim.x < nbatch) load_batch(bt + gridDim.x);
       const int r = ps * rpp + ar;
       if (r < R) {  // rows past the end of the data are transformed but never stored
         const int e0 = r * K + ab;
@@ -309,14 +333,14 @@ hipError_t launch_encode_m(const void* W, int wdt, int64_t rows, int K, int m, i
   int lg = 0;
   while ((1 << lg) < P) ++lg;
   p.lg_p = lg;
-  p.R = kMBatch / K;
+  p.R = kMBatch / K;  // >= 1: K <= 7168
   p.inv_k = static_cast<uint32_t>(((1ull << 32) + K - 1) / K);
   p.inv_sqrt_k = 1.0 / __builtin_sqrt(static_cast<double>(K));
   p.wpr = levels == 3 ? (K + 19) / 20
                       : (K * (levels == 4 ? 2 : levels == 8 ? 3 : levels == 16 ? 4 : 8)) / 32;
   if (!positive_threshold_bits(levels, levels == 256 ? p.tbig : p.tbits)) return hipErrorInvalidValue;
   const int64_t nbatch = (rows + p.R - 1) / p.R;
-  const int grid = static_cast<int>(nbatch < 256 ? nbatch : 256);  // one workgroup per CU
+  const int grid = static_cast<int>(nbatch < 512 ? nbatch : 512);  // two workgroups per CU
   const size_t lds = static_cast<size_t>(p.R) * K * 8;
   switch (m) {
     case 12: return launch_m_m<12>(p, levels, group, grid, lds, s);
