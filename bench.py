@@ -339,6 +339,14 @@ def encode_stack(E, N, K, levels, group, seed, cfg, tensor, dev, chunk=16, timin
     scales = torch.empty((E, N, K // group), dtype=torch.float16, device=dev)
     sg = tq.signs(seed, K, dev)
     ms = 0.0
+    if timing is not None:
+        # one untimed call of the same shape first: the first launch of a kernel in a
+        # process also loads its code
+        g = wl.torch_generator(dev, cfg, tensor, 0)
+        Wc = wl.torch_student_rows(g, min(chunk, E) * N, K, dev, torch.bfloat16).view(-1, N, K)
+        part = tq.QWeight(codes[:Wc.shape[0]], scales[:Wc.shape[0]], sg, levels, group, K, N, Wc.shape[0], seed)
+        tq.encode(Wc, levels, group, seed, out=part)
+        del Wc
     for e0 in range(0, E, chunk):
         e1 = min(E, e0 + chunk)
         g = wl.torch_generator(dev, cfg, tensor, e0)

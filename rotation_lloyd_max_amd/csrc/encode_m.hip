@@ -297,9 +297,7 @@ hipError_t launch_m_l(const EncMParams& p, int group, int grid, size_t lds, hipS
     case 64: kern = k_encode_m<M, LEVELS, 6>; break;
     default: kern = k_encode_m<M, LEVELS, 7>; break;
   }
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-  if (e != hipSuccess) return e;
+  // lds <= 64 KB, the default limit of dynamic LDS
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kMThreads), lds, s, p);
   return hipGetLastError();
 }
