@@ -56,11 +56,12 @@ __device__ __forceinline__ float kv_partner(float x) {
 
 template <int M>
 __device__ __forceinline__ void kv_lane_stage(float (&v)[kKvEl]) {
-  const bool upper = (threadIdx.x & M) != 0;
+  // the upper lane's partner - own as partner + (-own), the sign flipped in the bits (exact)
+  const uint32_t flip = (threadIdx.x & M) ? 0x80000000u : 0u;
 #pragma unroll
   for (int j = 0; j < kKvEl; ++j) {
     const float o = kv_partner<M>(v[j]);
-    v[j] = upper ? o - v[j] : v[j] + o;
+    v[j] = o + __uint_as_float(__float_as_uint(v[j]) ^ flip);
   }
 }
 
@@ -93,6 +94,14 @@ __global__ __launch_bounds__(kKvThreads) void k_kv_fetch(KvParams p) {
   for (int k = threadIdx.x; k < LEVELS; k += kKvThreads) lut[k] = p.lut[k];
   __syncthreads();
   const uint32_t sgn = p.signs[t];  // sign bits of elements col0 .. col0 + 31
+  // 16-bit outputs: the signs of elements 2k, 2k + 1 as the sign bits of packed pair k
+  // (negating before or after the rounding to nearest is the same)
+  uint32_t pmask[ODT == 0 ? 1 : kKvEl / 2];
+  if constexpr (ODT != 0) {
+#pragma unroll
+    for (int k = 0; k < kKvEl / 2; ++k)
+      pmask[k] = (((sgn >> (2 * k)) & 1u) << 15) | (((sgn >> (2 * k + 1)) & 1u) << 31);
+  }
   const int gi0 = col0 >> p.lg_group;
   u32x4_t* st = stage[wave];
 
@@ -115,8 +124,9 @@ __global__ __launch_bounds__(kKvThreads) void k_kv_fetch(KvParams p) {
     const KvIn<NW> in = nxt;
     if (b + stride < nb) fetch(b + stride, nxt);
     const int64_t row = b * rpw + rl;
-    const float s0 = half_bits_to_float(in.s0);
-    const float s1 = G16 ? half_bits_to_float(in.s1) : s0;
+    // the 1/sqrt(d) of R^T is folded into the group scales
+    const float s0 = half_bits_to_float(in.s0) * p.inv_sqrt_k;
+    const float s1 = G16 ? half_bits_to_float(in.s1) * p.inv_sqrt_k : s0;
     float v[kKvEl];
 #pragma unroll
     for (int j = 0; j < kKvEl; ++j) {
@@ -134,14 +144,11 @@ __global__ __launch_bounds__(kKvThreads) void k_kv_fetch(KvParams p) {
     if (tr > 8) kv_lane_stage<8>(v);
     if (tr > 16) kv_lane_stage<16>(v);
     if (tr > 32) kv_lane_stage<32>(v);
-    // R^T = diag(s) H / sqrt(d)
-#pragma unroll
-    for (int j = 0; j < kKvEl; ++j) {
-      const float x = v[j] * p.inv_sqrt_k;
-      v[j] = ((sgn >> j) & 1u) ? -x : x;
-    }
+    // R^T = diag(s) H / sqrt(d): the signs (1/sqrt(d) is in the scales)
     u32x4_t u[SU];
     if constexpr (ODT == 0) {
+#pragma unroll
+      for (int j = 0; j < kKvEl; ++j) v[j] = ((sgn >> j) & 1u) ? -v[j] : v[j];
 #pragma unroll
       for (int k = 0; k < SU; ++k)
         u[k] = u32x4_t{__float_as_uint(v[4 * k]), __float_as_uint(v[4 * k + 1]),
@@ -159,7 +166,7 @@ __global__ __launch_bounds__(kKvThreads) void k_kv_fetch(KvParams p) {
           a = float_to_half_rne(v[2 * k]);
           c = float_to_half_rne(v[2 * k + 1]);
         }
-        hw[k] = static_cast<uint32_t>(a) | (static_cast<uint32_t>(c) << 16);
+        hw[k] = (static_cast<uint32_t>(a) | (static_cast<uint32_t>(c) << 16)) ^ pmask[k];
       }
 #pragma unroll
       for (int k = 0; k < SU; ++k) u[k] = u32x4_t{hw[4 * k], hw[4 * k + 1], hw[4 * k + 2], hw[4 * k + 3]};
