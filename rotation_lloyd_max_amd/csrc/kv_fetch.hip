@@ -48,7 +48,7 @@ template <int M>
 __device__ __forceinline__ float kv_partner(float x) {
   if constexpr (M == 1 || M == 2) {
     constexpr int sel = M == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), sel, 0xf, 0xf, false));
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), sel, 0xf, 0xf, true));
   } else {
     return __shfl_xor(x, M);
   }
