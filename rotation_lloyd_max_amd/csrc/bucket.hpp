@@ -1,13 +1,18 @@
 // Counting sort of (input, expert) pairs by expert, for multi_gather_qmv: offsets[e] = first
 // position of expert e's pairs in `order`, order[] = pair indices grouped by expert (in any
 // order within an expert: atomics). Pairs with an expert id outside [0, E) get a row of NaN
-// in y and no position. Run by one workgroup of NT threads; cnt is LDS for E counters and
+// in y and no position. With `tiles` set, the pairs of every expert are also cut into tiles
+// of up to kTilePairs: tiles[t] = {expert, first position in order, pairs, 0} (experts in
+// increasing order), tile_rows[t][m] = pair m of the tile (zero_row past its pairs), and
+// *ntiles = their number. Run by one workgroup of NT threads; cnt is LDS for E counters and
 // wsum LDS for NT / 64 wave sums.
 #pragma once
 
 #include "device_common.hpp"
 
 namespace tq {
+
+constexpr int kTilePairs = 16;
 
 struct BucketJob {
   const int32_t* ids;
@@ -17,7 +22,40 @@ struct BucketJob {
   int32_t* order;
   void* y;
   int ydt, N;
+  int4* tiles;         // optional tile table (nullptr: none)
+  int32_t* tile_rows;
+  int32_t* ntiles;
+  int32_t zero_row;
 };
+
+// Exclusive scan of v(e) over e < E by the whole workgroup, NT values at a time with a
+// running carry: put(e, sum of v(e') for e' < e) for every e < E; returns the total. v(e)
+// is read before, and put called after, the barriers of its chunk.
+template <int NT, typename V, typename Put>
+__device__ __forceinline__ int block_exclusive_scan(int E, int32_t* wsum, V v_of, Put put) {
+  int carry = 0;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int base = 0; base < E; base += NT) {
+    const int e = base + threadIdx.x;
+    const int c = e < E ? v_of(e) : 0;
+    int v = c;
+    for (int off = 1; off < 64; off <<= 1) {  // inclusive wave scan
+      const int t = __shfl_up(v, off, 64);
+      if (lane >= off) v += t;
+    }
+    if (lane == 63) wsum[wave] = v;
+    __syncthreads();
+    int before = carry, total = carry;
+    for (int k = 0; k < NT / 64; ++k) {
+      before += k < wave ? wsum[k] : 0;
+      total += wsum[k];
+    }
+    __syncthreads();
+    if (e < E) put(e, before + v - c);
+    carry = total;
+  }
+  return carry;
+}
 
 template <int NT>
 __device__ __forceinline__ void bucket_pairs(const BucketJob& b, int32_t* cnt, int32_t* wsum) {
@@ -33,33 +71,13 @@ __device__ __forceinline__ void bucket_pairs(const BucketJob& b, int32_t* cnt, i
     }
   }
   __syncthreads();
-  // exclusive scan of cnt[0..E) in chunks of NT, carried as a running sum
-  int carry = 0;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int base = 0; base < E; base += NT) {
-    const int e = base + threadIdx.x;
-    const int c = e < E ? cnt[e] : 0;
-    int v = c;
-    for (int off = 1; off < 64; off <<= 1) {  // inclusive wave scan
-      const int t = __shfl_up(v, off, 64);
-      if (lane >= off) v += t;
-    }
-    if (lane == 63) wsum[wave] = v;
-    __syncthreads();
-    int before = carry, total = carry;
-    for (int k = 0; k < NT / 64; ++k) {
-      before += k < wave ? wsum[k] : 0;
-      total += wsum[k];
-    }
-    __syncthreads();
-    if (e < E) {
-      const int excl = before + v - c;
-      b.offsets[e] = excl;
-      cnt[e] = excl;  // becomes the scatter cursor
-    }
-    carry = total;
-  }
-  if (threadIdx.x == 0) b.offsets[E] = carry;
+  const int total = block_exclusive_scan<NT>(
+      E, wsum, [&](int e) { return cnt[e]; },
+      [&](int e, int excl) {
+        b.offsets[e] = excl;
+        cnt[e] = excl;  // becomes the scatter cursor
+      });
+  if (threadIdx.x == 0) b.offsets[E] = total;
   __syncthreads();
   for (int64_t p = threadIdx.x; p < b.P; p += NT) {
     const int e = b.ids[p];
@@ -68,6 +86,23 @@ __device__ __forceinline__ void bucket_pairs(const BucketJob& b, int32_t* cnt, i
       b.order[pos] = static_cast<int32_t>(p);
     }
   }
+  if (!b.tiles) return;
+  // cnt[e] is now the end of expert e's pairs (the start of expert e + 1's)
+  __syncthreads();
+  auto pairs_of = [&](int e) { return cnt[e] - (e > 0 ? cnt[e - 1] : 0); };
+  const int nt = block_exclusive_scan<NT>(
+      E, wsum, [&](int e) { return (pairs_of(e) + kTilePairs - 1) / kTilePairs; },
+      [&](int e, int t0) {
+        const int start = e > 0 ? cnt[e - 1] : 0, n = pairs_of(e);
+        for (int t = 0; t * kTilePairs < n; ++t) {
+          const int first = start + t * kTilePairs;
+          const int m = n - t * kTilePairs < kTilePairs ? n - t * kTilePairs : kTilePairs;
+          b.tiles[t0 + t] = make_int4(e, first, m, 0);
+          for (int j = 0; j < kTilePairs; ++j)
+            b.tile_rows[(t0 + t) * kTilePairs + j] = j < m ? b.order[first + j] : b.zero_row;
+        }
+      });
+  if (threadIdx.x == 0) *b.ntiles = nt;
 }
 
 }  // namespace tq

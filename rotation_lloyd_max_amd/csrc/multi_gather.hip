@@ -29,17 +29,25 @@ constexpr int kMgThreads = 64 * kMgWaves;
 static size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
 // Workspace: offsets [E+1] int32 | order [P] int32 | scale [P+1] float |
-// rotated rows [P+1][rot16_row_halves(K)] fp16 (row P all zero); 256-byte aligned sections.
+// rotated rows [P+1][rot16_row_halves(K)] fp16 (row P all zero) | tile count int32 |
+// tiles int4 [T] | tile rows int32 [T][16], T = ceil(P / 16) + min(E, P) at most;
+// 256-byte aligned sections.
 struct MgLayout {
-  size_t offsets, order, scale, rows, total;
+  size_t offsets, order, scale, rows, ntiles, tiles, tile_rows, total;
 };
+static int64_t mg_max_tiles(const WeightArgs& w, int64_t P) {
+  return (P + kTilePairs - 1) / kTilePairs + (P < w.E ? P : w.E);
+}
 static MgLayout mg_layout(const WeightArgs& w, int64_t P) {
   MgLayout l{};
   l.offsets = 0;
   l.order = align256(static_cast<size_t>(w.E + 1) * 4);
   l.scale = l.order + align256(static_cast<size_t>(P) * 4);
   l.rows = l.scale + align256(static_cast<size_t>(P + 1) * 4);
-  l.total = l.rows + align256(static_cast<size_t>(P + 1) * rot16_row_halves(w.K) * 2);
+  l.ntiles = l.rows + align256(static_cast<size_t>(P + 1) * rot16_row_halves(w.K) * 2);
+  l.tiles = l.ntiles + 256;
+  l.tile_rows = l.tiles + align256(static_cast<size_t>(mg_max_tiles(w, P)) * 16);
+  l.total = l.tile_rows + align256(static_cast<size_t>(mg_max_tiles(w, P)) * kTilePairs * 4);
   return l;
 }
 
@@ -346,6 +354,426 @@ __global__ __launch_bounds__(kMgThreads, 4) void k_mg(MgParams p) {
   }
 }
 
+// k_mgt: the trit layer with its staging done by direct loads into LDS.
+//
+// One persistent workgroup of 8 waves per compute unit walks its items (a tile of up to 16
+// pairs of one expert times a block of 128 output rows): items w, w + G, w + 2G, ... of
+// the tile-major list, every item's K in chunks of 480 elements (3 super-blocks of 160).
+// A chunk's code words, group scales and rotated inputs go from memory straight into LDS
+// (global_load_lds: no staging registers, no LDS store instructions) into stage s % 3 of a
+// ring, two chunks ahead of the chunk being decoded and across item boundaries, with one
+// barrier per chunk. Every thread requests the same number of direct loads per chunk
+// (rows, words and units past the data load valid addresses into LDS padding that is never
+// read), so a constant vmcnt waits for exactly the chunk about to be read. The direct loads
+// are written as inline assembly: the compiler then neither waits for them before reading
+// other stages nor counts them, and the kernel has no vector loads of its own (the items'
+// pairs and input scales come through scalar loads), so every wait for memory is the
+// explicit one before each barrier. Decode and matrix multiplies are those of k_mg.
+constexpr int kMtSB = 3;                                           // super-blocks per chunk
+constexpr int kMtKC = 160 * kMtSB;                                 // elements per chunk
+constexpr int kMtWPC = kMtKC / 20;                                 // code words per row and chunk
+constexpr int kMtCST = kMtWPC + 2;                                 // LDS words per row of codes
+constexpr int kMtCW = (128 * kMtCST + kMgThreads - 1) / kMgThreads;  // code loads per thread
+constexpr int kMtUnits = kMtKC / 8;                                // 16-byte input units per pair
+constexpr int kMtAST = 65;                                         // LDS units per pair (64 + pad)
+
+template <int LG>
+struct MtScales {
+  // groups a chunk touches at most, plus one half for a window that starts on an odd group
+  // (the loads move 4-byte pairs of scales)
+  static constexpr int halves = ((kMtKC + (1 << LG) - 1) >> LG) + 2;
+  static constexpr int SST = ((halves + 1) / 2) | 1;                   // dwords per row (odd)
+  static constexpr int SW = (128 * SST + kMgThreads - 1) / kMgThreads;  // scale loads per thread
+  static constexpr int NDMA = kMtCW + SW + 2;                           // direct loads per chunk
+};
+
+struct MtParams {
+  const uint32_t* codes;
+  const uint16_t* scales;
+  const _Float16* xh;
+  void* y;
+  int64_t rowh, zero_row;
+  int K, N, E, wpr, ngk, ydt, nblk;
+  CodebookArgs cb;
+};
+
+// Wait until at most N direct loads (and stores) of this wave are outstanding and its LDS
+// and scalar loads are done, then the workgroup barrier (no memory fence: a fence would
+// wait for every load in flight).
+template <int N>
+__device__ __forceinline__ void mt_sync() {
+  static_assert(N < 64, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(N) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void mt_wait_vm() {
+  static_assert(N < 64, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+}
+
+// LDS byte address of a __shared__ pointer (the value M0 takes for a direct load).
+__device__ __forceinline__ uint32_t mt_lds_addr(const void* ptr) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)(ptr)));
+}
+
+// Direct loads: every lane reads BYTES at base + voff (base uniform) and the wave writes
+// them to LDS at lds + BYTES * lane (lds uniform). M0 holds the LDS address; its write
+// needs one wait state before the load.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; the compiler reloads it
+__device__ __forceinline__ void mt_dma4(const void* base, uint32_t voff, const void* lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(mt_lds_addr(lds)),
+               "v"(voff), "s"(base)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void mt_dma4_at(const void* addr, const void* lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(mt_lds_addr(lds)),
+               "v"(addr)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void mt_dma16(const void* base, uint32_t voff, const void* lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(mt_lds_addr(lds)),
+               "v"(voff), "s"(base)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// The request side's per-item state: where the item's rows are, the rotated rows of this
+// wave's two pair slots, and each thread's row offsets of its code and scale loads.
+template <int LG>
+struct MtReq {
+  const uint32_t* codes;
+  const uint16_t* scales;
+  uint32_t slim;  // last 4-byte scale offset inside the array, from `scales`
+  int in[2];
+  uint32_t zoff[2];           // byte offset of the all-zero row from each slot's row
+  uint32_t cofs[kMtCW];       // byte offset of the thread's code word in chunk 0
+  uint32_t cend[kMtCW];       // ... and of the last word of its row
+  uint32_t sofs[MtScales<LG>::SW];  // byte offset of the thread's scale pair in chunk 0
+};
+
+// The request side's state for an item: e its expert, in0 / in1 the rotated rows of this
+// wave's two pair slots, row0 its first weight row. The thread's row and word of each
+// load depend on its index only, so per chunk every load address is one add and a clamp.
+template <int LG>
+__device__ __forceinline__ void mt_request_item(MtReq<LG>& d, const MtParams& p, int e, int in0,
+                                                int in1, int row0, int tid) {
+  using SC = MtScales<LG>;
+  d.codes = p.codes + static_cast<int64_t>(e) * p.N * p.wpr;
+  d.scales = p.scales + static_cast<int64_t>(e) * p.N * p.ngk;
+  const int64_t lim = (static_cast<int64_t>(p.E - e) * p.N * p.ngk - 2) * 2;
+  d.slim = lim < 0xfffffffcll ? static_cast<uint32_t>(lim) : 0xfffffffcu;
+  d.in[0] = in0;
+  d.in[1] = in1;
+  d.zoff[0] = static_cast<uint32_t>((p.zero_row - in0) * p.rowh) * 2u;
+  d.zoff[1] = static_cast<uint32_t>((p.zero_row - in1) * p.rowh) * 2u;
+  const uint32_t wpr4 = static_cast<uint32_t>(p.wpr) * 4u, ngk2 = static_cast<uint32_t>(p.ngk) * 2u;
+  // code words: LDS word i holds row i / 26, word i % 26 of the chunk (24, 25: padding,
+  // which load the row's word 23)
+#pragma unroll
+  for (int j = 0; j < kMtCW; ++j) {
+    const int i = j * kMgThreads + tid, r = i / kMtCST, wd = i - r * kMtCST;
+    int row = row0 + (r < 128 ? r : 127);
+    row = row < p.N ? row : p.N - 1;
+    const uint32_t base = __umul24(static_cast<uint32_t>(row), wpr4);
+    d.cofs[j] = base + static_cast<uint32_t>(wd < kMtWPC ? wd : kMtWPC - 1) * 4u;
+    d.cend[j] = base + wpr4 - 4u;
+  }
+#pragma unroll
+  for (int j = 0; j < SC::SW; ++j) {
+    const int i = j * kMgThreads + tid, r = i / SC::SST, dw = i - r * SC::SST;
+    int row = row0 + (r < 128 ? r : 127);
+    row = row < p.N ? row : p.N - 1;
+    d.sofs[j] = __umul24(static_cast<uint32_t>(row), ngk2) + static_cast<uint32_t>(dw) * 4u;
+  }
+}
+
+// Direct load I (of NDMA) of chunk c of the request item into one stage: code words,
+// then scale pairs, then the inputs of the wave's two pair slots.
+template <int LG, int I>
+__device__ __forceinline__ void mt_dma_one(const MtReq<LG>& d, const MtParams& p, int c,
+                                           uint32_t* lcw, uint32_t* lsw, u32x4_t* law, int wave,
+                                           int lane) {
+  using SC = MtScales<LG>;
+  if constexpr (I < kMtCW) {
+    // LDS word i holds row i / 26, word i % 26 of the chunk (24, 25: padding)
+    const uint32_t off = d.cofs[I] + static_cast<uint32_t>(c * kMtWPC) * 4u;
+    mt_dma4(d.codes, off < d.cend[I] ? off : d.cend[I], lcw + I * kMgThreads + wave * 64);
+  } else if constexpr (I < kMtCW + SC::SW) {
+    // 4-byte pairs from the even group at or below the chunk's first group
+    const uint32_t off = d.sofs[I - kMtCW] + static_cast<uint32_t>(((c * kMtKC) >> LG) & ~1) * 2u;
+    mt_dma4(d.scales, off < d.slim ? off : d.slim, lsw + (I - kMtCW) * kMgThreads + wave * 64);
+  } else {
+    // unit = lane of pair slot 2 wave + jj, as a byte offset from the slot's row (units past
+    // the chunk or past K read the all-zero row, which follows every pair's)
+    constexpr int jj = I - kMtCW - SC::SW;
+    const int e = c * kMtKC + 8 * lane;
+    const bool ok = lane < kMtUnits && e < p.K;
+    mt_dma16(p.xh + static_cast<int64_t>(d.in[jj]) * p.rowh,
+             ok ? static_cast<uint32_t>(e) * 2u : d.zoff[jj], law + (2 * wave + jj) * kMtAST);
+  }
+}
+
+// Part PART (of three) of the direct loads of chunk c: spread over the decode of the chunk
+// being read, so that the waves' address processing overlaps their arithmetic.
+template <int LG, int PART, int... I>
+__device__ __forceinline__ void mt_request_part_(std::integer_sequence<int, I...>, const MtReq<LG>& d,
+                                                 const MtParams& p, int c, uint32_t* lcw,
+                                                 uint32_t* lsw, u32x4_t* law, int wave, int lane) {
+  constexpr int per = (MtScales<LG>::NDMA + 2) / 3;
+  (mt_dma_one<LG, PART * per + I>(d, p, c, lcw, lsw, law, wave, lane), ...);
+}
+template <int LG, int PART>
+__device__ __forceinline__ void mt_request_part(const MtReq<LG>& d, const MtParams& p, int c,
+                                                uint32_t* lcw, uint32_t* lsw, u32x4_t* law,
+                                                int wave, int lane) {
+  constexpr int n = MtScales<LG>::NDMA, per = (n + 2) / 3;
+  constexpr int cnt = n - PART * per < per ? n - PART * per : per;
+  mt_request_part_<LG, PART>(std::make_integer_sequence<int, cnt>{}, d, p, c, lcw, lsw, law, wave,
+                             lane);
+}
+
+// Super-block SB of a chunk.
+template <int LG, int SB>
+__device__ __forceinline__ void mt_decode_sb(f32x4_t& acc, int kr, const uint32_t* cw,
+                                             const uint16_t* sw, const u32x4_t* aw,
+                                             const uint32_t* lut, uint32_t slot, int g) {
+  constexpr int sb = SB;
+  const uint32_t w[2] = {cw[8 * sb], cw[8 * sb + 1]};
+  uint32_t s2[5];
+  if constexpr (LG == 4) {
+    // the 40-element span of lane group g starts at 40 g: fragment f is in group
+    // 10 sb + floor(5 g / 2) + (g odd + f) / 2 of the chunk
+    const uint16_t* sg = sw + 10 * sb + ((5 * g) >> 1);
+    const uint32_t a0 = __umul24(static_cast<uint32_t>(sg[0]), 0x10001u);
+    const uint32_t a1 = __umul24(static_cast<uint32_t>(sg[1]), 0x10001u);
+    const uint32_t a2 = __umul24(static_cast<uint32_t>(sg[2]), 0x10001u);
+    const bool odd = (g & 1) != 0;
+    s2[0] = a0;
+    s2[1] = odd ? a1 : a0;
+    s2[2] = a1;
+    s2[3] = odd ? a2 : a1;
+    s2[4] = a2;
+  } else {
+#pragma unroll
+    for (int f = 0; f < 5; ++f)
+      s2[f] = __umul24(static_cast<uint32_t>(sw[(kr + 160 * sb + 40 * g + 8 * f) >> LG]),
+                       0x10001u);
+  }
+  u32x4_t b[5];
+  span_fragments<3>(w, lut, slot, s2, b);
+#pragma unroll
+  for (int f = 0; f < 5; ++f) acc = mfma_f16(aw[20 * sb + f], b[f], acc);
+}
+
+
+// Super-blocks 0 .. NSB - 1 of a chunk, after(sb) called after each (see mt_decode).
+template <int LG, int NSB, typename After>
+__device__ __forceinline__ void mt_decode_sbs(f32x4_t& acc, int kr, const uint32_t* cw,
+                                              const uint16_t* sw, const u32x4_t* aw,
+                                              const uint32_t* lut, uint32_t slot, int g,
+                                              After after) {
+  [&]<int... SB>(std::integer_sequence<int, SB...>) {
+    ((mt_decode_sb<LG, SB>(acc, kr, cw, sw, aw, lut, slot, g),
+      after(std::integral_constant<int, SB>{})),
+     ...);
+  }(std::make_integer_sequence<int, NSB>{});
+}
+
+// Decode chunk c from one stage into the lane's accumulator.
+template <int LG, typename After>
+__device__ __forceinline__ void mt_decode(f32x4_t& acc, const MtParams& p, int c,
+                                          const uint32_t* lcr, const uint32_t* lsr,
+                                          const u32x4_t* lar, const uint32_t* lut, uint32_t slot,
+                                          int nrow, int g, int col, After after) {
+  using SC = MtScales<LG>;
+  const int kc0 = c * kMtKC;
+  const int nsb = (p.K - kc0 + 159) / 160 < kMtSB ? (p.K - kc0 + 159) / 160 : kMtSB;
+  const int g0 = kc0 >> LG;
+  const uint32_t* cw = lcr + nrow * kMtCST + 2 * g;
+  // half index of group gi of this row: (gi - g0) + (g0 & 1)
+  const uint16_t* sw = reinterpret_cast<const uint16_t*>(lsr) + nrow * (2 * SC::SST) + (g0 & 1);
+  const u32x4_t* aw = lar + col * kMtAST + 5 * g;
+  const int kr = kc0 - (g0 << LG);  // chunk start within its group
+  // a full chunk as one block of straight-line code (the scheduler can then overlap the
+  // super-blocks' LDS reads with the arithmetic of the ones before); the last chunk of a
+  // row may hold fewer super-blocks, and after() still runs three times
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  if (nsb == kMtSB) {
+    mt_decode_sbs<LG, kMtSB>(acc, kr, cw, sw, aw, lut, slot, g, after);
+  } else if (nsb == 2) {
+    mt_decode_sbs<LG, 2>(acc, kr, cw, sw, aw, lut, slot, g, after);
+    after(I2{});
+  } else {
+    mt_decode_sbs<LG, 1>(acc, kr, cw, sw, aw, lut, slot, g, after);
+    after(I1{});
+    after(I2{});
+  }
+}
+
+// Items have at least two chunks (K > 480). Besides the chunks, wave 0 requests the
+// description of item k + 2 into LDS at the first chunk of item k (the tile's 16 pair rows
+// and its {expert, first position, pairs} entry) and the pairs' input scales at the second
+// (three slots, item j in slot j % 3), before that step's chunk requests, so that the
+// barrier's wait covers them; both sides then read the items from LDS. Item 0's expert and
+// pair rows for the first requests come from scalar loads.
+constexpr int kMtInfo = kTilePairs + 4;  // LDS words per item: pair rows, tile entry
+template <int LG>
+__global__ __launch_bounds__(kMgThreads) void k_mgt(MtParams p, const int4* __restrict__ tiles,
+                                                    const int32_t* __restrict__ tile_rows,
+                                                    const int32_t* __restrict__ ntiles,
+                                                    const float* __restrict__ xs) {
+  using SC = MtScales<LG>;
+  constexpr int CS = kMtCW * kMgThreads, SS = SC::SW * kMgThreads, AS = kTilePairs * kMtAST;
+  __shared__ __attribute__((aligned(16))) uint32_t lut[mlut_bytes<3>() / 4];
+  __shared__ __attribute__((aligned(16))) uint32_t lc0[CS], lc1[CS], lc2[CS];
+  __shared__ __attribute__((aligned(16))) uint32_t ls0[SS], ls1[SS], ls2[SS];
+  __shared__ __attribute__((aligned(16))) u32x4_t la0[AS], la1[AS], la2[AS];
+  __shared__ __attribute__((aligned(16))) int32_t info[3][kMtInfo];
+  __shared__ __attribute__((aligned(16))) float ixs[3][kTilePairs];
+  __shared__ uint16_t hs[16];
+
+  const int nitems = *ntiles * p.nblk;
+  const int G = static_cast<int>(gridDim.x), w0 = static_cast<int>(blockIdx.x);
+  if (w0 >= nitems) return;  // uniform
+  const int nch = (p.K + kMtKC - 1) / kMtKC;  // at least 2
+  const int nk = (nitems - w0 + G - 1) / G;   // items of this workgroup
+  const int total = nk * nch;                  // chunks of this workgroup
+
+  const int tid = static_cast<int>(threadIdx.x);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, g = lane >> 4, col = lane & 15;
+  const uint32_t slot = mlut_slot<3>(lane);
+  const int nrow = wave * 16 + col;  // this lane's weight row within the block
+  auto item_tile = [&](int k, int& T, int& row0) __attribute__((always_inline)) {
+    const int i = w0 + k * G;
+    T = i / p.nblk;
+    row0 = (i - T * p.nblk) * 128;
+  };
+  // wave 0: item k's pair rows (lanes 0..15) and tile entry (lanes 16..19) into LDS ...
+  auto info_req = [&](int k) __attribute__((always_inline)) {
+    if (wave == 0 && lane < kMtInfo) {
+      int T, row0;
+      item_tile(k, T, row0);
+      const void* a = lane < kTilePairs
+                          ? static_cast<const void*>(tile_rows + T * kTilePairs + lane)
+                          : static_cast<const void*>(reinterpret_cast<const int32_t*>(tiles + T) +
+                                                     (lane - kTilePairs));
+      mt_dma4_at(a, info[k % 3]);
+    }
+  };
+  // ... and, once those are in LDS, its pairs' input scales
+  auto info_xs = [&](int k) __attribute__((always_inline)) {
+    if (wave == 0 && lane < kTilePairs)
+      mt_dma4(xs, static_cast<uint32_t>(info[k % 3][lane]) * 4u, ixs[k % 3]);
+  };
+
+  // Request side: every step requests a chunk, so that each wave has the same loads in
+  // flight on every path; requests past the last chunk repeat it into a stage that is never
+  // read again. Counters move by arithmetic (a branch that picks which counter to bump turns
+  // them into memory).
+  MtReq<LG> d;
+  int dk = 0, dc = 0;
+  // request_begin returns the chunk to request (switching items where one starts), the
+  // parts go out during the decode, request_end moves on
+  auto request_begin = [&]() __attribute__((always_inline)) {
+    if (dc == 0 && dk > 0 && dk < nk) {
+      int T, row0;
+      item_tile(dk, T, row0);
+      const int* it = info[dk % 3];
+      mt_request_item<LG>(d, p, __builtin_amdgcn_readfirstlane(it[kTilePairs]),
+                          __builtin_amdgcn_readfirstlane(it[2 * wave]),
+                          __builtin_amdgcn_readfirstlane(it[2 * wave + 1]), row0, tid);
+    }
+    return dk < nk ? dc : nch - 1;
+  };
+  auto request_end = [&]() __attribute__((always_inline)) {
+    const bool wrap = dc + 1 == nch;
+    dk += wrap ? 1 : 0;
+    dc = wrap ? 0 : dc + 1;
+  };
+  auto request = [&](uint32_t* lcw, uint32_t* lsw, u32x4_t* law) __attribute__((always_inline)) {
+    const int c = request_begin();
+    mt_request_part<LG, 0>(d, p, c, lcw, lsw, law, wave, lane);
+    mt_request_part<LG, 1>(d, p, c, lcw, lsw, law, wave, lane);
+    mt_request_part<LG, 2>(d, p, c, lcw, lsw, law, wave, lane);
+    request_end();
+  };
+
+  // Prologue: items 0 and 1 described in LDS, the first two chunks requested (item 0 from
+  // scalar loads), the table built; wave 0 then waits for the descriptions (its oldest
+  // loads) and requests the input scales.
+  {
+    int T, row0;
+    item_tile(0, T, row0);
+    mt_request_item<LG>(d, p, tiles[T].x, tile_rows[T * kTilePairs + 2 * wave],
+                        tile_rows[T * kTilePairs + 2 * wave + 1], row0, tid);
+  }
+  info_req(0);
+  if (nk > 1) info_req(1);
+  if (tid < 16) hs[tid] = p.cb.h[tid];
+  request(lc0, ls0, la0);
+  request(lc1, ls1, la1);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  build_mlut<3, kMgThreads>(lut, hs);
+  if (wave == 0) {
+    mt_wait_vm<2 * SC::NDMA>();
+    info_xs(0);
+    if (nk > 1) info_xs(1);
+  }
+
+  // Decode side.
+  int kk = 0, kc = 0;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  auto step = [&](uint32_t* lcw, uint32_t* lsw, u32x4_t* law, const uint32_t* lcr,
+                  const uint32_t* lsr, const u32x4_t* lar) __attribute__((always_inline)) {
+    mt_sync<SC::NDMA>();
+    if (kk + 2 < nk) {
+      if (kc == 0) info_req(kk + 2);
+      else if (kc == 1) info_xs(kk + 2);
+    }
+    const int rc = request_begin();
+    mt_decode<LG>(acc, p, kc, lcr, lsr, lar, lut, slot, nrow, g, col, [&](auto part) {
+      mt_request_part<LG, decltype(part)::value>(d, p, rc, lcw, lsw, law, wave, lane);
+    });
+    request_end();
+    if (kc == nch - 1) {
+      // D[4 g + r][col] = output row row0 + nrow of the tile's pair 4 g + r
+      int T, row0;
+      item_tile(kk, T, row0);
+      const int n = row0 + nrow;
+      const int* it = info[kk % 3];
+      const int cnt = it[kTilePairs + 2];
+      const int4 pr = *reinterpret_cast<const int4*>(it + 4 * g);
+      const float4 sc = *reinterpret_cast<const float4*>(&ixs[kk % 3][4 * g]);
+      const int prs[4] = {pr.x, pr.y, pr.z, pr.w};
+      const float scs[4] = {sc.x, sc.y, sc.z, sc.w};
+      if (n < p.N) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (4 * g + r < cnt)
+            store_any(p.y, p.ydt, static_cast<int64_t>(prs[r]) * p.N + n, acc[r] * scs[r]);
+      }
+      acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    const bool wrap = kc + 1 == nch;
+    kk += wrap ? 1 : 0;
+    kc = wrap ? 0 : kc + 1;
+  };
+
+  for (int s = 0; s < total; s += 3) {
+    step(lc2, ls2, la2, lc0, ls0, la0);
+    if (s + 1 >= total) break;
+    step(lc0, ls0, la0, lc1, ls1, la1);
+    if (s + 2 >= total) break;
+    step(lc1, ls1, la1, lc2, ls2, la2);
+  }
+  // the repeated requests of the last steps land in LDS before the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // The workspace of tq_multi_gather_qmv_static: one fixed array per GPU, for callers that
 // cannot allocate. Host code never passes `scratch` itself (on the host it names a stand-in,
 // not device memory): static_scratch() resolves its address on the current device once
@@ -375,6 +803,24 @@ hipError_t static_scratch(void** ptr) {
   return hipSuccess;
 }
 
+// Compute units of the current device (looked up once per device).
+static hipError_t compute_units(int* n) {
+  static std::mutex mu;
+  static int cache[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cache[dev]) {
+    e = hipDeviceGetAttribute(&cache[dev], hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (cache[dev] <= 0) return hipErrorInvalidDevice;
+  }
+  *n = cache[dev];
+  return hipSuccess;
+}
+
 hipError_t launch_multi_gather(const WeightArgs& w, const int32_t* ids, int64_t P, const void* x,
                                int xdt, bool x_rotated, void* y, int ydt, void* ws,
                                hipStream_t s) {
@@ -386,10 +832,41 @@ hipError_t launch_multi_gather(const WeightArgs& w, const int32_t* ids, int64_t 
   float* xs = reinterpret_cast<float*>(base + lay.scale);
   _Float16* xh = reinterpret_cast<_Float16*>(base + lay.rows);
   if (w.E > kMaxExperts) return hipErrorInvalidValue;
+  // trits with 4-byte aligned rows of scales: the direct-load kernel, which needs the tiles
+  const bool direct = w.levels == 3 && w.group >= 16 && w.group <= 128 &&
+                      (w.K / w.group) % 2 == 0 && w.K > kMtKC &&
+                      (P + 1) * rot16_row_halves(w.K) * 2 < (int64_t(1) << 32);
+  int4* tiles = reinterpret_cast<int4*>(base + lay.tiles);
+  int32_t* tile_rows = reinterpret_cast<int32_t*>(base + lay.tile_rows);
+  int32_t* ntiles = reinterpret_cast<int32_t*>(base + lay.ntiles);
   // one launch rotates every pair's input and (one extra workgroup) buckets the pairs
-  BucketJob job{ids, P, w.E, offsets, order, y, ydt, w.N};
+  BucketJob job{ids, P, w.E, offsets, order, y, ydt, w.N,
+                direct ? tiles : nullptr, tile_rows, ntiles, static_cast<int32_t>(P)};
   hipError_t err = launch_rot16(x, xdt, nullptr, P, /*zero_rows=*/1, w, x_rotated, xh, xs, &job, s);
   if (err != hipSuccess) return err;
+  if (direct) {
+    MtParams q{};
+    q.codes = w.codes; q.scales = w.scales; q.xh = xh; q.y = y;
+    q.rowh = rot16_row_halves(w.K);
+    q.zero_row = P;
+    q.K = w.K; q.N = w.N; q.E = w.E; q.wpr = w.wpr; q.ngk = w.K / w.group; q.ydt = ydt;
+    q.nblk = (w.N + 127) / 128;
+    q.cb = *codebook_for(w.levels);
+    // one workgroup per compute unit (each holds 141 KB of LDS); the items are shared out
+    // on the device, where their number is known
+    int ncu = 0;
+    err = compute_units(&ncu);
+    if (err != hipSuccess) return err;
+    const int64_t items = mg_max_tiles(w, P) * q.nblk;
+    const int grid = static_cast<int>(items < ncu ? items : ncu);
+    switch (__builtin_ctz(w.group)) {
+      case 4: hipLaunchKernelGGL(k_mgt<4>, dim3(grid), dim3(kMgThreads), 0, s, q, tiles, tile_rows, ntiles, xs); break;
+      case 5: hipLaunchKernelGGL(k_mgt<5>, dim3(grid), dim3(kMgThreads), 0, s, q, tiles, tile_rows, ntiles, xs); break;
+      case 6: hipLaunchKernelGGL(k_mgt<6>, dim3(grid), dim3(kMgThreads), 0, s, q, tiles, tile_rows, ntiles, xs); break;
+      default: hipLaunchKernelGGL(k_mgt<7>, dim3(grid), dim3(kMgThreads), 0, s, q, tiles, tile_rows, ntiles, xs); break;
+    }
+    return hipGetLastError();
+  }
 
   MgParams p{};
   p.codes = w.codes; p.scales = w.scales; p.offsets = offsets; p.order = order;

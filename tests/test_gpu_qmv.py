@@ -241,6 +241,8 @@ def test_gather_qmv_bad_id_gives_nan_rows():
 
 
 @pytest.mark.parametrize("levels,group,K,N", [(3, 16, 2048, 96), (3, 16, 768, 160),
+                                              (3, 32, 2560, 136), (3, 64, 1280, 64),
+                                              (3, 128, 1536, 40), (3, 32, 384, 72),
                                               (16, 64, 1536, 64), (4, 32, 7168, 48),
                                               (8, 128, 6144, 40), (4, 64, 5120, 40)])
 def test_multi_gather(levels, group, K, N):
