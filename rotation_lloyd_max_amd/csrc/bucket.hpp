@@ -4,8 +4,7 @@
 // in y and no position. With `tiles` set, the pairs of every expert are also cut into tiles
 // of up to kTilePairs: tiles[t] = {expert, first position in order, pairs, 0} (experts in
 // increasing order), tile_rows[t][m] = pair m of the tile (zero_row past its pairs), and
-// *ntiles = their number. Run by one workgroup of NT threads; cnt is LDS for E counters and
-// wsum LDS for NT / 64 wave sums.
+// *ntiles = their number. Run by one workgroup of NT threads.
 #pragma once
 
 #include "device_common.hpp"
@@ -57,9 +56,50 @@ __device__ __forceinline__ int block_exclusive_scan(int E, int32_t* wsum, V v_of
   return carry;
 }
 
+// The same scan for two values at once: put(e, sums of a(e'), sums of b(e') for e' < e,
+// a(e), b(e)); returns both totals. wsum: 2 NT / 64 ints of LDS.
+template <int NT, typename V, typename Put>
+__device__ __forceinline__ int2 block_exclusive_scan2(int E, int32_t* wsum, V v_of, Put put) {
+  int2 carry = make_int2(0, 0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int base = 0; base < E; base += NT) {
+    const int e = base + threadIdx.x;
+    const int2 c = e < E ? v_of(e) : make_int2(0, 0);
+    int2 v = c;
+    for (int off = 1; off < 64; off <<= 1) {  // inclusive wave scans
+      const int tx = __shfl_up(v.x, off, 64), ty = __shfl_up(v.y, off, 64);
+      if (lane >= off) {
+        v.x += tx;
+        v.y += ty;
+      }
+    }
+    if (lane == 63) {
+      wsum[wave] = v.x;
+      wsum[NT / 64 + wave] = v.y;
+    }
+    __syncthreads();
+    int2 before = carry, total = carry;
+    for (int k = 0; k < NT / 64; ++k) {
+      const int ax = wsum[k], ay = wsum[NT / 64 + k];
+      if (k < wave) {
+        before.x += ax;
+        before.y += ay;
+      }
+      total.x += ax;
+      total.y += ay;
+    }
+    __syncthreads();
+    if (e < E) put(e, before.x + v.x - c.x, before.y + v.y - c.y, c.x, c.y);
+    carry = total;
+  }
+  return carry;
+}
+
+// cnt: E ints of LDS (2 E with tiles); wsum: 2 NT / 64 ints.
 template <int NT>
 __device__ __forceinline__ void bucket_pairs(const BucketJob& b, int32_t* cnt, int32_t* wsum) {
   const int E = b.E;
+  int32_t* t0 = cnt + E;  // with tiles: first tile of each expert
   for (int e = threadIdx.x; e < E; e += NT) cnt[e] = 0;
   __syncthreads();
   for (int64_t p = threadIdx.x; p < b.P; p += NT) {
@@ -71,38 +111,46 @@ __device__ __forceinline__ void bucket_pairs(const BucketJob& b, int32_t* cnt, i
     }
   }
   __syncthreads();
-  const int total = block_exclusive_scan<NT>(
-      E, wsum, [&](int e) { return cnt[e]; },
-      [&](int e, int excl) {
-        b.offsets[e] = excl;
-        cnt[e] = excl;  // becomes the scatter cursor
-      });
-  if (threadIdx.x == 0) b.offsets[E] = total;
+  if (!b.tiles) {
+    const int total = block_exclusive_scan<NT>(
+        E, wsum, [&](int e) { return cnt[e]; },
+        [&](int e, int excl) {
+          b.offsets[e] = excl;
+          cnt[e] = excl;  // becomes the scatter cursor
+        });
+    if (threadIdx.x == 0) b.offsets[E] = total;
+  } else {
+    // offsets and tile starts in one scan; each expert's tile entries, and the padding of
+    // its last tile, written by its thread
+    const int2 total = block_exclusive_scan2<NT>(
+        E, wsum,
+        [&](int e) { return make_int2(cnt[e], (cnt[e] + kTilePairs - 1) / kTilePairs); },
+        [&](int e, int start, int tstart, int n, int nt) {
+          b.offsets[e] = start;
+          cnt[e] = start;  // becomes the scatter cursor
+          t0[e] = tstart;
+          for (int t = 0; t < nt; ++t) {
+            const int m = n - t * kTilePairs < kTilePairs ? n - t * kTilePairs : kTilePairs;
+            b.tiles[tstart + t] = make_int4(e, start + t * kTilePairs, m, 0);
+          }
+          for (int j = n; j < nt * kTilePairs; ++j)
+            b.tile_rows[tstart * kTilePairs + j] = b.zero_row;
+        });
+    if (threadIdx.x == 0) {
+      b.offsets[E] = total.x;
+      *b.ntiles = total.y;
+    }
+  }
   __syncthreads();
   for (int64_t p = threadIdx.x; p < b.P; p += NT) {
     const int e = b.ids[p];
     if (e >= 0 && e < E) {
       const int pos = atomicAdd(&cnt[e], 1);
       b.order[pos] = static_cast<int32_t>(p);
+      // pair j of expert e is pair j % 16 of its tile j / 16
+      if (b.tiles) b.tile_rows[t0[e] * kTilePairs + (pos - b.offsets[e])] = static_cast<int32_t>(p);
     }
   }
-  if (!b.tiles) return;
-  // cnt[e] is now the end of expert e's pairs (the start of expert e + 1's)
-  __syncthreads();
-  auto pairs_of = [&](int e) { return cnt[e] - (e > 0 ? cnt[e - 1] : 0); };
-  const int nt = block_exclusive_scan<NT>(
-      E, wsum, [&](int e) { return (pairs_of(e) + kTilePairs - 1) / kTilePairs; },
-      [&](int e, int t0) {
-        const int start = e > 0 ? cnt[e - 1] : 0, n = pairs_of(e);
-        for (int t = 0; t * kTilePairs < n; ++t) {
-          const int first = start + t * kTilePairs;
-          const int m = n - t * kTilePairs < kTilePairs ? n - t * kTilePairs : kTilePairs;
-          b.tiles[t0 + t] = make_int4(e, first, m, 0);
-          for (int j = 0; j < kTilePairs; ++j)
-            b.tile_rows[(t0 + t) * kTilePairs + j] = j < m ? b.order[first + j] : b.zero_row;
-        }
-      });
-  if (threadIdx.x == 0) *b.ntiles = nt;
 }
 
 }  // namespace tq

@@ -18,18 +18,27 @@ hipError_t launch_rot16(const void* x, int xdt, const int32_t* rows, int64_t nro
   p.lk = lk;
   p.inv_sqrt_k = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(w.K)));
   if (bucket) p.bucket = *bucket;
-  const size_t lds = rot16_lds_bytes(w.K, bucket ? bucket->E : 0);
+  const size_t lds =
+      rot16_lds_bytes(w.K, bucket ? bucket->E * (bucket->tiles ? 2 : 1) : 0);
   const dim3 grid(static_cast<unsigned>(total < 65536 ? total : 65536),
                   static_cast<unsigned>((total + 65535) / 65536));
   // short rows take one wave each, unless the launch also sorts pairs (that workgroup
   // wants the full width)
+  void (*kern)(Rot16Params) = nullptr;
+  unsigned nt = kRotThreads;
   if (w.K <= kRotShortK && !bucket) {
-    if (xdt == 0) hipLaunchKernelGGL((k_rot16<true, 64, kRotShortK>), grid, dim3(64), lds, s, p);
-    else hipLaunchKernelGGL((k_rot16<false, 64, kRotShortK>), grid, dim3(64), lds, s, p);
+    kern = xdt == 0 ? k_rot16<true, 64, kRotShortK> : k_rot16<false, 64, kRotShortK>;
+    nt = 64;
   } else {
-    if (xdt == 0) hipLaunchKernelGGL((k_rot16<true, kRotThreads, kMaxK>), grid, dim3(kRotThreads), lds, s, p);
-    else hipLaunchKernelGGL((k_rot16<false, kRotThreads, kMaxK>), grid, dim3(kRotThreads), lds, s, p);
+    kern = xdt == 0 ? k_rot16<true, kRotThreads, kMaxK> : k_rot16<false, kRotThreads, kMaxK>;
   }
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, grid, dim3(nt), lds, s, p);
   return hipGetLastError();
 }
 

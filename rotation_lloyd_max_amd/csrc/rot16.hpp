@@ -38,14 +38,18 @@ __global__ __launch_bounds__(NT) void k_rot16(Rot16Params p) {
   uint32_t* xh = smem_r;                                     // Q * 20 words
   float* xf = reinterpret_cast<float*>(xh + Q * (kChunkHalves / 2));
   float* red = xf + padded_len(p.K);
-  const int64_t r = blockIdx.x + static_cast<int64_t>(blockIdx.y) * gridDim.x;
-  if (r >= p.nrows + p.zero_rows) {  // uniform per workgroup
-    if (r == p.nrows + p.zero_rows && p.bucket.ids) {
+  // with pairs to sort, workgroup 0 sorts them (dispatched first, it runs beside the
+  // rotations) and row r is workgroup r + 1
+  int64_t r = blockIdx.x + static_cast<int64_t>(blockIdx.y) * gridDim.x;
+  if (p.bucket.ids) {
+    if (r == 0) {  // uniform per workgroup
       int32_t* cnt = reinterpret_cast<int32_t*>(smem_r);
-      bucket_pairs<NT>(p.bucket, cnt, cnt + p.bucket.E);
+      bucket_pairs<NT>(p.bucket, cnt, cnt + (p.bucket.tiles ? 2 : 1) * p.bucket.E);
+      return;
     }
-    return;
+    --r;
   }
+  if (r >= p.nrows + p.zero_rows) return;  // uniform per workgroup
   if (r >= p.nrows) {
     uint4* dst = reinterpret_cast<uint4*>(p.out + r * rot16_row_halves(p.K));
     for (int i = threadIdx.x; i < Q * 4; i += NT) dst[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -71,11 +75,12 @@ __global__ __launch_bounds__(NT) void k_rot16(Rot16Params p) {
 // K up to this many elements take one wave per row
 constexpr int kRotShortK = 2048;
 
-inline size_t rot16_lds_bytes(int K, int bucket_experts) {
+// bucket_words: LDS words of the pair sort (0: none)
+inline size_t rot16_lds_bytes(int K, int bucket_words) {
   const int Q = (K + 31) / 32;
   const size_t rot = static_cast<size_t>(Q) * kChunkHalves * 2 + padded_len(K) * 4 +
                      (kRotThreads / 64) * 4 + 16;
-  const size_t bkt = static_cast<size_t>(bucket_experts + kRotThreads / 64) * 4;
+  const size_t bkt = bucket_words > 0 ? static_cast<size_t>(bucket_words + 2 * (kRotThreads / 64)) * 4 : 0;
   return rot > bkt ? rot : bkt;
 }
 
