@@ -12,6 +12,7 @@
 //              time with v_mfma_f32_16x16x32_f16, so every code word is read from memory
 //              and decoded once per 16 pairs, whatever the number of pairs.
 #include <mutex>
+#include <type_traits>
 
 #include "internal.hpp"
 #include "mfma_decode.hpp"
@@ -534,6 +535,94 @@ __device__ __forceinline__ void mt_request_part(const MtReq<LG>& d, const MtPara
                              lane);
 }
 
+// The 16-byte layout (groups of 16, rows of scales a multiple of 16 bytes, N * wpr a
+// multiple of 4, 16-byte aligned arrays): a chunk's code words come as 7 aligned 16-byte
+// units per row from the aligned word at or below the row's first word of the chunk (the
+// row's word r * wpr mod 4 is its shift inside the units; LDS rows of 28 words), its
+// scales as 5 aligned units from the aligned group at or below its first group (LDS rows of
+// 40 halves). 896 code units and 640 scale units: waves 0..5 load two code units and one
+// scale unit per lane, waves 6 and 7 one and two, so every wave issues 5 loads per chunk
+// (with its two input units). Units never cross the end of the arrays (their ends are
+// 16-byte aligned); units past a row's data hold the next row's (never decoded values
+// past K, whose inputs are zero).
+constexpr int kMt4CU = 7;   // code units per row and chunk
+constexpr int kMt4SU = 5;   // scale units per row and chunk
+constexpr int kMt4NDMA = 5;
+struct MtReq4 {
+  const uint32_t* codes;
+  const uint16_t* scales;
+  uint32_t clim, slim;  // last 16-byte unit inside each array, from `codes` / `scales`
+  int in[2];
+  uint32_t zoff[2];     // byte offset of the all-zero row from each slot's row
+  uint32_t cofs[2];     // byte offset of the thread's code units in chunk 0
+  uint32_t sofs[2];     // ... and of its scale units
+};
+
+__device__ __forceinline__ void mt_request_item4(MtReq4& d, const MtParams& p, int e, int in0,
+                                                 int in1, int row0, int wave, int lane) {
+  d.codes = p.codes + static_cast<int64_t>(e) * p.N * p.wpr;
+  d.scales = p.scales + static_cast<int64_t>(e) * p.N * p.ngk;
+  const int64_t cl = static_cast<int64_t>(p.E - e) * p.N * p.wpr * 4 - 16;
+  const int64_t sl = static_cast<int64_t>(p.E - e) * p.N * p.ngk * 2 - 16;
+  d.clim = cl < 0xfffffff0ll ? static_cast<uint32_t>(cl) : 0xfffffff0u;
+  d.slim = sl < 0xfffffff0ll ? static_cast<uint32_t>(sl) : 0xfffffff0u;
+  d.in[0] = in0;
+  d.in[1] = in1;
+  d.zoff[0] = static_cast<uint32_t>((p.zero_row - in0) * p.rowh) * 2u;
+  d.zoff[1] = static_cast<uint32_t>((p.zero_row - in1) * p.rowh) * 2u;
+  // code unit u = row u / 7, unit u % 7; units 0..511 by every wave, 512..895 by waves 0..5
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int u = j * kMgThreads + wave * 64 + lane;
+    const int r = u / kMt4CU, q = u - r * kMt4CU;
+    int row = row0 + (r < 128 ? r : 127);
+    row = row < p.N ? row : p.N - 1;
+    d.cofs[j] = (__umul24(static_cast<uint32_t>(row), static_cast<uint32_t>(p.wpr)) & ~3u) * 4u +
+                static_cast<uint32_t>(q) * 16u;
+  }
+  // scale unit u = row u / 5, unit u % 5; units 0..511 by every wave, 512..639 by waves 6, 7
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int u = j * kMgThreads + (j ? wave - 6 : wave) * 64 + lane;
+    const int r = u / kMt4SU, q = u - r * kMt4SU;
+    int row = row0 + (r < 128 ? r : 127);
+    row = row < p.N ? row : p.N - 1;
+    d.sofs[j] = __umul24(static_cast<uint32_t>(row), static_cast<uint32_t>(p.ngk) * 2u) +
+                static_cast<uint32_t>(q) * 16u;
+  }
+}
+
+// Part PART (of three) of the 16-byte loads of chunk c: code units and the wave's second
+// unit (code or scale), the first scale unit, the inputs.
+template <int PART>
+__device__ __forceinline__ void mt_request4_part(const MtReq4& d, const MtParams& p, int c,
+                                                 uint32_t* lcw, uint32_t* lsw, u32x4_t* law,
+                                                 int wave, int lane) {
+  const uint32_t cadd = static_cast<uint32_t>(c * kMtWPC) * 4u;            // 24 c words
+  const uint32_t sadd = static_cast<uint32_t>((c * kMtKC) >> 4) * 2u & ~15u;  // group 30 c
+  if constexpr (PART == 0) {
+    uint32_t off = d.cofs[0] + cadd;
+    mt_dma16(d.codes, off < d.clim ? off : d.clim, lcw + wave * 256);
+    if (wave < 6) {
+      off = d.cofs[1] + cadd;
+      mt_dma16(d.codes, off < d.clim ? off : d.clim, lcw + (kMgThreads + wave * 64) * 4);
+    } else {
+      off = d.sofs[1] + sadd;
+      mt_dma16(d.scales, off < d.slim ? off : d.slim, lsw + (kMgThreads + (wave - 6) * 64) * 4);
+    }
+  } else if constexpr (PART == 1) {
+    const uint32_t off = d.sofs[0] + sadd;
+    mt_dma16(d.scales, off < d.slim ? off : d.slim, lsw + wave * 256);
+  } else {
+    const int e = c * kMtKC + 8 * lane;
+    const bool ok = lane < kMtUnits && e < p.K;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+      mt_dma16(p.xh + static_cast<int64_t>(d.in[jj]) * p.rowh,
+               ok ? static_cast<uint32_t>(e) * 2u : d.zoff[jj], law + (2 * wave + jj) * kMtAST);
+  }
+}
+
 // Super-block SB of a chunk.
 template <int LG, int SB>
 __device__ __forceinline__ void mt_decode_sb(f32x4_t& acc, int kr, const uint32_t* cw,
@@ -582,18 +671,21 @@ __device__ __forceinline__ void mt_decode_sbs(f32x4_t& acc, int kr, const uint32
 }
 
 // Decode chunk c from one stage into the lane's accumulator.
-template <int LG, typename After>
+template <int LG, bool X4, typename After>
 __device__ __forceinline__ void mt_decode(f32x4_t& acc, const MtParams& p, int c,
                                           const uint32_t* lcr, const uint32_t* lsr,
                                           const u32x4_t* lar, const uint32_t* lut, uint32_t slot,
-                                          int nrow, int g, int col, After after) {
+                                          int nrow, int cshift, int g, int col, After after) {
   using SC = MtScales<LG>;
   const int kc0 = c * kMtKC;
   const int nsb = (p.K - kc0 + 159) / 160 < kMtSB ? (p.K - kc0 + 159) / 160 : kMtSB;
   const int g0 = kc0 >> LG;
-  const uint32_t* cw = lcr + nrow * kMtCST + 2 * g;
-  // half index of group gi of this row: (gi - g0) + (g0 & 1)
-  const uint16_t* sw = reinterpret_cast<const uint16_t*>(lsr) + nrow * (2 * SC::SST) + (g0 & 1);
+  // code words of this row (after the row's shift in the 16-byte layout); half index of
+  // group gi of this row: (gi - g0) + the window's offset (g0 mod 8 in 16-byte units,
+  // g0 mod 2 in 4-byte pairs)
+  const uint32_t* cw = X4 ? lcr + nrow * (4 * kMt4CU) + cshift + 2 * g : lcr + nrow * kMtCST + 2 * g;
+  const uint16_t* sw = X4 ? reinterpret_cast<const uint16_t*>(lsr) + nrow * (8 * kMt4SU) + (g0 & 7)
+                          : reinterpret_cast<const uint16_t*>(lsr) + nrow * (2 * SC::SST) + (g0 & 1);
   const u32x4_t* aw = lar + col * kMtAST + 5 * g;
   const int kr = kc0 - (g0 << LG);  // chunk start within its group
   // a full chunk as one block of straight-line code (the scheduler can then overlap the
@@ -620,13 +712,17 @@ __device__ __forceinline__ void mt_decode(f32x4_t& acc, const MtParams& p, int c
 // barrier's wait covers them; both sides then read the items from LDS. Item 0's expert and
 // pair rows for the first requests come from scalar loads.
 constexpr int kMtInfo = kTilePairs + 4;  // LDS words per item: pair rows, tile entry
-template <int LG>
+template <int LG, bool X4>
 __global__ __launch_bounds__(kMgThreads) void k_mgt(MtParams p, const int4* __restrict__ tiles,
                                                     const int32_t* __restrict__ tile_rows,
                                                     const int32_t* __restrict__ ntiles,
                                                     const float* __restrict__ xs) {
   using SC = MtScales<LG>;
-  constexpr int CS = kMtCW * kMgThreads, SS = SC::SW * kMgThreads, AS = kTilePairs * kMtAST;
+  static_assert(!X4 || LG == 4, "the 16-byte layout is for groups of 16");
+  constexpr int NDMA = X4 ? kMt4NDMA : SC::NDMA;  // direct loads per thread and chunk
+  constexpr int CS = X4 ? 896 * 4 : kMtCW * kMgThreads;
+  constexpr int SS = X4 ? 640 * 4 : SC::SW * kMgThreads;
+  constexpr int AS = kTilePairs * kMtAST;
   __shared__ __attribute__((aligned(16))) uint32_t lut[mlut_bytes<3>() / 4];
   __shared__ __attribute__((aligned(16))) uint32_t lc0[CS], lc1[CS], lc2[CS];
   __shared__ __attribute__((aligned(16))) uint32_t ls0[SS], ls1[SS], ls2[SS];
@@ -674,8 +770,17 @@ __global__ __launch_bounds__(kMgThreads) void k_mgt(MtParams p, const int4* __re
   // flight on every path; requests past the last chunk repeat it into a stage that is never
   // read again. Counters move by arithmetic (a branch that picks which counter to bump turns
   // them into memory).
-  MtReq<LG> d;
+  std::conditional_t<X4, MtReq4, MtReq<LG>> d;
   int dk = 0, dc = 0;
+  auto request_item = [&](int e, int in0, int in1, int row0) __attribute__((always_inline)) {
+    if constexpr (X4) mt_request_item4(d, p, e, in0, in1, row0, wave, lane);
+    else mt_request_item<LG>(d, p, e, in0, in1, row0, tid);
+  };
+  auto request_part = [&](auto part, int c, uint32_t* lcw, uint32_t* lsw, u32x4_t* law)
+                          __attribute__((always_inline)) {
+    if constexpr (X4) mt_request4_part<decltype(part)::value>(d, p, c, lcw, lsw, law, wave, lane);
+    else mt_request_part<LG, decltype(part)::value>(d, p, c, lcw, lsw, law, wave, lane);
+  };
   // request_begin returns the chunk to request (switching items where one starts), the
   // parts go out during the decode, request_end moves on
   auto request_begin = [&]() __attribute__((always_inline)) {
@@ -683,9 +788,9 @@ __global__ __launch_bounds__(kMgThreads) void k_mgt(MtParams p, const int4* __re
       int T, row0;
       item_tile(dk, T, row0);
       const int* it = info[dk % 3];
-      mt_request_item<LG>(d, p, __builtin_amdgcn_readfirstlane(it[kTilePairs]),
-                          __builtin_amdgcn_readfirstlane(it[2 * wave]),
-                          __builtin_amdgcn_readfirstlane(it[2 * wave + 1]), row0, tid);
+      request_item(__builtin_amdgcn_readfirstlane(it[kTilePairs]),
+                   __builtin_amdgcn_readfirstlane(it[2 * wave]),
+                   __builtin_amdgcn_readfirstlane(it[2 * wave + 1]), row0);
     }
     return dk < nk ? dc : nch - 1;
   };
@@ -696,9 +801,9 @@ __global__ __launch_bounds__(kMgThreads) void k_mgt(MtParams p, const int4* __re
   };
   auto request = [&](uint32_t* lcw, uint32_t* lsw, u32x4_t* law) __attribute__((always_inline)) {
     const int c = request_begin();
-    mt_request_part<LG, 0>(d, p, c, lcw, lsw, law, wave, lane);
-    mt_request_part<LG, 1>(d, p, c, lcw, lsw, law, wave, lane);
-    mt_request_part<LG, 2>(d, p, c, lcw, lsw, law, wave, lane);
+    request_part(std::integral_constant<int, 0>{}, c, lcw, lsw, law);
+    request_part(std::integral_constant<int, 1>{}, c, lcw, lsw, law);
+    request_part(std::integral_constant<int, 2>{}, c, lcw, lsw, law);
     request_end();
   };
 
@@ -708,8 +813,8 @@ __global__ __launch_bounds__(kMgThreads) void k_mgt(MtParams p, const int4* __re
   {
     int T, row0;
     item_tile(0, T, row0);
-    mt_request_item<LG>(d, p, tiles[T].x, tile_rows[T * kTilePairs + 2 * wave],
-                        tile_rows[T * kTilePairs + 2 * wave + 1], row0, tid);
+    request_item(tiles[T].x, tile_rows[T * kTilePairs + 2 * wave],
+                 tile_rows[T * kTilePairs + 2 * wave + 1], row0);
   }
   info_req(0);
   if (nk > 1) info_req(1);
@@ -719,25 +824,33 @@ __global__ __launch_bounds__(kMgThreads) void k_mgt(MtParams p, const int4* __re
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   build_mlut<3, kMgThreads>(lut, hs);
   if (wave == 0) {
-    mt_wait_vm<2 * SC::NDMA>();
+    mt_wait_vm<2 * NDMA>();
     info_xs(0);
     if (nk > 1) info_xs(1);
   }
 
   // Decode side.
   int kk = 0, kc = 0;
+  int cshift = 0;  // this lane's row's shift inside the 16-byte code units
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   auto step = [&](uint32_t* lcw, uint32_t* lsw, u32x4_t* law, const uint32_t* lcr,
                   const uint32_t* lsr, const u32x4_t* lar) __attribute__((always_inline)) {
-    mt_sync<SC::NDMA>();
+    mt_sync<NDMA>();
+    if constexpr (X4) {
+      if (kc == 0) {
+        int T, row0;
+        item_tile(kk, T, row0);
+        const int row = row0 + nrow < p.N ? row0 + nrow : p.N - 1;
+        cshift = static_cast<int>(__umul24(static_cast<uint32_t>(row), static_cast<uint32_t>(p.wpr)) & 3u);
+      }
+    }
     if (kk + 2 < nk) {
       if (kc == 0) info_req(kk + 2);
       else if (kc == 1) info_xs(kk + 2);
     }
     const int rc = request_begin();
-    mt_decode<LG>(acc, p, kc, lcr, lsr, lar, lut, slot, nrow, g, col, [&](auto part) {
-      mt_request_part<LG, decltype(part)::value>(d, p, rc, lcw, lsw, law, wave, lane);
-    });
+    mt_decode<LG, X4>(acc, p, kc, lcr, lsr, lar, lut, slot, nrow, cshift, g, col,
+                      [&](auto part) { request_part(part, rc, lcw, lsw, law); });
     request_end();
     if (kc == nch - 1) {
       // D[4 g + r][col] = output row row0 + nrow of the tile's pair 4 g + r
@@ -859,11 +972,20 @@ hipError_t launch_multi_gather(const WeightArgs& w, const int32_t* ids, int64_t 
     if (err != hipSuccess) return err;
     const int64_t items = mg_max_tiles(w, P) * q.nblk;
     const int grid = static_cast<int>(items < ncu ? items : ncu);
-    switch (__builtin_ctz(w.group)) {
-      case 4: hipLaunchKernelGGL(k_mgt<4>, dim3(grid), dim3(kMgThreads), 0, s, q, tiles, tile_rows, ntiles, xs); break;
-      case 5: hipLaunchKernelGGL(k_mgt<5>, dim3(grid), dim3(kMgThreads), 0, s, q, tiles, tile_rows, ntiles, xs); break;
-      case 6: hipLaunchKernelGGL(k_mgt<6>, dim3(grid), dim3(kMgThreads), 0, s, q, tiles, tile_rows, ntiles, xs); break;
-      default: hipLaunchKernelGGL(k_mgt<7>, dim3(grid), dim3(kMgThreads), 0, s, q, tiles, tile_rows, ntiles, xs); break;
+    // 16-byte loads where every unit stays inside its array: groups of 16, rows of scales a
+    // multiple of 16 bytes, whole 16-byte units of codes per expert, aligned arrays
+    const bool x4 = w.group == 16 && q.ngk % 8 == 0 && (static_cast<int64_t>(w.N) * w.wpr) % 4 == 0 &&
+                    (reinterpret_cast<uintptr_t>(w.codes) & 15) == 0 &&
+                    (reinterpret_cast<uintptr_t>(w.scales) & 15) == 0;
+    if (x4) {
+      hipLaunchKernelGGL((k_mgt<4, true>), dim3(grid), dim3(kMgThreads), 0, s, q, tiles, tile_rows, ntiles, xs);
+    } else {
+      switch (__builtin_ctz(w.group)) {
+        case 4: hipLaunchKernelGGL((k_mgt<4, false>), dim3(grid), dim3(kMgThreads), 0, s, q, tiles, tile_rows, ntiles, xs); break;
+        case 5: hipLaunchKernelGGL((k_mgt<5, false>), dim3(grid), dim3(kMgThreads), 0, s, q, tiles, tile_rows, ntiles, xs); break;
+        case 6: hipLaunchKernelGGL((k_mgt<6, false>), dim3(grid), dim3(kMgThreads), 0, s, q, tiles, tile_rows, ntiles, xs); break;
+        default: hipLaunchKernelGGL((k_mgt<7, false>), dim3(grid), dim3(kMgThreads), 0, s, q, tiles, tile_rows, ntiles, xs); break;
+      }
     }
     return hipGetLastError();
   }

@@ -241,6 +241,7 @@ def test_gather_qmv_bad_id_gives_nan_rows():
 
 
 @pytest.mark.parametrize("levels,group,K,N", [(3, 16, 2048, 96), (3, 16, 768, 160),
+                                              (3, 16, 2048, 33), (3, 16, 1280, 72),
                                               (3, 32, 2560, 136), (3, 64, 1280, 64),
                                               (3, 128, 1536, 40), (3, 32, 384, 72),
                                               (16, 64, 1536, 64), (4, 32, 7168, 48),
