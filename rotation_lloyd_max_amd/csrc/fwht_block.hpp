@@ -201,13 +201,23 @@ __device__ __forceinline__ void hadamard_lds(T* buf, int nrows, int m, int P) {
 
 // Outputs of part Q of TPC parts of one column: rows a (or row pairs R) with
 // a % TPC == Q. Q is a template constant, so only this part's rows are computed. For H_28
-// TPC is 1 or 2, and part Q computes side Q.
-template <typename T, int M, int TPC, int Q, bool OUT>
-__device__ __forceinline__ void hadamard_part(T* col, int pstride, const T (&x)[M], int b,
+// TPC is 1 or 2, and part Q computes side Q. Element (a, b) goes to col[a * pstride], or
+// with OUT to half index hb + half_off(a) of the sink: for P a multiple of 32,
+// idx(a P + b) = a (P / 32) kChunkHalves + idx(b), and for P = 16 the offset of row a is
+// (a / 2) kChunkHalves + 16 (a % 2); either way a uniform value, so no per-element index
+// arithmetic (with P a template constant, PC > 0, an immediate offset).
+template <typename T, int M, int TPC, int Q, bool OUT, int PC>
+__device__ __forceinline__ void hadamard_part(T* col, int pstride, const T (&x)[M], int hb,
                                               int P, HalfSink sink) {
+  const int Pv = PC > 0 ? PC : P;
   auto put = [&](int a, T v) {
-    if constexpr (OUT) sink.put_at(HalfSink::idx(a * P + b), v);
-    else col[a * pstride] = v;
+    if constexpr (OUT) {
+      const int off = Pv == 16 ? (a >> 1) * kChunkHalves + (a & 1) * 16
+                               : a * ((Pv >> 5) * kChunkHalves);
+      sink.put_at(hb + off, v);
+    } else {
+      col[a * pstride] = v;
+    }
   };
   if constexpr (M == 28) {
     static_assert(TPC <= 2, "H_28 is split into at most two sides");
@@ -225,8 +235,9 @@ __device__ __forceinline__ void hadamard_part(T* col, int pstride, const T (&x)[
 // TPC threads per column (a power of two, the same for a whole wave when P >= 64); thread
 // part q = t / P computes the outputs of its part. All inputs are read before any output is
 // written; the function synchronizes at the end. With OUT the outputs go to the sink.
-template <typename T, int M, int TPC, int NT, bool OUT>
-__device__ __forceinline__ void hadamard_factor_split(T* buf, int P, HalfSink sink) {
+template <typename T, int M, int TPC, int NT, bool OUT, int PC = 0>
+__device__ __forceinline__ void hadamard_factor_split(T* buf, int Pr, HalfSink sink) {
+  const int P = PC > 0 ? PC : Pr;  // a template constant for the common row lengths
   // TPC == 1 loops over the columns when there are more columns than threads; with
   // TPC > 1 (P * TPC <= NT) there is one pass
   const int span = TPC == 1 ? P : NT;
@@ -245,8 +256,10 @@ __device__ __forceinline__ void hadamard_factor_split(T* buf, int P, HalfSink si
       }
       if constexpr (TPC > 1) __syncthreads();  // the other parts read the same inputs
       if (active) {
+        const int hb = HalfSink::idx(b);
         [&]<int... Q>(std::integer_sequence<int, Q...>) {
-          ((q == Q ? (hadamard_part<T, M, TPC, Q, OUT>(col, pstride, x, b, P, sink), 0) : 0), ...);
+          ((q == Q ? (hadamard_part<T, M, TPC, Q, OUT, PC>(col, pstride, x, hb, P, sink), 0) : 0),
+           ...);
         }(std::make_integer_sequence<int, TPC>{});
       }
     } else if (active) {
@@ -274,6 +287,13 @@ __device__ __forceinline__ void hadamard_factor_m(T* buf, int P, HalfSink sink) 
     return;
   }
   const int tpc = NT / P;  // 0 (more columns than threads) .. NT / 64, a power of two
+  if constexpr (M == 28 && NT == 1024) {
+    // K = 7168, the common 28-point width: every offset an immediate
+    if (P == 256) {
+      hadamard_factor_split<T, M, 2, NT, OUT, 256>(buf, P, sink);
+      return;
+    }
+  }
   if constexpr (M == 28) {
     if (tpc >= 2) hadamard_factor_split<T, M, 2, NT, OUT>(buf, P, sink);
     else hadamard_factor_split<T, M, 1, NT, OUT>(buf, P, sink);
