@@ -258,7 +258,8 @@ def bench_dense(args):
 def moe_decode_measure(steps, warmup):
     """The MoE decode layer (384 experts, hidden 7168, intermediate 2048; gate and up 2-bit
     g64, down 4-bit g64): every step routes one token to 8 experts drawn uniformly and runs
-    gather_qmv for gate, up (shared 7168-wide input) and down (2048-wide input). Steps are
+    gather_qmv_pair for gate and up (one launch: shared 7168-wide input, same ids, one
+    rotation) and gather_qmv for down (2048-wide input). Steps are
     captured 20 to a graph with 20 different routings and timed with HIP events around the
     replays. Bytes per step = the 8 routed experts' codes and scales of the three
     projections + the bf16 inputs (128,450,560 + 32,768 B). Also returns the encode rates of
@@ -286,12 +287,12 @@ def moe_decode_measure(steps, warmup):
                                      for s in range(per_graph)])).to(dev)
     x1 = torch.randn(K1, generator=wl.torch_generator(dev, c.cid, wl.T_X), device=dev).to(torch.bfloat16)
     x2 = torch.randn(K2, generator=wl.torch_generator(dev, c.cid, wl.T_XD), device=dev).to(torch.bfloat16)
-    ys = {pr.name: torch.empty((8, pr.N), dtype=torch.float32, device=dev) for pr in c.projs}
+    y_gu = torch.empty((16, c.projs[0].N), dtype=torch.float32, device=dev)  # gate; up
+    y_down = torch.empty((8, c.projs[2].N), dtype=torch.float32, device=dev)
 
     def step(s):
-        tq.gather_qmv(layer["gate"], ids[s], x1, out=ys["gate"])
-        tq.gather_qmv(layer["up"], ids[s], x1, out=ys["up"])
-        tq.gather_qmv(layer["down"], ids[s], x2, out=ys["down"])
+        tq.gather_qmv_pair(layer["gate"], layer["up"], ids[s], x1, out=y_gu)
+        tq.gather_qmv(layer["down"], ids[s], x2, out=y_down)
 
     for s in range(per_graph):
         step(s)

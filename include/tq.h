@@ -176,6 +176,20 @@ int tq_gather_qmv(const tq_qweight *w, const int32_t *ids, int32_t n, const void
                   tq_dtype x_dtype, void *y, tq_dtype y_dtype, uint32_t flags, void *ws,
                   size_t ws_bytes, void *stream);
 
+/* tq_gather_qmv of two weights that read the same token through the same routed experts,
+ * in one launch: a Mixture-of-Experts layer's gate and up projections ("Running a
+ * quantized layer", kernel table, first row: one token, shared input; both projections of
+ * an expert see that token). y[k][N] = W1_{ids[k]} R x and y[n + k][N] = W2_{ids[k]} R x
+ * for k < n; y device [2n][N]. The input is rotated once for both, so the two weights must
+ * have the same n_levels, group, K, N and E and share one rotation: the same `signs`
+ * pointer (encoded with the same seed); with TQ_X_ROTATED no signs are read. Results are
+ * those of two tq_gather_qmv calls, bit for bit. An id outside [0, E) yields NaN rows.
+ * Workspace: none. Errors: the tq_gather_qmv ones; TQ_ERR_ARG when the weights differ in
+ * format or shape, do not share their signs array, or n is above 65535. */
+int tq_gather_qmv_pair(const tq_qweight *w1, const tq_qweight *w2, const int32_t *ids,
+                       int32_t n, const void *x, tq_dtype x_dtype, void *y, tq_dtype y_dtype,
+                       uint32_t flags, void *stream);
+
 /* P (input, expert) pairs, each with its own input ("Running a quantized layer", kernel
  * table, second row): y[p] = W_{ids[p]} R x[p]. x device [P][K], y device [P][N]. Pairs
  * are bucketed by expert on the device so that each W_e is streamed once; y keeps the

@@ -64,6 +64,8 @@ SIGNATURES = [
     ("tq_qmv", ctypes.c_int, [_QW, _P, ctypes.c_int, _P, ctypes.c_int, _U32, _P, _SZ, _P]),
     ("tq_gather_qmv", ctypes.c_int,
      [_QW, _P, _I32, _P, ctypes.c_int, _P, ctypes.c_int, _U32, _P, _SZ, _P]),
+    ("tq_gather_qmv_pair", ctypes.c_int,
+     [_QW, _QW, _P, _I32, _P, ctypes.c_int, _P, ctypes.c_int, _U32, _P]),
     ("tq_multi_gather_qmv", ctypes.c_int,
      [_QW, _P, _I64, _P, ctypes.c_int, _P, ctypes.c_int, _U32, _P, _SZ, _P]),
     ("tq_multi_gather_qmv_static", ctypes.c_int,
@@ -364,6 +366,25 @@ def gather_qmv(qw, ids, x, out_dtype=torch.float32, rotated=False, out=None):
     d = qw.desc()
     _check(lib().tq_gather_qmv(ctypes.byref(d), _ptr(ids), n, _ptr(x), _dt(x), _ptr(y), _dt(y),
                                X_ROTATED if rotated else 0, None, 0, _stream()))
+    return y
+
+
+def gather_qmv_pair(qw1, qw2, ids, x, out_dtype=torch.float32, rotated=False, out=None):
+    """gather_qmv of two weights sharing the routed ids and the input (gate and up of a MoE
+    layer) in one launch: [2n, N], rows n.. from qw2. The weights must be rotated alike
+    (same seed and K); the library then reads one sign array, qw1's."""
+    if qw1.seed != qw2.seed or qw1.K != qw2.K:
+        raise ValueError("gather_qmv_pair: the two weights must share seed and K")
+    x = x.contiguous()
+    ids = ids.to(torch.int32).contiguous()
+    n = ids.numel()
+    y = out if out is not None else torch.empty((2 * n, qw1.N), dtype=out_dtype, device=x.device)
+    d1 = qw1.desc()
+    d2 = qw2.desc()
+    d2.signs = d1.signs
+    _check(lib().tq_gather_qmv_pair(ctypes.byref(d1), ctypes.byref(d2), _ptr(ids), n, _ptr(x),
+                                    _dt(x), _ptr(y), _dt(y), X_ROTATED if rotated else 0,
+                                    _stream()))
     return y
 
 

@@ -70,8 +70,11 @@ hipError_t launch_encode_p2(const void* W, int wdt, int64_t rows, int K, int lev
 hipError_t launch_dequant(const WeightArgs& w, const int32_t* ids, int n, void* out, int odt,
                           hipStream_t s);
 
+// With w2 (same format, shape and experts as w, rotated alike), 2n slots: slot k < n
+// reads w at ids[k], slot n + k reads w2 at ids[k]; y holds 2n rows.
 hipError_t launch_qmv(const WeightArgs& w, const int32_t* ids, int n, const void* x, int xdt,
-                      bool x_rotated, void* y, int ydt, hipStream_t s);
+                      bool x_rotated, void* y, int ydt, hipStream_t s,
+                      const WeightArgs* w2 = nullptr);
 
 // Rotate nrows input rows (input row rows[r], or r when rows is null) into fp16 rows in
 // the layout of rot16.hpp, then write zero_rows rows of zeros after them; with a bucket job

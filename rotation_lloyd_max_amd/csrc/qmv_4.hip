@@ -3,6 +3,6 @@
 
 namespace tq {
 
-template hipError_t launch_qmv_l<4>(QmvParams& p, int n_slots, hipStream_t s);
+template hipError_t launch_qmv_l<4>(QmvParams& p, int n_slots, int n_weights, hipStream_t s);
 
 }  // namespace tq

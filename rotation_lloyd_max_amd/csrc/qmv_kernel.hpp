@@ -13,9 +13,9 @@
 // "row set" of KS waves, and the lanes of a wave take fixed chunk positions of their
 // slice (at most two per lane), so every lane keeps the rotated input of its chunks in
 // registers for all rows. Grid row y = routed slot (its expert id is uniform in the
-// workgroup); grid columns loop over groups of rows, keeping D groups of code and scale
-// loads in flight per wave (a ring of register sets), the first D - 1 of them issued
-// before the input rotation.
+// workgroup), grid layer z = the weight (two for gate and up in one launch); grid columns
+// loop over groups of rows, keeping D groups of code and scale loads in flight per wave (a
+// ring of register sets), the first D - 1 of them issued before the input rotation.
 //
 // Codes are decoded through LDS tables into fp16 centroid pairs (qmv_decode.hpp) and
 // multiplied with v_dot2 (fp32 accumulate); each group's partial sum is multiplied by its
@@ -59,6 +59,10 @@ struct QmvParams {
   int mrot;       // rotate on the matrix cores (K = 4096, 16-bit input, bit formats)
   float inv_sqrt_k;
   CodebookArgs cb;
+  // the second weight of a two-weight launch (grid.z = 2; same format, shape and experts):
+  // a MoE layer's gate and up projections, read by the workgroups with blockIdx.z = 1
+  const uint32_t* codes2;
+  const uint16_t* scales2;
 };
 
 // fp32 words of the kernel's row buffer: the padded row, or (rotation on the matrix cores)
@@ -243,6 +247,10 @@ __global__ __launch_bounds__(kQmvThreads) void k_qmv(QmvParams p) {
   }
   const int ngroups_k = p.K / p.group;
   const int slot = blockIdx.y;
+  // the second weight (its outputs follow the first's); two-weight launches use the ring
+  // kernels (D > 1), so the one-group kernel keeps its first loads free of the choice
+  const bool second = D > 1 && blockIdx.z != 0;
+  const int64_t orow = D > 1 ? static_cast<int64_t>(blockIdx.z) * gridDim.y + slot : slot;
   const bool last_lane = seg_sum_lane(ln.c0, p.lpr_log);
 
   // Loads, in this order: input row and sign words, expert id (a dense layer reads none),
@@ -254,8 +262,8 @@ __global__ __launch_bounds__(kQmvThreads) void k_qmv(QmvParams p) {
   if (p.ids) e = p.ids[slot];
   const bool bad = e < 0 || e >= p.E;
   const int64_t ebase = static_cast<int64_t>(bad ? 0 : e) * p.N;
-  const uint32_t* cexp = p.codes + ebase * p.wpr;
-  const uint16_t* sexp = p.scales + ebase * ngroups_k;
+  const uint32_t* cexp = (second ? p.codes2 : p.codes) + ebase * p.wpr;
+  const uint16_t* sexp = (second ? p.scales2 : p.scales) + ebase * ngroups_k;
 
   const int grp0 = blockIdx.x, stride = gridDim.x;
   GroupRegs<L, CPL> buf[D];
@@ -291,7 +299,7 @@ __global__ __launch_bounds__(kQmvThreads) void k_qmv(QmvParams p) {
       // a whole row per lane segment and no loads left: its last lane stores the result
       const int n = grp0 * ln.rows_per_group + rloc;
       if (last_lane && n < p.N)
-        store_any(p.y, p.ydt, static_cast<int64_t>(slot) * p.N + n, bad ? nan : v * out_scale);
+        store_any(p.y, p.ydt, orow * p.N + n, bad ? nan : v * out_scale);
       return;
     }
     if (last_lane) rowpart[rloc * KS + ln.ks] = v;
@@ -327,7 +335,7 @@ done:
     float v = 0.f;
     for (int k = 0; k < KS; ++k) v += rowpart[i * KS + k];
     if (n < p.N)
-      store_any(p.y, p.ydt, static_cast<int64_t>(slot) * p.N + n, bad ? nan : v * out_scale);
+      store_any(p.y, p.ydt, orow * p.N + n, bad ? nan : v * out_scale);
   }
 }
 
@@ -370,7 +378,7 @@ static const void* pick_kernel(bool g16, bool x32, int depth) {
 }
 
 template <int L>
-hipError_t launch_qmv_l(QmvParams& p, int n_slots, hipStream_t s) {
+hipError_t launch_qmv_l(QmvParams& p, int n_slots, int n_weights, hipStream_t s) {
   using F = Fmt<L>;
   p.Q = (p.wpr + F::cw - 1) / F::cw;
   p.lk = pow2_ceil_log(p.K);
@@ -388,7 +396,8 @@ hipError_t launch_qmv_l(QmvParams& p, int n_slots, hipStream_t s) {
   p.ngroups = (p.N + rows_per_group - 1) / rows_per_group;
 
   // one workgroup per compute unit in total, each looping over its row groups
-  int per_slot = (256 + n_slots - 1) / n_slots;
+  const int jobs = n_slots * n_weights;
+  int per_slot = (256 + jobs - 1) / jobs;
   if (per_slot > p.ngroups) per_slot = p.ngroups;
   if (per_slot < 1) per_slot = 1;
   int iters = (p.ngroups + per_slot - 1) / per_slot;
@@ -402,8 +411,9 @@ hipError_t launch_qmv_l(QmvParams& p, int n_slots, hipStream_t s) {
     }
   }
   p.max_iters = iters;
-  // one group per workgroup: no ring (depth 1, lookups overlap the rotation)
-  const int depth = iters <= 1 ? 1 : iters <= 2 ? 2 : iters <= 4 ? 4 : 8;
+  // one group per workgroup: no ring (depth 1, lookups overlap the rotation); a two-weight
+  // launch always takes a ring kernel
+  const int depth = iters <= 1 && n_weights == 1 ? 1 : iters <= 2 ? 2 : iters <= 4 ? 4 : 8;
   const bool g16 = (L != 3) && p.group == 16;
   const bool x32 = p.xdt == 0;
   const void* kern = cpl <= 1 ? pick_kernel<L, 1>(g16, x32, depth)
@@ -419,7 +429,7 @@ hipError_t launch_qmv_l(QmvParams& p, int n_slots, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(reinterpret_cast<void (*)(QmvParams)>(const_cast<void*>(kern)),
-                     dim3(per_slot, n_slots), dim3(kQmvThreads), lds, s, p);
+                     dim3(per_slot, n_slots, n_weights), dim3(kQmvThreads), lds, s, p);
   return hipGetLastError();
 }
 

@@ -229,6 +229,50 @@ def test_gather_qmv(levels, group, K, N):
     assert torch.equal(y0, y[0]) and torch.equal(y0, y[3])
 
 
+@pytest.mark.parametrize("levels,group,K,N,xdt,rotated",
+                         [(4, 64, 7168, 96, torch.bfloat16, False), (3, 16, 768, 64, torch.float16, False),
+                          (8, 128, 4096, 40, torch.bfloat16, False), (16, 64, 2048, 72, torch.float32, True)])
+def test_gather_qmv_pair(levels, group, K, N, xdt, rotated):
+    # gate and up in one launch: rows k from the first weight, rows n + k from the second,
+    # each equal to its own gather_qmv call bit for bit and to the oracle within the bound
+    E = 7
+    g1, _ = make_experts(930, E, N, K, levels, group, seed=5)
+    W2 = torch.stack([to_dev(wl.student_rows(wl.rng(931, 20, e), N, K), torch.bfloat16)
+                      for e in range(E)])
+    g2, _ = encode_both(W2, levels, group, 5)
+    ids_np = np.array([6, 0, 3, 3, E, 2, -2, 5], dtype=np.int32)
+    ids = torch.from_numpy(ids_np).cuda()
+    x0 = wl.gaussian(wl.rng(930, 1), 1, K)[0]
+    if rotated:
+        # the oracle rotates the original input; the kernel takes R x in fp32
+        xf = x0.astype(np.float64)
+        x = torch.from_numpy(ohd.rotate(xf, 5).astype(np.float32)).cuda()
+        extra = 1e-6
+    else:
+        x = to_dev(x0, xdt)
+        xf = as_f64(x)
+        extra = 0.0
+    y = tq.gather_qmv_pair(g1, g2, ids, x, rotated=rotated)
+    y1 = tq.gather_qmv(g1, ids, x, rotated=rotated)
+    y2 = tq.gather_qmv(g2, ids, x, rotated=rotated)
+    torch.cuda.synchronize()
+    n = len(ids_np)
+    assert y.shape == (2 * n, N)
+    assert torch.equal(torch.nan_to_num(y[:n], nan=7.0), torch.nan_to_num(y1, nan=7.0))
+    assert torch.equal(torch.nan_to_num(y[n:], nan=7.0), torch.nan_to_num(y2, nan=7.0))
+    yg = as_f64(y)
+    for half, qw in ((0, g1), (1, g2)):
+        codes, scales = gpu_arrays(qw)
+        for k, e in enumerate(ids_np):
+            row = yg[half * n + k]
+            if 0 <= e < E:
+                want, bound = qmv_reference(codes[e], scales[e], levels, group, K, 5, xf)
+                check_outputs(row, want, bound + extra * np.abs(want),
+                              f"weight {half} slot {k} expert {e}")
+            else:
+                assert np.all(np.isnan(row)), (half, k)
+
+
 def test_gather_qmv_bad_id_gives_nan_rows():
     K, N, levels, group = 512, 40, 16, 64
     qw, _ = make_experts(915, 3, N, K, levels, group, seed=0)

@@ -35,7 +35,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     handle = ctypes.CDLL(tq.LIB_PATH)
     for n in names:
         assert hasattr(handle, n), n
@@ -199,6 +199,33 @@ def test_validation_statuses():
     # workspace query with a bad descriptor
     assert L.tq_workspace_bytes(3, None, 1, 0) == ctypes.c_size_t(-1).value
     assert L.tq_workspace_bytes(9, ctypes.byref(desc()), 1, 0) == ctypes.c_size_t(-1).value
+
+
+def test_gather_qmv_pair_validation():
+    # the two weights must match in format and shape and share one signs array; every
+    # rejection happens before a launch
+    L = tq.lib()
+
+    def pair(d1, d2, n=4, ids=16, flags=0):
+        return L.tq_gather_qmv_pair(ctypes.byref(d1), ctypes.byref(d2), ids, n, 16, 1, 16, 0,
+                                    flags, None)
+
+    a = desc(E=3)
+    assert pair(a, desc(E=3, n_levels=8)) == ERR_ARG
+    assert pair(a, desc(E=3, group=128)) == ERR_ARG
+    assert pair(a, desc(E=3, N=8)) == ERR_ARG
+    assert pair(a, desc(E=4)) == ERR_ARG
+    assert pair(a, desc(E=3, K=1024)) == ERR_ARG
+    assert pair(a, desc(E=3, signs=32)) == ERR_ARG       # a second rotation
+    assert pair(a, desc(E=3), n=65536) == ERR_ARG        # past the grid's y limit
+    assert pair(a, desc(E=3), n=-1) == ERR_ARG
+    assert pair(a, desc(E=3), ids=0) == ERR_ARG
+    assert pair(a, desc(E=3), ids=18) == ERR_ALIGN
+    assert pair(a, desc(E=3, codes=8)) == ERR_ALIGN
+    assert L.tq_gather_qmv_pair(None, ctypes.byref(a), 16, 4, 16, 1, 16, 0, 0, None) == ERR_ARG
+    # zero ids: nothing to do; a pre-rotated input reads no signs, so they need not match
+    assert pair(a, desc(E=3), n=0, ids=0) == 0
+    assert pair(desc(E=3, N=0, signs=0), desc(E=3, N=0, signs=16), n=4, flags=1) == 0
 
 
 def test_empty_calls_are_no_ops():
