@@ -412,20 +412,20 @@ def bench_moe(args):
         ids = torch.from_numpy(ids_np).to(dev)
         Kg, Kd = c.projs[0].K, c.projs[2].K
         g = wl.torch_generator(dev, c.cid, wl.T_X)
+        # a pair's input is its token's row, read by gate and up; down reads its own rows
         xg = torch.randn((P, Kg), generator=g, device=dev).to(torch.bfloat16)
-        xu = torch.randn((P, Kg), generator=g, device=dev).to(torch.bfloat16)
         xd = torch.randn((P, Kd), generator=g, device=dev).to(torch.bfloat16)
-        ys = {pr.name: torch.empty((P, pr.N), dtype=torch.float32, device=dev) for pr in c.projs}
+        y_gu = torch.empty((2 * P, c.projs[0].N), dtype=torch.float32, device=dev)  # gate; up
+        y_d = torch.empty((P, c.projs[2].N), dtype=torch.float32, device=dev)
         wss = {pr.name: torch.empty((tq.workspace_bytes(tq.OP_MULTI_GATHER_QMV, layers[0][pr.name], P) + 7) // 8,
                                     dtype=torch.int64, device=dev) for pr in c.projs}
 
         def step(s):
             L = layers[s % ncopy]
-            tq.multi_gather_qmv(L["gate"], ids, xg, out=ys["gate"], ws=wss["gate"])
-            tq.multi_gather_qmv(L["up"], ids, xu, out=ys["up"], ws=wss["up"])
-            tq.multi_gather_qmv(L["down"], ids, xd, out=ys["down"], ws=wss["down"])
+            tq.multi_gather_qmv_pair(L["gate"], L["up"], ids, xg, out=y_gu, ws=wss["gate"])
+            tq.multi_gather_qmv(L["down"], ids, xd, out=y_d, ws=wss["down"])
         touched = len(np.unique(ids_np))
-        bytes_step = touched * sum(wbytes.values()) + (xg.numel() + xu.numel() + xd.numel()) * 2
+        bytes_step = touched * sum(wbytes.values()) + (xg.numel() + xd.numel()) * 2
         unit, metric = "GB/s", "multi_gather_qmv HBM GB/s (ternary MoE prefill: gate+up+down)"
     else:
         T, k = 4096, 8

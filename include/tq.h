@@ -198,6 +198,22 @@ int tq_multi_gather_qmv(const tq_qweight *w, const int32_t *ids, int64_t P, cons
                         tq_dtype x_dtype, void *y, tq_dtype y_dtype, uint32_t flags, void *ws,
                         size_t ws_bytes, void *stream);
 
+/* tq_multi_gather_qmv of two weights over the same pairs, in one call: a Mixture-of-Experts
+ * layer's gate and up projections, which read each token's input through the same routed
+ * experts ("Running a quantized layer", kernel table, second row: per-expert inputs).
+ * y[p][N] = W1_{ids[p]} R x[p] and y[P + p][N] = W2_{ids[p]} R x[p]; y device [2P][N].
+ * The inputs are rotated and the pairs bucketed once for both weights, and the trit kernel
+ * takes the row blocks of both in one launch. The weights must have the same n_levels,
+ * group, K, N and E and share one `signs` array (with TQ_X_ROTATED none is read). Results
+ * are those of two tq_multi_gather_qmv calls, bit for bit; a pair with an id outside
+ * [0, E) gets NaN rows in both halves. Workspace: tq_workspace_bytes(TQ_OP_MULTI_GATHER_QMV,
+ * w1, P, 0) bytes, 16-byte aligned. Errors: the tq_multi_gather_qmv ones; TQ_ERR_ARG when
+ * the weights differ in format or shape or do not share their signs array, or P > 2^29. */
+int tq_multi_gather_qmv_pair(const tq_qweight *w1, const tq_qweight *w2, const int32_t *ids,
+                             int64_t P, const void *x, tq_dtype x_dtype, void *y,
+                             tq_dtype y_dtype, uint32_t flags, void *ws, size_t ws_bytes,
+                             void *stream);
+
 /* tq_multi_gather_qmv with no workspace argument and no allocation of any kind, for
  * callers that cannot allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc). Its workspace is one fixed array of 8 MiB per GPU,

@@ -68,6 +68,8 @@ SIGNATURES = [
      [_QW, _QW, _P, _I32, _P, ctypes.c_int, _P, ctypes.c_int, _U32, _P]),
     ("tq_multi_gather_qmv", ctypes.c_int,
      [_QW, _P, _I64, _P, ctypes.c_int, _P, ctypes.c_int, _U32, _P, _SZ, _P]),
+    ("tq_multi_gather_qmv_pair", ctypes.c_int,
+     [_QW, _QW, _P, _I64, _P, ctypes.c_int, _P, ctypes.c_int, _U32, _P, _SZ, _P]),
     ("tq_multi_gather_qmv_static", ctypes.c_int,
      [_QW, _P, _I64, _P, ctypes.c_int, _P, ctypes.c_int, _U32, _P]),
     ("tq_gather_qmm", ctypes.c_int,
@@ -400,6 +402,30 @@ def multi_gather_qmv(qw, ids, X, out_dtype=torch.float32, rotated=False, out=Non
     _check(lib().tq_multi_gather_qmv(ctypes.byref(d), _ptr(ids), P, _ptr(X), _dt(X), _ptr(y),
                                      _dt(y), X_ROTATED if rotated else 0, _ptr(ws), nbytes,
                                      _stream()))
+    return y
+
+
+def multi_gather_qmv_pair(qw1, qw2, ids, X, out_dtype=torch.float32, rotated=False, out=None,
+                          ws=None):
+    """multi_gather_qmv of two weights over the same (input, expert) pairs (gate and up of a
+    MoE layer) in one call: [2P, N], rows P.. from qw2. The weights must be rotated alike
+    (same seed and K); the library then reads one sign array, qw1's."""
+    if qw1.seed != qw2.seed or qw1.K != qw2.K:
+        raise ValueError("multi_gather_qmv_pair: the two weights must share seed and K")
+    X = X.contiguous()
+    ids = ids.to(torch.int32).contiguous()
+    P = ids.numel()
+    y = out if out is not None else torch.empty((2 * P, qw1.N), dtype=out_dtype, device=X.device)
+    nbytes = workspace_bytes(OP_MULTI_GATHER_QMV, qw1, P)
+    if ws is None:
+        ws = _workspace(nbytes, X.device)
+    d1 = qw1.desc()
+    d2 = qw2.desc()
+    d2.signs = d1.signs
+    _check(lib().tq_multi_gather_qmv_pair(ctypes.byref(d1), ctypes.byref(d2), _ptr(ids), P,
+                                          _ptr(X), _dt(X), _ptr(y), _dt(y),
+                                          X_ROTATED if rotated else 0, _ptr(ws), nbytes,
+                                          _stream()))
     return y
 
 

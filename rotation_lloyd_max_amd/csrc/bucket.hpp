@@ -25,6 +25,8 @@ struct BucketJob {
   int32_t* tile_rows;
   int32_t* ntiles;
   int32_t zero_row;
+  int nw = 1;  // weights sharing the pairs: the NaN row of a bad pair is written in each
+               // weight's rows (weight h at rows h P ..)
 };
 
 // Exclusive scan of v(e) over e < E by the whole workgroup, NT values at a time with a
@@ -107,7 +109,9 @@ __device__ __forceinline__ void bucket_pairs(const BucketJob& b, int32_t* cnt, i
     if (e >= 0 && e < E) {
       atomicAdd(&cnt[e], 1);
     } else {
-      for (int n = 0; n < b.N; ++n) store_any(b.y, b.ydt, p * b.N + n, __builtin_nanf(""));
+      for (int h = 0; h < b.nw; ++h)
+        for (int n = 0; n < b.N; ++n)
+          store_any(b.y, b.ydt, (h * b.P + p) * b.N + n, __builtin_nanf(""));
     }
   }
   __syncthreads();

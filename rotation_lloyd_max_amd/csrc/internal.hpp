@@ -88,9 +88,11 @@ size_t multi_gather_workspace(const WeightArgs& w, int64_t P);
 // device, resolved once per device).
 constexpr size_t kStaticScratchBytes = size_t(8) << 20;
 hipError_t static_scratch(void** ptr);
+// With w2 (same format, shape and experts as w, rotated alike): both weights over the same
+// pairs, one rotation and one bucketing; y holds 2P rows (w2's from row P).
 hipError_t launch_multi_gather(const WeightArgs& w, const int32_t* ids, int64_t P,
                                const void* x, int xdt, bool x_rotated, void* y, int ydt,
-                               void* ws, hipStream_t s);
+                               void* ws, hipStream_t s, const WeightArgs* w2 = nullptr);
 
 size_t gather_qmm_workspace(const WeightArgs& w, int64_t M, int64_t T);
 hipError_t launch_gather_qmm(const WeightArgs& w, const void* x, int xdt, int64_t T,

@@ -396,6 +396,10 @@ struct MtParams {
   int64_t rowh, zero_row;
   int K, N, E, wpr, ngk, ydt, nblk;
   CodebookArgs cb;
+  // a second weight over the same pairs (the two-weight kernels: a MoE layer's gate and
+  // up): items nitems .. 2 nitems - 1 read it and write rows P .. 2 P - 1
+  const uint32_t* codes2;
+  const uint16_t* scales2;
 };
 
 // Wait until at most N direct loads (and stores) of this wave are outstanding and its LDS
@@ -459,10 +463,10 @@ struct MtReq {
 // load depend on its index only, so per chunk every load address is one add and a clamp.
 template <int LG>
 __device__ __forceinline__ void mt_request_item(MtReq<LG>& d, const MtParams& p, int e, int in0,
-                                                int in1, int row0, int tid) {
+                                                int in1, int row0, int tid, int wsel) {
   using SC = MtScales<LG>;
-  d.codes = p.codes + static_cast<int64_t>(e) * p.N * p.wpr;
-  d.scales = p.scales + static_cast<int64_t>(e) * p.N * p.ngk;
+  d.codes = (wsel ? p.codes2 : p.codes) + static_cast<int64_t>(e) * p.N * p.wpr;
+  d.scales = (wsel ? p.scales2 : p.scales) + static_cast<int64_t>(e) * p.N * p.ngk;
   const int64_t lim = (static_cast<int64_t>(p.E - e) * p.N * p.ngk - 2) * 2;
   d.slim = lim < 0xfffffffcll ? static_cast<uint32_t>(lim) : 0xfffffffcu;
   d.in[0] = in0;
@@ -559,9 +563,9 @@ struct MtReq4 {
 };
 
 __device__ __forceinline__ void mt_request_item4(MtReq4& d, const MtParams& p, int e, int in0,
-                                                 int in1, int row0, int wave, int lane) {
-  d.codes = p.codes + static_cast<int64_t>(e) * p.N * p.wpr;
-  d.scales = p.scales + static_cast<int64_t>(e) * p.N * p.ngk;
+                                                 int in1, int row0, int wave, int lane, int wsel) {
+  d.codes = (wsel ? p.codes2 : p.codes) + static_cast<int64_t>(e) * p.N * p.wpr;
+  d.scales = (wsel ? p.scales2 : p.scales) + static_cast<int64_t>(e) * p.N * p.ngk;
   const int64_t cl = static_cast<int64_t>(p.E - e) * p.N * p.wpr * 4 - 16;
   const int64_t sl = static_cast<int64_t>(p.E - e) * p.N * p.ngk * 2 - 16;
   d.clim = cl < 0xfffffff0ll ? static_cast<uint32_t>(cl) : 0xfffffff0u;
@@ -712,7 +716,7 @@ __device__ __forceinline__ void mt_decode(f32x4_t& acc, const MtParams& p, int c
 // barrier's wait covers them; both sides then read the items from LDS. Item 0's expert and
 // pair rows for the first requests come from scalar loads.
 constexpr int kMtInfo = kTilePairs + 4;  // LDS words per item: pair rows, tile entry
-template <int LG, bool X4>
+template <int LG, bool X4, bool NW2>
 __global__ __launch_bounds__(kMgThreads) void k_mgt(MtParams p, const int4* __restrict__ tiles,
                                                     const int32_t* __restrict__ tile_rows,
                                                     const int32_t* __restrict__ ntiles,
@@ -731,7 +735,8 @@ __global__ __launch_bounds__(kMgThreads) void k_mgt(MtParams p, const int4* __re
   __shared__ __attribute__((aligned(16))) float ixs[3][kTilePairs];
   __shared__ uint16_t hs[16];
 
-  const int nitems = *ntiles * p.nblk;
+  const int nitems1 = *ntiles * p.nblk;  // items of one weight
+  const int nitems = NW2 ? 2 * nitems1 : nitems1;
   const int G = static_cast<int>(gridDim.x), w0 = static_cast<int>(blockIdx.x);
   if (w0 >= nitems) return;  // uniform
   const int nch = (p.K + kMtKC - 1) / kMtKC;  // at least 2
@@ -743,16 +748,18 @@ __global__ __launch_bounds__(kMgThreads) void k_mgt(MtParams p, const int4* __re
   const int lane = tid & 63, g = lane >> 4, col = lane & 15;
   const uint32_t slot = mlut_slot<3>(lane);
   const int nrow = wave * 16 + col;  // this lane's weight row within the block
-  auto item_tile = [&](int k, int& T, int& row0) __attribute__((always_inline)) {
-    const int i = w0 + k * G;
+  auto item_tile = [&](int k, int& T, int& row0, int& wsel) __attribute__((always_inline)) {
+    int i = w0 + k * G;
+    wsel = NW2 && i >= nitems1 ? 1 : 0;  // a constant 0 in the one-weight kernels
+    i -= wsel ? nitems1 : 0;
     T = i / p.nblk;
     row0 = (i - T * p.nblk) * 128;
   };
   // wave 0: item k's pair rows (lanes 0..15) and tile entry (lanes 16..19) into LDS ...
   auto info_req = [&](int k) __attribute__((always_inline)) {
     if (wave == 0 && lane < kMtInfo) {
-      int T, row0;
-      item_tile(k, T, row0);
+      int T, row0, wsel;
+      item_tile(k, T, row0, wsel);
       const void* a = lane < kTilePairs
                           ? static_cast<const void*>(tile_rows + T * kTilePairs + lane)
                           : static_cast<const void*>(reinterpret_cast<const int32_t*>(tiles + T) +
@@ -772,9 +779,10 @@ __global__ __launch_bounds__(kMgThreads) void k_mgt(MtParams p, const int4* __re
   // them into memory).
   std::conditional_t<X4, MtReq4, MtReq<LG>> d;
   int dk = 0, dc = 0;
-  auto request_item = [&](int e, int in0, int in1, int row0) __attribute__((always_inline)) {
-    if constexpr (X4) mt_request_item4(d, p, e, in0, in1, row0, wave, lane);
-    else mt_request_item<LG>(d, p, e, in0, in1, row0, tid);
+  auto request_item = [&](int e, int in0, int in1, int row0, int wsel)
+                          __attribute__((always_inline)) {
+    if constexpr (X4) mt_request_item4(d, p, e, in0, in1, row0, wave, lane, wsel);
+    else mt_request_item<LG>(d, p, e, in0, in1, row0, tid, wsel);
   };
   auto request_part = [&](auto part, int c, uint32_t* lcw, uint32_t* lsw, u32x4_t* law)
                           __attribute__((always_inline)) {
@@ -785,12 +793,12 @@ __global__ __launch_bounds__(kMgThreads) void k_mgt(MtParams p, const int4* __re
   // parts go out during the decode, request_end moves on
   auto request_begin = [&]() __attribute__((always_inline)) {
     if (dc == 0 && dk > 0 && dk < nk) {
-      int T, row0;
-      item_tile(dk, T, row0);
+      int T, row0, wsel;
+      item_tile(dk, T, row0, wsel);
       const int* it = info[dk % 3];
       request_item(__builtin_amdgcn_readfirstlane(it[kTilePairs]),
                    __builtin_amdgcn_readfirstlane(it[2 * wave]),
-                   __builtin_amdgcn_readfirstlane(it[2 * wave + 1]), row0);
+                   __builtin_amdgcn_readfirstlane(it[2 * wave + 1]), row0, wsel);
     }
     return dk < nk ? dc : nch - 1;
   };
@@ -811,10 +819,10 @@ __global__ __launch_bounds__(kMgThreads) void k_mgt(MtParams p, const int4* __re
   // scalar loads), the table built; wave 0 then waits for the descriptions (its oldest
   // loads) and requests the input scales.
   {
-    int T, row0;
-    item_tile(0, T, row0);
+    int T, row0, wsel;
+    item_tile(0, T, row0, wsel);
     request_item(tiles[T].x, tile_rows[T * kTilePairs + 2 * wave],
-                 tile_rows[T * kTilePairs + 2 * wave + 1], row0);
+                 tile_rows[T * kTilePairs + 2 * wave + 1], row0, wsel);
   }
   info_req(0);
   if (nk > 1) info_req(1);
@@ -838,8 +846,8 @@ __global__ __launch_bounds__(kMgThreads) void k_mgt(MtParams p, const int4* __re
     mt_sync<NDMA>();
     if constexpr (X4) {
       if (kc == 0) {
-        int T, row0;
-        item_tile(kk, T, row0);
+        int T, row0, wsel;
+        item_tile(kk, T, row0, wsel);
         const int row = row0 + nrow < p.N ? row0 + nrow : p.N - 1;
         cshift = static_cast<int>(__umul24(static_cast<uint32_t>(row), static_cast<uint32_t>(p.wpr)) & 3u);
       }
@@ -854,9 +862,10 @@ __global__ __launch_bounds__(kMgThreads) void k_mgt(MtParams p, const int4* __re
     request_end();
     if (kc == nch - 1) {
       // D[4 g + r][col] = output row row0 + nrow of the tile's pair 4 g + r
-      int T, row0;
-      item_tile(kk, T, row0);
+      int T, row0, wsel;
+      item_tile(kk, T, row0, wsel);
       const int n = row0 + nrow;
+      const int64_t ybase = wsel ? p.zero_row : 0;  // the second weight's rows follow the P first
       const int* it = info[kk % 3];
       const int cnt = it[kTilePairs + 2];
       const int4 pr = *reinterpret_cast<const int4*>(it + 4 * g);
@@ -867,7 +876,7 @@ __global__ __launch_bounds__(kMgThreads) void k_mgt(MtParams p, const int4* __re
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (4 * g + r < cnt)
-            store_any(p.y, p.ydt, static_cast<int64_t>(prs[r]) * p.N + n, acc[r] * scs[r]);
+            store_any(p.y, p.ydt, (ybase + prs[r]) * p.N + n, acc[r] * scs[r]);
       }
       acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
@@ -936,7 +945,7 @@ static hipError_t compute_units(int* n) {
 
 hipError_t launch_multi_gather(const WeightArgs& w, const int32_t* ids, int64_t P, const void* x,
                                int xdt, bool x_rotated, void* y, int ydt, void* ws,
-                               hipStream_t s) {
+                               hipStream_t s, const WeightArgs* w2) {
   if (P == 0 || w.N == 0) return hipSuccess;
   const MgLayout lay = mg_layout(w, P);
   char* base = static_cast<char*>(ws);
@@ -954,7 +963,7 @@ hipError_t launch_multi_gather(const WeightArgs& w, const int32_t* ids, int64_t 
   int32_t* ntiles = reinterpret_cast<int32_t*>(base + lay.ntiles);
   // one launch rotates every pair's input and (one extra workgroup) buckets the pairs
   BucketJob job{ids, P, w.E, offsets, order, y, ydt, w.N,
-                direct ? tiles : nullptr, tile_rows, ntiles, static_cast<int32_t>(P)};
+                direct ? tiles : nullptr, tile_rows, ntiles, static_cast<int32_t>(P), w2 ? 2 : 1};
   hipError_t err = launch_rot16(x, xdt, nullptr, P, /*zero_rows=*/1, w, x_rotated, xh, xs, &job, s);
   if (err != hipSuccess) return err;
   if (direct) {
@@ -965,28 +974,39 @@ hipError_t launch_multi_gather(const WeightArgs& w, const int32_t* ids, int64_t 
     q.K = w.K; q.N = w.N; q.E = w.E; q.wpr = w.wpr; q.ngk = w.K / w.group; q.ydt = ydt;
     q.nblk = (w.N + 127) / 128;
     q.cb = *codebook_for(w.levels);
+    q.codes2 = w2 ? w2->codes : w.codes;
+    q.scales2 = w2 ? w2->scales : w.scales;
+    const int nw = w2 ? 2 : 1;
     // one workgroup per compute unit (each holds 141 KB of LDS); the items are shared out
     // on the device, where their number is known
     int ncu = 0;
     err = compute_units(&ncu);
     if (err != hipSuccess) return err;
-    const int64_t items = mg_max_tiles(w, P) * q.nblk;
+    const int64_t items = mg_max_tiles(w, P) * q.nblk * nw;
     const int grid = static_cast<int>(items < ncu ? items : ncu);
     // 16-byte loads where every unit stays inside its array: groups of 16, rows of scales a
     // multiple of 16 bytes, whole 16-byte units of codes per expert, aligned arrays
     const bool x4 = w.group == 16 && q.ngk % 8 == 0 && (static_cast<int64_t>(w.N) * w.wpr) % 4 == 0 &&
-                    (reinterpret_cast<uintptr_t>(w.codes) & 15) == 0 &&
-                    (reinterpret_cast<uintptr_t>(w.scales) & 15) == 0;
-    if (x4) {
-      hipLaunchKernelGGL((k_mgt<4, true>), dim3(grid), dim3(kMgThreads), 0, s, q, tiles, tile_rows, ntiles, xs);
-    } else {
-      switch (__builtin_ctz(w.group)) {
-        case 4: hipLaunchKernelGGL((k_mgt<4, false>), dim3(grid), dim3(kMgThreads), 0, s, q, tiles, tile_rows, ntiles, xs); break;
-        case 5: hipLaunchKernelGGL((k_mgt<5, false>), dim3(grid), dim3(kMgThreads), 0, s, q, tiles, tile_rows, ntiles, xs); break;
-        case 6: hipLaunchKernelGGL((k_mgt<6, false>), dim3(grid), dim3(kMgThreads), 0, s, q, tiles, tile_rows, ntiles, xs); break;
-        default: hipLaunchKernelGGL((k_mgt<7, false>), dim3(grid), dim3(kMgThreads), 0, s, q, tiles, tile_rows, ntiles, xs); break;
+                    ((reinterpret_cast<uintptr_t>(w.codes) | reinterpret_cast<uintptr_t>(q.codes2)) & 15) == 0 &&
+                    ((reinterpret_cast<uintptr_t>(w.scales) | reinterpret_cast<uintptr_t>(q.scales2)) & 15) == 0;
+    const auto launch = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(kMgThreads), 0, s, q, tiles, tile_rows, ntiles, xs);
+    };
+    const auto pick = [&](auto nw2) {
+      constexpr bool N2 = decltype(nw2)::value;
+      if (x4) {
+        launch(k_mgt<4, true, N2>);
+      } else {
+        switch (__builtin_ctz(w.group)) {
+          case 4: launch(k_mgt<4, false, N2>); break;
+          case 5: launch(k_mgt<5, false, N2>); break;
+          case 6: launch(k_mgt<6, false, N2>); break;
+          default: launch(k_mgt<7, false, N2>); break;
+        }
       }
-    }
+    };
+    if (nw == 2) pick(std::true_type{});
+    else pick(std::false_type{});
     return hipGetLastError();
   }
 
@@ -1000,13 +1020,23 @@ hipError_t launch_multi_gather(const WeightArgs& w, const int32_t* ids, int64_t 
   p.ydt = ydt;
   p.cb = *codebook_for(w.levels);
   const dim3 grid((w.N + 16 * kMgWaves - 1) / (16 * kMgWaves), w.E);
-  switch (w.levels) {
-    case 16: hipLaunchKernelGGL(k_mg<16>, grid, dim3(kMgThreads), 0, s, p); break;
-    case 8: hipLaunchKernelGGL(k_mg<8>, grid, dim3(kMgThreads), 0, s, p); break;
-    case 4: hipLaunchKernelGGL(k_mg<4>, grid, dim3(kMgThreads), 0, s, p); break;
-    default: hipLaunchKernelGGL(k_mg<3>, grid, dim3(kMgThreads), 0, s, p); break;
+  // with a second weight: a second launch over the same rotated inputs and buckets
+  for (int h = 0; h < (w2 ? 2 : 1); ++h) {
+    if (h == 1) {
+      p.codes = w2->codes;
+      p.scales = w2->scales;
+      p.y = static_cast<char*>(y) + P * w.N * (ydt == 0 ? 4 : 2);
+    }
+    switch (w.levels) {
+      case 16: hipLaunchKernelGGL(k_mg<16>, grid, dim3(kMgThreads), 0, s, p); break;
+      case 8: hipLaunchKernelGGL(k_mg<8>, grid, dim3(kMgThreads), 0, s, p); break;
+      case 4: hipLaunchKernelGGL(k_mg<4>, grid, dim3(kMgThreads), 0, s, p); break;
+      default: hipLaunchKernelGGL(k_mg<3>, grid, dim3(kMgThreads), 0, s, p); break;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace tq

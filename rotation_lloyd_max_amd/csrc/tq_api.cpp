@@ -519,6 +519,35 @@ int tq_multi_gather_qmv(const tq_qweight* w, const int32_t* ids, int64_t P, cons
                     "tq_multi_gather_qmv");
 }
 
+int tq_multi_gather_qmv_pair(const tq_qweight* w1, const tq_qweight* w2, const int32_t* ids,
+                             int64_t P, const void* x, tq_dtype x_dtype, void* y,
+                             tq_dtype y_dtype, uint32_t flags, void* ws, size_t ws_bytes,
+                             void* stream) {
+  const bool rotated = (flags & TQ_X_ROTATED) != 0;
+  WeightArgs a{}, b{};
+  int rc = check_weight(w1, &a, false, rotated);
+  if (rc != TQ_OK) return rc;
+  rc = check_weight(w2, &b, false, rotated);
+  if (rc != TQ_OK) return rc;
+  if (a.levels != b.levels || a.group != b.group || a.K != b.K || a.N != b.N || a.E != b.E)
+    return fail(TQ_ERR_ARG, "tq_multi_gather_qmv_pair: the two weights differ in format or shape");
+  if (!rotated && w1->signs != w2->signs)
+    return fail(TQ_ERR_ARG, "tq_multi_gather_qmv_pair: the two weights must share one signs array");
+  if (P < 0 || P > (1 << 29)) return fail(TQ_ERR_ARG, "P out of range");
+  if (P > 0 && !ids) return fail(TQ_ERR_ARG, "ids is NULL");
+  if (P > 0 && !aligned(ids, 4)) return fail(TQ_ERR_ALIGN, "ids misaligned");
+  rc = check_io(x, x_dtype, y, y_dtype, P > 0 && a.N > 0);
+  if (rc != TQ_OK) return rc;
+  if (P == 0 || a.N == 0) return TQ_OK;
+  const size_t need = multi_gather_workspace(a, P);
+  if (!ws || ws_bytes < need)
+    return fail(TQ_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  if (!aligned(ws, 16)) return fail(TQ_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return hip_status(launch_multi_gather(a, ids, P, x, x_dtype, rotated, y, y_dtype, ws,
+                                        static_cast<hipStream_t>(stream), &b),
+                    "tq_multi_gather_qmv_pair");
+}
+
 int tq_multi_gather_qmv_static(const tq_qweight* w, const int32_t* ids, int64_t P,
                                const void* x, tq_dtype x_dtype, void* y, tq_dtype y_dtype,
                                uint32_t flags, void* stream) {

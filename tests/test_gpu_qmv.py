@@ -310,6 +310,44 @@ def test_multi_gather(levels, group, K, N):
         check_outputs(yg[p_], want, bound, f"pair {p_} expert {e}")
 
 
+@pytest.mark.parametrize("levels,group,K,N", [(3, 16, 2048, 96), (3, 32, 1280, 136),
+                                              (3, 16, 768, 64), (16, 64, 1536, 64)])
+def test_multi_gather_pair(levels, group, K, N):
+    # gate and up over the same pairs in one call: rows p from the first weight, rows P + p
+    # from the second, each equal to its own multi_gather_qmv call bit for bit and to the
+    # oracle within the bound; bad pairs give NaN rows in both halves
+    E = 9
+    g1, _ = make_experts(932, E, N, K, levels, group, seed=2)
+    W2 = torch.stack([to_dev(wl.student_rows(wl.rng(933, 20, e), N, K), torch.bfloat16)
+                      for e in range(E)])
+    g2, _ = encode_both(W2, levels, group, 2)
+    g = wl.rng(932, 2)
+    ids = np.concatenate([np.full(21, 4), g.integers(0, E, 40), [8, 0, E, -3]]).astype(np.int32)
+    g.shuffle(ids)
+    P = len(ids)
+    X = to_dev(wl.gaussian(g, P, K), torch.bfloat16)
+    ids_d = torch.from_numpy(ids).cuda()
+    y = tq.multi_gather_qmv_pair(g1, g2, ids_d, X)
+    y1 = tq.multi_gather_qmv(g1, ids_d, X)
+    y2 = tq.multi_gather_qmv(g2, ids_d, X)
+    torch.cuda.synchronize()
+    assert y.shape == (2 * P, N)
+    assert torch.equal(torch.nan_to_num(y[:P], nan=7.0), torch.nan_to_num(y1, nan=7.0))
+    assert torch.equal(torch.nan_to_num(y[P:], nan=7.0), torch.nan_to_num(y2, nan=7.0))
+    Xf = as_f64(X)
+    yg = as_f64(y)
+    for half, qw in ((0, g1), (1, g2)):
+        codes, scales = gpu_arrays(qw)
+        for p_ in range(P):
+            e = ids[p_]
+            row = yg[half * P + p_]
+            if 0 <= e < E:
+                want, bound = qmv_reference(codes[e], scales[e], levels, group, K, 2, Xf[p_])
+                check_outputs(row, want, bound, f"weight {half} pair {p_} expert {e}")
+            else:
+                assert np.all(np.isnan(row)), (half, p_)
+
+
 def test_multi_gather_bad_ids_and_empty():
     K, N, levels, group = 512, 32, 8, 64
     qw, _ = make_experts(917, 4, N, K, levels, group, seed=0)

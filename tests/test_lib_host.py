@@ -35,7 +35,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     handle = ctypes.CDLL(tq.LIB_PATH)
     for n in names:
         assert hasattr(handle, n), n
@@ -226,6 +226,30 @@ def test_gather_qmv_pair_validation():
     # zero ids: nothing to do; a pre-rotated input reads no signs, so they need not match
     assert pair(a, desc(E=3), n=0, ids=0) == 0
     assert pair(desc(E=3, N=0, signs=0), desc(E=3, N=0, signs=16), n=4, flags=1) == 0
+
+
+def test_multi_gather_qmv_pair_validation():
+    L = tq.lib()
+    a = desc(E=4)
+    need = L.tq_workspace_bytes(3, ctypes.byref(a), 10, 0)
+
+    def pair(d1, d2, P=10, ids=16, ws=256, nbytes=need, flags=0):
+        return L.tq_multi_gather_qmv_pair(ctypes.byref(d1), ctypes.byref(d2), ids, P, 16, 1, 16,
+                                          0, flags, ws, nbytes, None)
+
+    assert pair(a, desc(E=4, n_levels=3, group=16)) == ERR_ARG
+    assert pair(a, desc(E=4, N=8)) == ERR_ARG
+    assert pair(a, desc(E=5)) == ERR_ARG
+    assert pair(a, desc(E=4, signs=32)) == ERR_ARG
+    assert pair(a, desc(E=4), P=-1) == ERR_ARG
+    assert pair(a, desc(E=4), ids=0) == ERR_ARG
+    assert pair(a, desc(E=4), ids=18) == ERR_ALIGN
+    assert pair(a, desc(E=4), nbytes=need - 1) == ERR_WORKSPACE
+    assert pair(a, desc(E=4), ws=0) == ERR_WORKSPACE
+    assert pair(a, desc(E=4), ws=264) == ERR_ALIGN
+    assert pair(a, desc(E=4), P=0, ids=0, ws=0, nbytes=0) == 0
+    assert L.tq_multi_gather_qmv_pair(None, ctypes.byref(a), 16, 10, 16, 1, 16, 0, 0, 256, need,
+                                      None) == ERR_ARG
 
 
 def test_empty_calls_are_no_ops():
