@@ -26,9 +26,12 @@ def empty_weight(dev):
 
 def outputs(dev, M):
     return {"qw": empty_weight(dev),
+            "qw2": empty_weight(dev),
             "qmv": torch.empty(N, dtype=torch.float32, device=dev),
             "gather": torch.empty((4, N), dtype=torch.bfloat16, device=dev),
+            "gather_pair": torch.empty((8, N), dtype=torch.float32, device=dev),
             "multi": torch.empty((P, N), dtype=torch.float32, device=dev),
+            "multi_pair": torch.empty((2 * P, N), dtype=torch.float32, device=dev),
             "qmm": torch.empty((M, N), dtype=torch.float16, device=dev),
             "dequant": torch.empty((E, N, K), dtype=torch.bfloat16, device=dev)}
 
@@ -37,6 +40,7 @@ def test_graph_replays_match_eager():
     dev = torch.device("cuda")
     g = wl.rng(950, 0)
     Wb = torch.empty((E, N, K), dtype=torch.bfloat16, device=dev)
+    Wb2 = torch.empty((E, N, K), dtype=torch.bfloat16, device=dev)
     x = torch.empty(K, dtype=torch.bfloat16, device=dev)
     X = torch.empty((P, K), dtype=torch.bfloat16, device=dev)
     Xq = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
@@ -49,6 +53,7 @@ def test_graph_replays_match_eager():
     def fill(rep):
         r = wl.rng(951, rep)
         Wb.copy_(to_dev(wl.student_rows(r, E * N, K), torch.bfloat16).view(E, N, K))
+        Wb2.copy_(to_dev(wl.student_rows(r, E * N, K), torch.bfloat16).view(E, N, K))
         x.copy_(to_dev(wl.gaussian(r, 1, K)[0], torch.bfloat16))
         X.copy_(to_dev(wl.gaussian(r, P, K), torch.bfloat16))
         Xq.copy_(to_dev(wl.gaussian(r, T, K, outliers=4), torch.bfloat16))
@@ -59,7 +64,10 @@ def test_graph_replays_match_eager():
         one = tq.QWeight(q.codes[2:3], q.scales[2:3], q.signs, LEVELS, GROUP, K, N, 1, SEED)
         tq.qmv(one, x, out=o["qmv"])
         tq.gather_qmv(o["qw"], ids, x, out=o["gather"])
+        tq.encode(Wb2, LEVELS, GROUP, SEED, out=o["qw2"])
+        tq.gather_qmv_pair(o["qw"], o["qw2"], ids, x, out=o["gather_pair"])
         tq.multi_gather_qmv(o["qw"], pids, X, out=o["multi"])
+        tq.multi_gather_qmv_pair(o["qw"], o["qw2"], pids, X, out=o["multi_pair"])
         tq.gather_qmm(o["qw"], Xq, rt, off, out=o["qmm"])
         tq.dequant(o["qw"], out=o["dequant"])
 
@@ -80,7 +88,7 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(og["qw"].codes, oe["qw"].codes), rep
         assert torch.equal(og["qw"].scales, oe["qw"].scales), rep
-        for k in ("qmv", "gather", "multi", "qmm", "dequant"):
+        for k in ("qmv", "gather", "gather_pair", "multi", "multi_pair", "qmm", "dequant"):
             assert torch.isfinite(oe[k]).all(), (rep, k)
             assert torch.equal(og[k], oe[k]), (rep, k)
     # the replays saw new inputs: the last results differ from the first ones
