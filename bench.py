@@ -438,17 +438,18 @@ def bench_moe(args):
         g = wl.torch_generator(dev, c.cid, wl.T_X)
         x = torch.randn((T, Kg), generator=g, device=dev).to(torch.bfloat16)
         xd = torch.randn((M, Kd), generator=g, device=dev).to(torch.bfloat16)
-        ys = {pr.name: torch.empty((M, pr.N), dtype=torch.bfloat16, device=dev) for pr in c.projs}
+        ys = {"down": torch.empty((M, c.projs[2].N), dtype=torch.bfloat16, device=dev)}
         wsg = torch.empty((tq.workspace_bytes(tq.OP_GATHER_QMM, layers[0]["gate"], M, T) + 7) // 8,
                           dtype=torch.int64, device=dev)
         wsd = torch.empty((tq.workspace_bytes(tq.OP_GATHER_QMM, layers[0]["down"], M, M) + 7) // 8,
                           dtype=torch.int64, device=dev)
         steps_per_graph = 1
 
+        y_gu = torch.empty((2 * M, c.projs[0].N), dtype=torch.bfloat16, device=dev)  # gate; up
+
         def step(s):
             L = layers[0]
-            tq.gather_qmm(L["gate"], x, rt, off, out=ys["gate"], ws=wsg)
-            tq.gather_qmm(L["up"], x, rt, off, out=ys["up"], ws=wsg)
+            tq.gather_qmm_pair(L["gate"], L["up"], x, rt, off, out=y_gu, ws=wsg)
             tq.gather_qmm(L["down"], xd, ident, off, out=ys["down"], ws=wsd)
         flops_step = 2.0 * M * (2 * Kg * c.projs[0].N + Kd * c.projs[2].N)
         bytes_step = c.E * sum(wbytes.values())

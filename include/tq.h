@@ -242,6 +242,21 @@ int tq_gather_qmm(const tq_qweight *w, const void *x, tq_dtype x_dtype, int64_t 
                   const int32_t *row_token, const int32_t *expert_offsets, int64_t M, void *y,
                   tq_dtype y_dtype, uint32_t flags, void *ws, size_t ws_bytes, void *stream);
 
+/* tq_gather_qmm of two weights over the same sorted rows: a Mixture-of-Experts layer's gate
+ * and up projections, which multiply the same token rows by the same experts' weights
+ * ("Running a quantized layer", kernel table, third row). y[m] = W1_e R x[row_token[m]] and
+ * y[M + m] = W2_e R x[row_token[m]] for offsets[e] <= m < offsets[e+1]; y device [2M][N].
+ * The rows are rotated and the tiles scheduled once, then each weight's matrix kernel runs.
+ * The weights must have the same n_levels, group, K, N and E and share one `signs` array
+ * (with TQ_X_ROTATED none is read). Results are those of two tq_gather_qmm calls, bit for
+ * bit. Workspace: tq_workspace_bytes(TQ_OP_GATHER_QMM, w1, M, T). Errors: the
+ * tq_gather_qmm ones; TQ_ERR_ARG when the weights differ in format or shape or do not share
+ * their signs array, or M >= 2^30. */
+int tq_gather_qmm_pair(const tq_qweight *w1, const tq_qweight *w2, const void *x,
+                       tq_dtype x_dtype, int64_t T, const int32_t *row_token,
+                       const int32_t *expert_offsets, int64_t M, void *y, tq_dtype y_dtype,
+                       uint32_t flags, void *ws, size_t ws_bytes, void *stream);
+
 /* Decoded weights of n experts in the rotated basis, for the shapes of work the fused
  * kernels above do not cover ("Running a quantized layer", kernel table, fourth row:
  * dequantize the experts, then a regular matrix multiply):

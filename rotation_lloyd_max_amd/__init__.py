@@ -74,6 +74,8 @@ SIGNATURES = [
      [_QW, _P, _I64, _P, ctypes.c_int, _P, ctypes.c_int, _U32, _P]),
     ("tq_gather_qmm", ctypes.c_int,
      [_QW, _P, ctypes.c_int, _I64, _P, _P, _I64, _P, ctypes.c_int, _U32, _P, _SZ, _P]),
+    ("tq_gather_qmm_pair", ctypes.c_int,
+     [_QW, _QW, _P, ctypes.c_int, _I64, _P, _P, _I64, _P, ctypes.c_int, _U32, _P, _SZ, _P]),
     ("tq_dequant", ctypes.c_int, [_QW, _P, _I64, _P, ctypes.c_int, _P]),
     ("tq_encode_stream", ctypes.c_int,
      [_P, ctypes.c_int, _I64, _I64, _I32, _I32, _U64, _P, _P, _P, _SZ, _P, _P]),
@@ -459,6 +461,31 @@ def gather_qmm(qw, X, row_token, offsets, out_dtype=torch.float32, rotated=False
     _check(lib().tq_gather_qmm(ctypes.byref(d), _ptr(X), _dt(X), T, _ptr(row_token),
                                _ptr(offsets), M, _ptr(y), _dt(y),
                                X_ROTATED if rotated else 0, _ptr(ws), nbytes, _stream()))
+    return y
+
+
+def gather_qmm_pair(qw1, qw2, X, row_token, offsets, out_dtype=torch.float32, rotated=False,
+                    out=None, ws=None):
+    """gather_qmm of two weights over the same sorted rows (gate and up of a MoE layer):
+    [2M, N], rows M.. from qw2; the rows are rotated and the tiles scheduled once. The
+    weights must be rotated alike (same seed and K); the library then reads qw1's signs."""
+    if qw1.seed != qw2.seed or qw1.K != qw2.K:
+        raise ValueError("gather_qmm_pair: the two weights must share seed and K")
+    X = X.contiguous()
+    row_token = row_token.to(torch.int32).contiguous()
+    offsets = offsets.to(torch.int32).contiguous()
+    T = X.shape[0]
+    M = row_token.numel()
+    y = out if out is not None else torch.empty((2 * M, qw1.N), dtype=out_dtype, device=X.device)
+    nbytes = workspace_bytes(OP_GATHER_QMM, qw1, M, T)
+    if ws is None:
+        ws = _workspace(nbytes, X.device)
+    d1 = qw1.desc()
+    d2 = qw2.desc()
+    d2.signs = d1.signs
+    _check(lib().tq_gather_qmm_pair(ctypes.byref(d1), ctypes.byref(d2), _ptr(X), _dt(X), T,
+                                    _ptr(row_token), _ptr(offsets), M, _ptr(y), _dt(y),
+                                    X_ROTATED if rotated else 0, _ptr(ws), nbytes, _stream()))
     return y
 
 

@@ -550,7 +550,8 @@ __global__ __launch_bounds__(kQmmThreads) void k_gqmm(QmmParams p) {
 
 hipError_t launch_gather_qmm(const WeightArgs& w, const void* x, int xdt, int64_t T,
                              const int32_t* row_token, const int32_t* offsets, int64_t M,
-                             bool x_rotated, void* y, int ydt, void* ws, hipStream_t s) {
+                             bool x_rotated, void* y, int ydt, void* ws, hipStream_t s,
+                             const WeightArgs* w2) {
   if (M == 0 || w.N == 0) return hipSuccess;
   if (w.E > kMaxExpertsQmm) return hipErrorInvalidValue;
   // one expert's codes and scales are addressed with 32-bit byte offsets
@@ -587,27 +588,38 @@ hipError_t launch_gather_qmm(const WeightArgs& w, const void* x, int xdt, int64_
   // groups fit one window (never with groups of 16, whose scales are per half fragment).
   const bool sl = !g16 && p.ngk <= qmm_lds_groups<16>();
   const dim3 blk(kQmmThreads);
-  switch (w.levels) {
-    case 16:
-      if (g16) hipLaunchKernelGGL((k_gqmm<16, true, false>), grid, blk, 0, s, p);
-      else if (sl) hipLaunchKernelGGL((k_gqmm<16, false, true>), grid, blk, 0, s, p);
-      else hipLaunchKernelGGL((k_gqmm<16, false, false>), grid, blk, 0, s, p);
-      break;
-    case 8:
-      if (g16) hipLaunchKernelGGL((k_gqmm<8, true, false>), grid, blk, 0, s, p);
-      else if (sl) hipLaunchKernelGGL((k_gqmm<8, false, true>), grid, blk, 0, s, p);
-      else hipLaunchKernelGGL((k_gqmm<8, false, false>), grid, blk, 0, s, p);
-      break;
-    case 4:
-      if (g16) hipLaunchKernelGGL((k_gqmm<4, true, false>), grid, blk, 0, s, p);
-      else if (sl) hipLaunchKernelGGL((k_gqmm<4, false, true>), grid, blk, 0, s, p);
-      else hipLaunchKernelGGL((k_gqmm<4, false, false>), grid, blk, 0, s, p);
-      break;
-    default:
-      hipLaunchKernelGGL((k_gqmm<3, false, true>), grid, blk, 0, s, p);
-      break;
+  // with a second weight: a second matrix launch over the same rotated rows and tiles,
+  // writing rows M .. 2M - 1
+  for (int h = 0; h < (w2 ? 2 : 1); ++h) {
+    if (h == 1) {
+      p.codes = w2->codes;
+      p.scales = w2->scales;
+      p.y = static_cast<char*>(y) + M * w.N * (ydt == 0 ? 4 : 2);
+    }
+    switch (w.levels) {
+      case 16:
+        if (g16) hipLaunchKernelGGL((k_gqmm<16, true, false>), grid, blk, 0, s, p);
+        else if (sl) hipLaunchKernelGGL((k_gqmm<16, false, true>), grid, blk, 0, s, p);
+        else hipLaunchKernelGGL((k_gqmm<16, false, false>), grid, blk, 0, s, p);
+        break;
+      case 8:
+        if (g16) hipLaunchKernelGGL((k_gqmm<8, true, false>), grid, blk, 0, s, p);
+        else if (sl) hipLaunchKernelGGL((k_gqmm<8, false, true>), grid, blk, 0, s, p);
+        else hipLaunchKernelGGL((k_gqmm<8, false, false>), grid, blk, 0, s, p);
+        break;
+      case 4:
+        if (g16) hipLaunchKernelGGL((k_gqmm<4, true, false>), grid, blk, 0, s, p);
+        else if (sl) hipLaunchKernelGGL((k_gqmm<4, false, true>), grid, blk, 0, s, p);
+        else hipLaunchKernelGGL((k_gqmm<4, false, false>), grid, blk, 0, s, p);
+        break;
+      default:
+        hipLaunchKernelGGL((k_gqmm<3, false, true>), grid, blk, 0, s, p);
+        break;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace tq

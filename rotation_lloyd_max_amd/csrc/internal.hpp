@@ -95,9 +95,12 @@ hipError_t launch_multi_gather(const WeightArgs& w, const int32_t* ids, int64_t 
                                void* ws, hipStream_t s, const WeightArgs* w2 = nullptr);
 
 size_t gather_qmm_workspace(const WeightArgs& w, int64_t M, int64_t T);
+// With w2 (same format, shape and experts as w, rotated alike): y holds 2M rows, w2's
+// from row M; the rows are rotated and the tiles scheduled once.
 hipError_t launch_gather_qmm(const WeightArgs& w, const void* x, int xdt, int64_t T,
                              const int32_t* row_token, const int32_t* offsets, int64_t M,
-                             bool x_rotated, void* y, int ydt, void* ws, hipStream_t s);
+                             bool x_rotated, void* y, int ydt, void* ws, hipStream_t s,
+                             const WeightArgs* w2 = nullptr);
 
 // KV-cache fetch: out[r] = R^T (c[idx] * scale) for `rows` rows of a power-of-two K <= 2048.
 bool kv_fetch_supported(int K, int levels);

@@ -686,6 +686,40 @@ int tq_gather_qmm(const tq_qweight* w, const void* x, tq_dtype x_dtype, int64_t 
                     "tq_gather_qmm");
 }
 
+int tq_gather_qmm_pair(const tq_qweight* w1, const tq_qweight* w2, const void* x,
+                       tq_dtype x_dtype, int64_t T, const int32_t* row_token,
+                       const int32_t* expert_offsets, int64_t M, void* y, tq_dtype y_dtype,
+                       uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  const bool rotated = (flags & TQ_X_ROTATED) != 0;
+  WeightArgs a{}, b{};
+  int rc = check_weight(w1, &a, false, rotated);
+  if (rc != TQ_OK) return rc;
+  rc = check_weight(w2, &b, false, rotated);
+  if (rc != TQ_OK) return rc;
+  if (a.levels != b.levels || a.group != b.group || a.K != b.K || a.N != b.N || a.E != b.E)
+    return fail(TQ_ERR_ARG, "tq_gather_qmm_pair: the two weights differ in format or shape");
+  if (!rotated && w1->signs != w2->signs)
+    return fail(TQ_ERR_ARG, "tq_gather_qmm_pair: the two weights must share one signs array");
+  if (T < 0 || M < 0 || M > (1ll << 30) - 1 || T > (1ll << 31) - 1)
+    return fail(TQ_ERR_ARG, "T must be in [0, 2^31) and M in [0, 2^30)");
+  rc = check_io(x, x_dtype, y, y_dtype, M > 0 && a.N > 0);
+  if (rc != TQ_OK) return rc;
+  if (M == 0 || a.N == 0) return TQ_OK;
+  if (T == 0) return fail(TQ_ERR_ARG, "T must be > 0 when M > 0");
+  if (!row_token || !expert_offsets) return fail(TQ_ERR_ARG, "row_token and expert_offsets needed");
+  if (!aligned(row_token, 4) || !aligned(expert_offsets, 4))
+    return fail(TQ_ERR_ALIGN, "row_token/expert_offsets misaligned");
+  if (rotated && x_dtype == TQ_BF16 && !aligned(x, 16))
+    return fail(TQ_ERR_ALIGN, "rotated bf16 x must be 16-byte aligned");
+  const size_t need = gather_qmm_workspace(a, M, T);
+  if (!ws || ws_bytes < need)
+    return fail(TQ_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  if (!aligned(ws, 256)) return fail(TQ_ERR_ALIGN, "workspace must be 256-byte aligned");
+  return hip_status(launch_gather_qmm(a, x, x_dtype, T, row_token, expert_offsets, M, rotated, y,
+                                      y_dtype, ws, static_cast<hipStream_t>(stream), &b),
+                    "tq_gather_qmm_pair");
+}
+
 // ---- expert cache ------------------------------------------------------------------------
 // Host state (caller-owned memory): a header, then slot_expert[slots] (int32, -1 = empty),
 // slot_tick[slots] (uint64, the call that last used the slot), expert_slot[E] (int32, -1 =

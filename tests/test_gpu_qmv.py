@@ -397,6 +397,44 @@ def test_gather_qmm(levels, group, K, N):
         check_outputs(yg[a:b], want, bound, f"expert {e}")
 
 
+@pytest.mark.parametrize("levels,group,K,N", [(16, 128, 4096, 192), (3, 16, 2048, 64),
+                                              (8, 32, 1280, 90)])
+def test_gather_qmm_pair(levels, group, K, N):
+    # gate and up over the same sorted rows: rows m from the first weight, rows M + m from
+    # the second, each equal to its own gather_qmm call bit for bit and to the oracle within
+    # the bound; an out-of-range token gives NaN rows in both halves
+    E, T, k = 8, 64, 3
+    g1, _ = make_experts(934, E, N, K, levels, group, seed=6)
+    W2 = torch.stack([to_dev(wl.student_rows(wl.rng(935, 20, e), N, K), torch.bfloat16)
+                      for e in range(E)])
+    g2, _ = encode_both(W2, levels, group, 6)
+    row_token, _, offsets = routing_case(T, E, k, 934 + K)
+    row_token = row_token.copy()
+    row_token[5] = T + 3
+    M = len(row_token)
+    X = to_dev(wl.gaussian(wl.rng(934, 3), T, K), torch.bfloat16)
+    rt, off = torch.from_numpy(row_token).cuda(), torch.from_numpy(offsets).cuda()
+    y = tq.gather_qmm_pair(g1, g2, X, rt, off)
+    y1 = tq.gather_qmm(g1, X, rt, off)
+    y2 = tq.gather_qmm(g2, X, rt, off)
+    torch.cuda.synchronize()
+    assert y.shape == (2 * M, N)
+    assert torch.equal(torch.nan_to_num(y[:M], nan=7.0), torch.nan_to_num(y1, nan=7.0))
+    assert torch.equal(torch.nan_to_num(y[M:], nan=7.0), torch.nan_to_num(y2, nan=7.0))
+    Xf = as_f64(X)
+    yg = as_f64(y)
+    assert np.isnan(yg[5]).all() and np.isnan(yg[M + 5]).all()
+    for half, qw in ((0, g1), (1, g2)):
+        codes, scales = gpu_arrays(qw)
+        for e in range(E):
+            rows = [m for m in range(offsets[e], offsets[e + 1]) if m != 5]
+            if not rows:
+                continue
+            want, bound = qmv_reference(codes[e], scales[e], levels, group, K, 6,
+                                        Xf[row_token[rows]])
+            check_outputs(yg[half * M + np.array(rows)], want, bound, f"weight {half} expert {e}")
+
+
 def test_gather_qmm_edges():
     # experts with no rows, an expert with more rows than one tile, rows past the end of N,
     # an out-of-range token id (NaN row), and a pre-rotated bf16 input

@@ -35,7 +35,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     handle = ctypes.CDLL(tq.LIB_PATH)
     for n in names:
         assert hasattr(handle, n), n
@@ -250,6 +250,27 @@ def test_multi_gather_qmv_pair_validation():
     assert pair(a, desc(E=4), P=0, ids=0, ws=0, nbytes=0) == 0
     assert L.tq_multi_gather_qmv_pair(None, ctypes.byref(a), 16, 10, 16, 1, 16, 0, 0, 256, need,
                                       None) == ERR_ARG
+
+
+def test_gather_qmm_pair_validation():
+    L = tq.lib()
+    a = desc(E=4)
+    need = L.tq_workspace_bytes(4, ctypes.byref(a), 100, 50)
+
+    def pair(d1, d2, M=100, rt=16, off=16, ws=256, nbytes=need, flags=0):
+        return L.tq_gather_qmm_pair(ctypes.byref(d1), ctypes.byref(d2), 16, 1, 50, rt, off, M,
+                                    16, 0, flags, ws, nbytes, None)
+
+    assert pair(a, desc(E=4, group=128)) == ERR_ARG
+    assert pair(a, desc(E=4, N=8)) == ERR_ARG
+    assert pair(a, desc(E=3)) == ERR_ARG
+    assert pair(a, desc(E=4, signs=32)) == ERR_ARG
+    assert pair(a, desc(E=4), M=1 << 30) == ERR_ARG
+    assert pair(a, desc(E=4), rt=0) == ERR_ARG
+    assert pair(a, desc(E=4), off=18) == ERR_ALIGN
+    assert pair(a, desc(E=4), nbytes=need - 1) == ERR_WORKSPACE
+    assert pair(a, desc(E=4), ws=272) == ERR_ALIGN
+    assert pair(a, desc(E=4), M=0, rt=0, off=0, ws=0, nbytes=0) == 0
 
 
 def test_empty_calls_are_no_ops():
