@@ -127,6 +127,22 @@ def _dt(t):
         raise TypeError(f"unsupported dtype {t.dtype}") from None
 
 
+def _out(out, shape, dtype, device):
+    """A new output tensor, or the caller's out= once it is known to hold exactly the
+    elements the call writes (the library writes through the pointer, so a smaller or
+    strided buffer would be written past its end)."""
+    shape = (shape,) if isinstance(shape, int) else tuple(shape)
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    n = 1
+    for d in shape:
+        n *= int(d)
+    if out.numel() != n or not out.is_contiguous() or out.device != torch.device(device):
+        raise ValueError(f"out= must be a contiguous tensor of {n} elements {tuple(shape)} on "
+                         f"{device}, got {tuple(out.shape)} on {out.device}")
+    return out
+
+
 def words_per_row(K, levels):
     return int(lib().tq_words_per_row(K, levels))
 
@@ -286,7 +302,7 @@ def _workspace(nbytes, device):
 
 def qmv(qw, x, out_dtype=torch.float32, rotated=False, out=None):
     x = x.contiguous()
-    y = out if out is not None else torch.empty(qw.N, dtype=out_dtype, device=x.device)
+    y = _out(out, qw.N, out_dtype, x.device)
     d = qw.desc()
     _check(lib().tq_qmv(ctypes.byref(d), _ptr(x), _dt(x), _ptr(y), _dt(y),
                         X_ROTATED if rotated else 0, None, 0, _stream()))
@@ -301,7 +317,7 @@ def rotate_dense(x, R, out_dtype=torch.float32, out=None):
     if R.dtype != torch.float32 or tuple(R.shape) != (K, K):
         raise ValueError("R must be a float32 [K, K] tensor")
     R = R.contiguous()
-    o = out if out is not None else torch.empty(x.shape, dtype=out_dtype, device=x.device)
+    o = _out(out, x.shape, out_dtype, x.device)
     with torch.cuda.device(x.device):
         _check(lib().tq_rotate_dense(_ptr(x), _dt(x), rows, K, _ptr(R), _ptr(o), _dt(o),
                                      _stream(x.device)))
@@ -339,8 +355,7 @@ def encode_dense(W, R, levels, group, ws_bytes=256 << 20, out=None):
 def kv_fetch(qw, out_dtype=torch.bfloat16, out=None):
     """Every row of a compressed KV cache (a QWeight of E x N rows of head_dim K, typically
     from encode(x, 256 or 8, group, seed)) dequantized and rotated back: [E, N, K]."""
-    o = out if out is not None else torch.empty((qw.E, qw.N, qw.K), dtype=out_dtype,
-                                                device=qw.codes.device)
+    o = _out(out, (qw.E, qw.N, qw.K), out_dtype, qw.codes.device)
     d = qw.desc()
     with torch.cuda.device(qw.codes.device):
         _check(lib().tq_kv_fetch(ctypes.byref(d), _ptr(o), _dt(o), _stream(qw.codes.device)))
@@ -355,7 +370,7 @@ def dequant(qw, ids=None, out_dtype=torch.bfloat16, out=None):
     else:
         n = qw.E
     dev = qw.codes.device
-    w = out if out is not None else torch.empty((n, qw.N, qw.K), dtype=out_dtype, device=dev)
+    w = _out(out, (n, qw.N, qw.K), out_dtype, dev)
     d = qw.desc()
     _check(lib().tq_dequant(ctypes.byref(d), _ptr(ids) if ids is not None else None, n,
                             _ptr(w), _dt(w), _stream()))
@@ -366,7 +381,7 @@ def gather_qmv(qw, ids, x, out_dtype=torch.float32, rotated=False, out=None):
     x = x.contiguous()
     ids = ids.to(torch.int32).contiguous()
     n = ids.numel()
-    y = out if out is not None else torch.empty((n, qw.N), dtype=out_dtype, device=x.device)
+    y = _out(out, (n, qw.N), out_dtype, x.device)
     d = qw.desc()
     _check(lib().tq_gather_qmv(ctypes.byref(d), _ptr(ids), n, _ptr(x), _dt(x), _ptr(y), _dt(y),
                                X_ROTATED if rotated else 0, None, 0, _stream()))
@@ -382,7 +397,7 @@ def gather_qmv_pair(qw1, qw2, ids, x, out_dtype=torch.float32, rotated=False, ou
     x = x.contiguous()
     ids = ids.to(torch.int32).contiguous()
     n = ids.numel()
-    y = out if out is not None else torch.empty((2 * n, qw1.N), dtype=out_dtype, device=x.device)
+    y = _out(out, (2 * n, qw1.N), out_dtype, x.device)
     d1 = qw1.desc()
     d2 = qw2.desc()
     d2.signs = d1.signs
@@ -396,7 +411,7 @@ def multi_gather_qmv(qw, ids, X, out_dtype=torch.float32, rotated=False, out=Non
     X = X.contiguous()
     ids = ids.to(torch.int32).contiguous()
     P = ids.numel()
-    y = out if out is not None else torch.empty((P, qw.N), dtype=out_dtype, device=X.device)
+    y = _out(out, (P, qw.N), out_dtype, X.device)
     nbytes = workspace_bytes(OP_MULTI_GATHER_QMV, qw, P)
     if ws is None:
         ws = _workspace(nbytes, X.device)
@@ -417,7 +432,7 @@ def multi_gather_qmv_pair(qw1, qw2, ids, X, out_dtype=torch.float32, rotated=Fal
     X = X.contiguous()
     ids = ids.to(torch.int32).contiguous()
     P = ids.numel()
-    y = out if out is not None else torch.empty((2 * P, qw1.N), dtype=out_dtype, device=X.device)
+    y = _out(out, (2 * P, qw1.N), out_dtype, X.device)
     nbytes = workspace_bytes(OP_MULTI_GATHER_QMV, qw1, P)
     if ws is None:
         ws = _workspace(nbytes, X.device)
@@ -437,7 +452,7 @@ def multi_gather_qmv_static(qw, ids, X, out_dtype=torch.float32, rotated=False, 
     X = X.contiguous()
     ids = ids.to(torch.int32).contiguous()
     P = ids.numel()
-    y = out if out is not None else torch.empty((P, qw.N), dtype=out_dtype, device=X.device)
+    y = _out(out, (P, qw.N), out_dtype, X.device)
     d = qw.desc()
     with torch.cuda.device(X.device):
         _check(lib().tq_multi_gather_qmv_static(ctypes.byref(d), _ptr(ids), P, _ptr(X), _dt(X),
@@ -453,7 +468,7 @@ def gather_qmm(qw, X, row_token, offsets, out_dtype=torch.float32, rotated=False
     offsets = offsets.to(torch.int32).contiguous()
     T = X.shape[0]
     M = row_token.numel()
-    y = out if out is not None else torch.empty((M, qw.N), dtype=out_dtype, device=X.device)
+    y = _out(out, (M, qw.N), out_dtype, X.device)
     nbytes = workspace_bytes(OP_GATHER_QMM, qw, M, T)
     if ws is None:
         ws = _workspace(nbytes, X.device)
@@ -476,7 +491,7 @@ def gather_qmm_pair(qw1, qw2, X, row_token, offsets, out_dtype=torch.float32, ro
     offsets = offsets.to(torch.int32).contiguous()
     T = X.shape[0]
     M = row_token.numel()
-    y = out if out is not None else torch.empty((2 * M, qw1.N), dtype=out_dtype, device=X.device)
+    y = _out(out, (2 * M, qw1.N), out_dtype, X.device)
     nbytes = workspace_bytes(OP_GATHER_QMM, qw1, M, T)
     if ws is None:
         ws = _workspace(nbytes, X.device)

@@ -252,6 +252,9 @@ def test_gather_qmv_pair(levels, group, K, N, xdt, rotated):
         x = to_dev(x0, xdt)
         xf = as_f64(x)
         extra = 0.0
+    with pytest.raises(ValueError):  # an output buffer one row short is refused
+        tq.gather_qmv_pair(g1, g2, ids, x, rotated=rotated,
+                           out=torch.empty((2 * len(ids_np) - 1, N), device="cuda"))
     y = tq.gather_qmv_pair(g1, g2, ids, x, rotated=rotated)
     y1 = tq.gather_qmv(g1, ids, x, rotated=rotated)
     y2 = tq.gather_qmv(g2, ids, x, rotated=rotated)

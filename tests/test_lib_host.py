@@ -273,6 +273,20 @@ def test_gather_qmm_pair_validation():
     assert pair(a, desc(E=4), M=0, rt=0, off=0, ws=0, nbytes=0) == 0
 
 
+def test_output_buffers_are_checked():
+    # an out= buffer must hold exactly the elements a call writes, contiguously, on the
+    # call's device: the library writes through its pointer
+    import torch
+    cpu = torch.device("cpu")
+    assert tuple(tq._out(None, 7, torch.float32, cpu).shape) == (7,)
+    o = torch.empty(4, 6)
+    assert tq._out(o, (4, 6), torch.float32, cpu) is o
+    assert tq._out(o.view(24), (4, 6), torch.float32, cpu).numel() == 24
+    for bad in (torch.empty(4, 5), torch.empty(6, 4).t(), torch.empty(4, 12)[:, ::2]):
+        with pytest.raises(ValueError):
+            tq._out(bad, (4, 6), torch.float32, cpu)
+
+
 def test_empty_calls_are_no_ops():
     L = tq.lib()
     # zero rows / zero ids / zero pairs return OK without touching the device
