@@ -130,3 +130,63 @@ def test_dequant_full_size_gate_stack():
         got = as_f64(out[int(e), torch.from_numpy(rows).to(DEV)])
         tol = np.abs(want) * 2.0 ** -7
         assert np.all(np.abs(got - want) <= tol), f"expert {e}"
+
+
+def test_full_size_pairs_equal_single_calls():
+    # the gate/up pair calls of the three MoE workloads at full size, in the configuration
+    # bench.py times: each half equals the one-weight call bit for bit, and sampled rows of
+    # the second weight's half match the oracle
+    g = wl.rng(93, 0)
+    # MoE decode: gather_qmv_pair over 8 routed experts of 384
+    c = wl.C3
+    gate = encode_stack(c, c.projs[0])
+    up = encode_stack(c, c.projs[1])
+    ids = torch.from_numpy(wl.decode_ids(c.cid, 1, c.E, 8)).to(DEV)
+    x = torch.randn(c.projs[0].K, generator=wl.torch_generator(DEV, c.cid, wl.T_X),
+                    device=DEV).to(torch.bfloat16)
+    y = tq.gather_qmv_pair(gate, up, ids, x)
+    y1, y2 = tq.gather_qmv(gate, ids, x), tq.gather_qmv(up, ids, x)
+    torch.cuda.synchronize()
+    assert torch.equal(y[:8], y1) and torch.equal(y[8:], y2)
+    yg, xf = as_f64(y), as_f64(x)
+    for k in (0, 5):
+        rows = np.sort(g.choice(up.N, 32, replace=False))
+        sampled_check(up, int(ids[k]), rows, xf, yg[8 + k, rows], f"C3 up slot {k}")
+    del gate, up, y, y1, y2
+    # ternary prefill: multi_gather_qmv_pair over 512 pairs (both weights' items in one launch)
+    c = wl.C4
+    gate = encode_stack(c, c.projs[0])
+    up = encode_stack(c, c.projs[1])
+    ids_np = wl.topk_routing(c.cid, 64, c.E, 8)
+    P = len(ids_np)
+    ids = torch.from_numpy(ids_np).to(DEV)
+    X = torch.randn((P, gate.K), generator=wl.torch_generator(DEV, c.cid, wl.T_X),
+                    device=DEV).to(torch.bfloat16)
+    y = tq.multi_gather_qmv_pair(gate, up, ids, X)
+    y1, y2 = tq.multi_gather_qmv(gate, ids, X), tq.multi_gather_qmv(up, ids, X)
+    torch.cuda.synchronize()
+    assert torch.equal(y[:P], y1) and torch.equal(y[P:], y2)
+    yg, Xf = as_f64(y), as_f64(X)
+    for p_ in np.sort(g.choice(P, 8, replace=False)):
+        rows = np.sort(g.choice(up.N, 24, replace=False))
+        sampled_check(up, int(ids_np[p_]), rows, Xf[p_], yg[P + p_, rows], f"C4 up pair {p_}")
+    del gate, up, y, y1, y2
+    # batched MoE: gather_qmm_pair over 32,768 sorted rows
+    c = wl.C5
+    gate = encode_stack(c, c.projs[0])
+    up = encode_stack(c, c.projs[1])
+    T = 4096
+    row_token, row_expert, offsets = wl.zipf_sorted_routing(c.cid, T, c.E, 8)
+    M = len(row_token)
+    X = torch.randn((T, gate.K), generator=wl.torch_generator(DEV, c.cid, wl.T_X),
+                    device=DEV).to(torch.bfloat16)
+    rt, off = torch.from_numpy(row_token).to(DEV), torch.from_numpy(offsets).to(DEV)
+    y = tq.gather_qmm_pair(gate, up, X, rt, off)
+    y1, y2 = tq.gather_qmm(gate, X, rt, off), tq.gather_qmm(up, X, rt, off)
+    torch.cuda.synchronize()
+    assert torch.equal(y[:M], y1) and torch.equal(y[M:], y2)
+    for m in np.sort(g.choice(M, 6, replace=False)):
+        cols = np.sort(g.choice(up.N, 32, replace=False))
+        ym = as_f64(y[M + int(m)])
+        sampled_check(up, int(row_expert[m]), cols, as_f64(X[int(row_token[m])]), ym[cols],
+                      f"C5 up row {m}")
