@@ -249,7 +249,8 @@ int tq_gather_qmm(const tq_qweight *w, const void *x, tq_dtype x_dtype, int64_t 
  * The rows are rotated and the tiles scheduled once, then each weight's matrix kernel runs.
  * The weights must have the same n_levels, group, K, N and E and share one `signs` array
  * (with TQ_X_ROTATED none is read). Results are those of two tq_gather_qmm calls, bit for
- * bit. Workspace: tq_workspace_bytes(TQ_OP_GATHER_QMM, w1, M, T). Errors: the
+ * bit; a row_token outside [0, T) gives NaN rows in both halves. Workspace:
+ * tq_workspace_bytes(TQ_OP_GATHER_QMM, w1, M, T). Errors: the
  * tq_gather_qmm ones; TQ_ERR_ARG when the weights differ in format or shape or do not share
  * their signs array, or M >= 2^30. */
 int tq_gather_qmm_pair(const tq_qweight *w1, const tq_qweight *w2, const void *x,
