@@ -438,6 +438,41 @@ def test_gather_qmm_pair(levels, group, K, N):
             check_outputs(yg[half * M + np.array(rows)], want, bound, f"weight {half} expert {e}")
 
 
+@pytest.mark.parametrize("op", ["multi_gather", "gather_qmm"])
+def test_pair_calls_take_pre_rotated_inputs(op):
+    # the multi_gather and gather_qmm pairs with inputs already rotated (fp32 R x): no signs
+    # are read, and each half matches the oracle on the original inputs
+    levels, group, K, N, E = 16, 64, 1536, 48, 5
+    g1, _ = make_experts(936, E, N, K, levels, group, seed=3)
+    W2 = torch.stack([to_dev(wl.student_rows(wl.rng(937, 20, e), N, K), torch.bfloat16)
+                      for e in range(E)])
+    g2, _ = encode_both(W2, levels, group, 3)
+    g = wl.rng(936, 2)
+    rows = 12
+    X0 = wl.gaussian(g, rows, K).astype(np.float64)
+    Xr = torch.from_numpy(ohd.rotate(X0, 3).astype(np.float32)).cuda()
+    if op == "multi_gather":
+        ids = g.integers(0, E, rows).astype(np.int32)
+        y = tq.multi_gather_qmv_pair(g1, g2, torch.from_numpy(ids).cuda(), Xr, rotated=True)
+        experts, xs, n = ids, X0, rows
+    else:
+        offsets = np.array([0, 3, 3, 8, 10, 12], dtype=np.int32)
+        row_token = g.integers(0, rows, 12).astype(np.int32)
+        y = tq.gather_qmm_pair(g1, g2, Xr, torch.from_numpy(row_token).cuda(),
+                               torch.from_numpy(offsets).cuda(), rotated=True)
+        experts = np.repeat(np.arange(E), np.diff(offsets))
+        xs, n = X0[row_token], 12
+    torch.cuda.synchronize()
+    yg = as_f64(y)
+    for half, qw in ((0, g1), (1, g2)):
+        codes, scales = gpu_arrays(qw)
+        for i in range(n):
+            e = int(experts[i])
+            want, bound = qmv_reference(codes[e], scales[e], levels, group, K, 3, xs[i])
+            check_outputs(yg[half * n + i], want, bound + 1e-6 * np.abs(want),
+                          f"{op} weight {half} row {i}")
+
+
 def test_gather_qmm_edges():
     # experts with no rows, an expert with more rows than one tile, rows past the end of N,
     # an out-of-range token id (NaN row), and a pre-rotated bf16 input
