@@ -116,7 +116,7 @@ constexpr int prefetch_passes() {
   return M == 12 ? 3 : 1;
 }
 
-template <int M, int LEVELS, int LG_G>
+template <int M, int LEVELS, int LG_G, bool FAST_A>
 __global__ __launch_bounds__(kMThreads, 2) void k_encode_m(EncMParams p) {
   constexpr int NP = prefetch_passes<M>();
   constexpr int MAXP = M == 12 ? 3 : 2;
@@ -177,6 +177,17 @@ __global__ __launch_bounds__(kMThreads, 2) void k_encode_m(EncMParams p) {
     smask |= ((sw[e >> 5] >> (e & 31)) & 1u) << a;
   }
 
+  // Addresses of the m-point outputs (FAST_A: P >= 128). The slot swizzle is linear over
+  // the bits of the element index and reads only bits 4..8, so with P >= 128 and m a
+  // multiple of 4 element (row r, a, column b) lies at 8 P (r m + a - a % 4) + tA[a % 4],
+  // tA[k] the address of element k P + b: one add per output instead of the swizzle.
+  static_assert(M % 4 == 0, "the address split needs m = 0 mod 4");
+  int tA[4];
+  if constexpr (FAST_A) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) tA[k] = melem_addr(k * P + ab);
+  }
+
   // C lanes: 32 consecutive elements of the batch
   const int nC = (R * K) >> 5;
   const int crr = static_cast<int>(__umulhi(static_cast<uint32_t>(32 * tid), p.inv_k));  // row in batch
@@ -211,15 +222,26 @@ __global__ __launch_bounds__(kMThreads, 2) void k_encode_m(EncMParams p) {
       if (ps == npass - 1 && bt + gridDim.x < nbatch) load_batch(bt + gridDim.x);
       const int r = ps * rpp + ar;
       if (r < R) {  // rows past the end of the data are transformed but never stored
-        const int e0 = r * K + ab;
-        auto put = [&](int a, double y) { *reinterpret_cast<double*>(buf + melem_addr(e0 + a * P)) = y; };
-        if constexpr (M == 28) {
-          hadamard28_side<double, 0>(x, [&](int Rr, double y) { put(2 * Rr, y); });
-          hadamard28_side<double, 1>(x, [&](int Rr, double y) { put(2 * Rr + 1, y); });
+        auto factor = [&](auto put) __attribute__((always_inline)) {
+          if constexpr (M == 28) {
+            hadamard28_side<double, 0>(x, [&](int Rr, double y) { put(2 * Rr, y); });
+            hadamard28_side<double, 1>(x, [&](int Rr, double y) { put(2 * Rr + 1, y); });
+          } else {
+            [&]<int... A>(std::integer_sequence<int, A...>) {
+              (put(A, hadamard_row<double, M, A>(x, std::make_integer_sequence<int, M>{})), ...);
+            }(std::make_integer_sequence<int, M>{});
+          }
+        };
+        if constexpr (FAST_A) {
+          const int bq = (r * M) << (lgp + 3);
+          factor([&](int a, double y) {
+            *reinterpret_cast<double*>(buf + bq + ((a & ~3) << (lgp + 3)) + tA[a & 3]) = y;
+          });
         } else {
-          [&]<int... A>(std::integer_sequence<int, A...>) {
-            (put(A, hadamard_row<double, M, A>(x, std::make_integer_sequence<int, M>{})), ...);
-          }(std::make_integer_sequence<int, M>{});
+          const int e0 = r * K + ab;
+          factor([&](int a, double y) {
+            *reinterpret_cast<double*>(buf + melem_addr(e0 + a * P)) = y;
+          });
         }
       }
     }
@@ -288,18 +310,25 @@ __global__ __launch_bounds__(kMThreads, 2) void k_encode_m(EncMParams p) {
   }
 }
 
-template <int M, int LEVELS>
-hipError_t launch_m_l(const EncMParams& p, int group, int grid, size_t lds, hipStream_t s) {
+template <int M, int LEVELS, bool FAST_A>
+hipError_t launch_m_f(const EncMParams& p, int group, int grid, size_t lds, hipStream_t s) {
   void (*kern)(EncMParams) = nullptr;
   switch (group) {
-    case 16: kern = k_encode_m<M, LEVELS, 4>; break;
-    case 32: kern = k_encode_m<M, LEVELS, 5>; break;
-    case 64: kern = k_encode_m<M, LEVELS, 6>; break;
-    default: kern = k_encode_m<M, LEVELS, 7>; break;
+    case 16: kern = k_encode_m<M, LEVELS, 4, FAST_A>; break;
+    case 32: kern = k_encode_m<M, LEVELS, 5, FAST_A>; break;
+    case 64: kern = k_encode_m<M, LEVELS, 6, FAST_A>; break;
+    default: kern = k_encode_m<M, LEVELS, 7, FAST_A>; break;
   }
   // lds <= 64 KB, the default limit of dynamic LDS
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kMThreads), lds, s, p);
   return hipGetLastError();
+}
+
+template <int M, int LEVELS>
+hipError_t launch_m_l(const EncMParams& p, int group, int grid, size_t lds, hipStream_t s) {
+  // the one-add output addresses of phase A hold for rows of P >= 128
+  return p.lg_p >= 7 ? launch_m_f<M, LEVELS, true>(p, group, grid, lds, s)
+                     : launch_m_f<M, LEVELS, false>(p, group, grid, lds, s);
 }
 
 template <int M>
