@@ -359,6 +359,12 @@ constexpr int max_depth() {
 
 template <int L, int CPL, bool G16, bool X32>
 static const void* pick_depth(int depth) {
+  // 4-bit rows of one chunk per lane (K <= 2048; the MoE down projection, 14 row groups per
+  // workgroup): a ring of two measured faster than four there (15.3-15.7 against
+  // 15.7-16.1 us per call), one of eight slower; the other kernels keep four
+  if constexpr (L == 16 && CPL == 1) {
+    if (depth >= 2) return reinterpret_cast<const void*>(k_qmv<L, CPL, G16, X32, 2>);
+  }
   if constexpr (max_depth<L, CPL>() >= 8) {
     if (depth >= 8) return reinterpret_cast<const void*>(k_qmv<L, CPL, G16, X32, 8>);
   }
